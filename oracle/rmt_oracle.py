@@ -1,0 +1,297 @@
+"""CPU oracle for diagonal-batched recurrent-memory-transformer (RMT) inference.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path imports this module:
+only the tests, the smoke check and the benchmark's CPU-baseline leg may call
+it.  It shares no code with the HIP library; the only thing both sides use is
+the seeded input generator in ``rmt_inputs``.
+
+What it computes, and where the pages say so
+--------------------------------------------
+Sources: "Diagonal Batching for Recurrent Memory Transformers" (skill page
+summarising arXiv 2506.05229: sections *Core Concept*, *Architecture
+Overview*, *Implementation*) and "Diagonal Batching Unlocks Parallelism in
+Recurrent Memory Transformers for Long Contexts" (catalogue record, abstract).
+
+* An RMT splits one long sequence into S segments of n tokens.  Layer l keeps
+  m memory rows that carry state from segment s to segment s+1 (abstract:
+  linear time, constant memory).  Cell (l, s) consumes
+  ``A = [M(l, s-1); X(l-1, s)]`` (memory rows first) and produces R = m + n
+  rows Y; the first n rows become X(l, s), the last m rows become M(l, s).
+* The (layer, segment) grid is swept along anti-diagonals d = l + s
+  (*Implementation*, the scheduler's diagonal enumeration; *Architecture
+  Overview*, "Diagonal Reorganization").  Every cell of a diagonal depends
+  only on (l-1, s) and (l, s-1), so the reordering is exact (*Architecture
+  Overview*, "Dependency Preservation"; abstract, "preserving exact
+  recurrence", "purely a run-time computation reordering").
+
+Readings where the pages are silent (each is listed in the design doc):
+  - the cell function is the one each workload defines: linear+GELU (tiny
+    grid), RMSNorm+SwiGLU with residual (attention-free), or a pre-norm
+    LLaMA block (RMSNorm, QKV, RoPE, causal GQA, O, RMSNorm, SwiGLU);
+  - RMSNorm is ``x * rsqrt(mean(x^2) + eps) * g``;
+  - RoPE is the rotate-half form with positions 0..R-1 local to the cell,
+    memory rows included;
+  - attention is causal over all R rows of the cell, scale 1/sqrt(hd),
+    query head h reads KV head h // (Hq / Hkv);
+  - GELU is the exact erf form.
+
+Arithmetic is in the dtype of the inputs (float32 by default, float64 for
+the pins).  There is no blocking, fusion or reordering beyond the per-cell
+definition: every product is one ``numpy.matmul`` call.
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict, List, Sequence, Tuple
+
+import numpy as np
+from scipy.special import erf as _erf
+
+CELL_LINEAR_GELU = 0
+CELL_NORM_SWIGLU = 1
+CELL_LLAMA = 2
+
+
+# ---------------------------------------------------------------------------
+# Schedule: skill page, *Implementation*, the scheduler's diagonal enumeration.
+# For each diagonal index d in [0, L+S-1), walk the layers in ascending order,
+# set s = d - l and keep (l, s) when 0 <= s < S; keep only non-empty diagonals.
+# ---------------------------------------------------------------------------
+
+def schedule(L: int, S: int) -> List[List[Tuple[int, int]]]:
+    diagonals = []
+    for d in range(L + S - 1):
+        diagonal = []
+        for l in range(L):
+            s = d - l
+            if 0 <= s < S:
+                diagonal.append((l, s))
+        if diagonal:
+            diagonals.append(diagonal)
+    return diagonals
+
+
+def schedule_table(L: int, S: int) -> Tuple[np.ndarray, np.ndarray]:
+    """CSR form of ``schedule``: ``diag_ptr[k]..diag_ptr[k+1]`` index the cells
+    of diagonal k; each cell row is (layer, segment, slot), slot being the
+    cell's position within its diagonal."""
+    diags = schedule(L, S)
+    diag_ptr = np.zeros(len(diags) + 1, np.int32)
+    cells = np.zeros((L * S, 3), np.int32)
+    k = 0
+    for i, diag in enumerate(diags):
+        for slot, (l, s) in enumerate(diag):
+            cells[k] = (l, s, slot)
+            k += 1
+        diag_ptr[i + 1] = k
+    return diag_ptr, cells
+
+
+# ---------------------------------------------------------------------------
+# Elementwise pieces of the cells.
+# ---------------------------------------------------------------------------
+
+def gelu_erf(z: np.ndarray) -> np.ndarray:
+    """GELU, exact form: z * Phi(z) = 0.5 z (1 + erf(z / sqrt 2))."""
+    one = z.dtype.type(1.0)
+    half = z.dtype.type(0.5)
+    return half * z * (one + _erf(z / z.dtype.type(math.sqrt(2.0))))
+
+
+def silu(t: np.ndarray) -> np.ndarray:
+    """SiLU t * sigmoid(t)."""
+    one = t.dtype.type(1.0)
+    return t / (one + np.exp(-t))
+
+
+def rms_norm(x: np.ndarray, g: np.ndarray, eps: float) -> np.ndarray:
+    """Row-wise RMSNorm: x * rsqrt(mean(x^2) + eps) * g."""
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return x * (x.dtype.type(1.0) / np.sqrt(ms + x.dtype.type(eps))) * g.astype(x.dtype)
+
+
+def rope_rotate_half(x: np.ndarray, pos: np.ndarray, theta: float) -> np.ndarray:
+    """Rotary position embedding in the rotate-half layout.
+
+    x: [R, H, hd].  Element i of the first half pairs with element i + hd/2;
+    the pair turns by angle pos * theta**(-2i/hd).  Angles are formed in
+    float64 and the cos/sin cast to x's dtype.
+    """
+    hd = x.shape[-1]
+    half = hd // 2
+    inv_freq = theta ** (-(2.0 * np.arange(half, dtype=np.float64)) / hd)
+    ang = pos.astype(np.float64)[:, None] * inv_freq[None, :]
+    cos = np.cos(ang).astype(x.dtype)[:, None, :]
+    sin = np.sin(ang).astype(x.dtype)[:, None, :]
+    x1 = x[..., :half]
+    x2 = x[..., half:]
+    return np.concatenate([x1 * cos - x2 * sin, x2 * cos + x1 * sin], axis=-1)
+
+
+def causal_gqa_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray) -> np.ndarray:
+    """softmax(q_h k_j^T / sqrt(hd) + causal mask) v_j per query head h, with
+    j = h // (Hq / Hkv).  q: [R, Hq, hd]; k, v: [R, Hkv, hd] -> [R, Hq*hd]."""
+    R, Hq, hd = q.shape
+    Hkv = k.shape[1]
+    rep = Hq // Hkv
+    scale = q.dtype.type(1.0 / math.sqrt(hd))
+    future = np.triu(np.ones((R, R), dtype=bool), k=1)
+    out = np.empty((R, Hq, hd), dtype=q.dtype)
+    for h in range(Hq):
+        j = h // rep
+        s = (q[:, h, :] @ k[:, j, :].T) * scale
+        s[future] = -np.inf
+        s = s - s.max(axis=1, keepdims=True)
+        p = np.exp(s)
+        p = p / p.sum(axis=1, keepdims=True)
+        out[:, h, :] = p @ v[:, j, :]
+    return out.reshape(R, Hq * hd)
+
+
+def swiglu(z: np.ndarray, wg: np.ndarray, wu: np.ndarray, wd: np.ndarray) -> np.ndarray:
+    """(silu(z Wg) * (z Wu)) Wd."""
+    return (silu(z @ wg) * (z @ wu)) @ wd
+
+
+# ---------------------------------------------------------------------------
+# Cells.  A is [R, d] = [M(l, s-1); X(l-1, s)]; the result is Y [R, d].
+# ---------------------------------------------------------------------------
+
+def cell_linear_gelu(A: np.ndarray, w: Dict[str, np.ndarray]) -> np.ndarray:
+    """Y = GELU(A W_l + b_l)."""
+    return gelu_erf(A @ w["w"] + w["b"])
+
+
+def cell_norm_swiglu(A: np.ndarray, w: Dict[str, np.ndarray], eps: float) -> np.ndarray:
+    """Y = A + SwiGLU(RMSNorm(A))."""
+    return A + swiglu(rms_norm(A, w["g2"], eps), w["wg"], w["wu"], w["wd"])
+
+
+def cell_llama(A: np.ndarray, w: Dict[str, np.ndarray], Hq: int, Hkv: int, hd: int,
+               eps: float, theta: float) -> np.ndarray:
+    """Pre-norm LLaMA block over the cell's R rows:
+    H = A + Attn(RMSNorm1(A)) Wo;  Y = H + SwiGLU(RMSNorm2(H))."""
+    R = A.shape[0]
+    h = rms_norm(A, w["g1"], eps)
+    qkv = h @ w["wqkv"]
+    nq, nk = Hq * hd, Hkv * hd
+    q = qkv[:, :nq].reshape(R, Hq, hd)
+    k = qkv[:, nq:nq + nk].reshape(R, Hkv, hd)
+    v = qkv[:, nq + nk:nq + 2 * nk].reshape(R, Hkv, hd)
+    pos = np.arange(R)
+    q = rope_rotate_half(q, pos, theta)
+    k = rope_rotate_half(k, pos, theta)
+    att = causal_gqa_attention(q, k, v)
+    H = A + att @ w["wo"]
+    return H + swiglu(rms_norm(H, w["g2"], eps), w["wg"], w["wu"], w["wd"])
+
+
+def cell(cfg, w: Dict[str, np.ndarray], A: np.ndarray) -> np.ndarray:
+    if cfg.cell == CELL_LINEAR_GELU:
+        return cell_linear_gelu(A, w)
+    if cfg.cell == CELL_NORM_SWIGLU:
+        return cell_norm_swiglu(A, w, cfg.eps)
+    if cfg.cell == CELL_LLAMA:
+        return cell_llama(A, w, cfg.Hq, cfg.Hkv, cfg.hd, cfg.eps, cfg.theta)
+    raise ValueError(f"unknown cell kind {cfg.cell}")
+
+
+# ---------------------------------------------------------------------------
+# Sweeps.
+# ---------------------------------------------------------------------------
+
+def _cast_weights(weights: Sequence[Dict[str, np.ndarray]], dtype) -> List[Dict[str, np.ndarray]]:
+    return [{k: np.asarray(v, dtype=dtype) for k, v in w.items()} for w in weights]
+
+
+def segment_input(cfg, inputs: np.ndarray, s: int, embed, dtype) -> np.ndarray:
+    """X(-1, s): the segment's n input rows.  For the LLaMA cell ``inputs``
+    are token ids looked up in ``embed``; otherwise they are rows [T, d]."""
+    n = cfg.n
+    if cfg.cell == CELL_LLAMA:
+        return np.asarray(embed[inputs[s * n:(s + 1) * n]], dtype=dtype)
+    return np.asarray(inputs[s * n:(s + 1) * n], dtype=dtype)
+
+
+def _num_segments(cfg, inputs) -> int:
+    T = inputs.shape[0]
+    if T % cfg.n != 0:
+        raise ValueError("sequence length must be a whole number of segments")
+    return T // cfg.n
+
+
+def forward_sequential(cfg, weights, inputs, mem0, embed=None, dtype=np.float32):
+    """Segment by segment, then layer by layer.
+
+    Returns (hidden [S*n, d] = X(L-1, .), memory [L, m, d] = M(., S-1)).
+    The number of segments is taken from ``inputs``."""
+    S = _num_segments(cfg, inputs)
+    L, n = cfg.L, cfg.n
+    ws = _cast_weights(weights, dtype)
+    M = [np.array(mem0[l], dtype=dtype) for l in range(L)]
+    hidden = []
+    for s in range(S):
+        x = segment_input(cfg, inputs, s, embed, dtype)
+        for l in range(L):
+            A = np.concatenate([M[l], x], axis=0)
+            Y = cell(cfg, ws[l], A)
+            x, M[l] = Y[:n], Y[n:]
+        hidden.append(x)
+    return np.concatenate(hidden, axis=0), np.stack(M)
+
+
+def forward_diagonal(cfg, weights, inputs, mem0, embed=None, dtype=np.float32):
+    """The same recurrence swept along anti-diagonals d = l + s.
+
+    Every cell of a diagonal reads its inputs as they stood at the end of the
+    previous diagonal: all inputs of a diagonal are gathered first, then the
+    cells run, and their X outputs go to a fresh buffer.  (Writing X in place
+    while walking the diagonal would let cell (l-1, s+1) overwrite X(l-1, s)
+    before cell (l, s) reads it.)"""
+    S = _num_segments(cfg, inputs)
+    L, n = cfg.L, cfg.n
+    ws = _cast_weights(weights, dtype)
+    M = [np.array(mem0[l], dtype=dtype) for l in range(L)]
+    hidden = [None] * S
+    prev_x: Dict[Tuple[int, int], np.ndarray] = {}
+    for diag in schedule(L, S):
+        A_list = []
+        for (l, s) in diag:
+            x_in = segment_input(cfg, inputs, s, embed, dtype) if l == 0 else prev_x[(l - 1, s)]
+            A_list.append(np.concatenate([M[l], x_in], axis=0))
+        next_x = {}
+        for (l, s), A in zip(diag, A_list):
+            Y = cell(cfg, ws[l], A)
+            next_x[(l, s)] = Y[:n]
+            M[l] = Y[n:]
+            if l == L - 1:
+                hidden[s] = Y[:n]
+        prev_x = next_x
+    return np.concatenate(hidden, axis=0), np.stack(M)
+
+
+# ---------------------------------------------------------------------------
+# Whole-sequence evaluation of the linear-GELU stack (no segment loop, no
+# schedule), in float64.  The cell is row-wise, so the last m output rows of
+# cell (l, s) depend only on input rows n..R-1, i.e. on X(l-1, s) rows
+# n-m..n-1: M(l, s) = f_l(X(l-1, s)[n-m:n]).  Each layer is then two
+# whole-sequence products: all memory rows first, then every cell's
+# [M(l, s-1); X(l-1, s)] stacked into one [S*R, d] matrix.
+# ---------------------------------------------------------------------------
+
+def bruteforce_linear_gelu(cfg, weights, x0, mem0):
+    assert cfg.cell == CELL_LINEAR_GELU and cfg.m <= cfg.n
+    L, n, m, d = cfg.L, cfg.n, cfg.m, cfg.d
+    S = x0.shape[0] // n
+    X = np.asarray(x0, np.float64).reshape(S, n, d)
+    mem_last = []
+    for l in range(L):
+        W = np.asarray(weights[l]["w"], np.float64)
+        b = np.asarray(weights[l]["b"], np.float64)
+        f = lambda rows: gelu_erf(rows @ W + b)  # noqa: E731
+        M_all = f(X[:, n - m:, :].reshape(S * m, d)).reshape(S, m, d)
+        M_prev = np.concatenate([np.asarray(mem0[l], np.float64)[None], M_all[:-1]], axis=0)
+        A = np.concatenate([M_prev, X], axis=1).reshape(S * (m + n), d)
+        X = f(A).reshape(S, m + n, d)[:, :n, :]
+        mem_last.append(M_all[-1])
+    return X.reshape(S * n, d), np.stack(mem_last)

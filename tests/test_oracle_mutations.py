@@ -1,0 +1,172 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check that the pins
+catch each one.  A pin set that passes a mutated oracle would not be pinning
+that part of it."""
+import dataclasses
+
+import numpy as np
+import pytest
+
+import rmt_inputs as ri
+from oracle import rmt_oracle as orc
+
+import pins
+
+
+def _fails(fn, *a, **k):
+    try:
+        fn(*a, **k)
+    except AssertionError:
+        return True
+    return False
+
+
+def _forward_with_split(split_first_m_to_memory=False, memory_after_x=False):
+    """A sequential sweep with the write-back split or the input order changed."""
+    def fwd(cfg, weights, inputs, mem0, embed=None, dtype=np.float32):
+        S = inputs.shape[0] // cfg.n
+        L, n, m = cfg.L, cfg.n, cfg.m
+        ws = [{k: np.asarray(v, dtype) for k, v in w.items()} for w in weights]
+        M = [np.array(mem0[l], dtype) for l in range(L)]
+        hidden = []
+        for s in range(S):
+            x = orc.segment_input(cfg, inputs, s, embed, dtype)
+            for l in range(L):
+                A = np.concatenate([x, M[l]] if memory_after_x else [M[l], x])
+                Y = orc.cell(cfg, ws[l], A)
+                if split_first_m_to_memory:
+                    M[l], x = Y[:m], Y[m:]
+                else:
+                    x, M[l] = Y[:n], Y[n:]
+            hidden.append(x)
+        return np.concatenate(hidden), np.stack(M)
+    return fwd
+
+
+def test_mutation_schedule_descending_layers():
+    bad = lambda L, S: [list(reversed(dg)) for dg in orc.schedule(L, S)]  # noqa: E731
+    assert _fails(pins.pin_schedule_golden, schedule=bad)
+    assert _fails(pins.pin_schedule_invariants, 4, 6, schedule=bad)
+
+
+def test_mutation_schedule_missing_last_diagonal():
+    bad = lambda L, S: orc.schedule(L, S)[:-1]  # noqa: E731
+    assert _fails(pins.pin_schedule_invariants, 4, 6, schedule=bad)
+
+
+def test_mutation_writeback_split():
+    bad = _forward_with_split(split_first_m_to_memory=True)
+    assert _fails(pins.pin_linear_gelu_bruteforce, forward=bad)
+    assert _fails(pins.pin_shift_register, ri.TINY_SWIGLU, forward=bad)
+
+
+def test_mutation_memory_after_segment():
+    bad = _forward_with_split(memory_after_x=True)
+    assert _fails(pins.pin_linear_gelu_bruteforce, forward=bad)
+    assert _fails(pins.pin_shift_register, ri.TINY_LLAMA, forward=bad)
+
+
+def test_mutation_no_bias(monkeypatch):
+    monkeypatch.setattr(orc, "cell_linear_gelu", lambda A, w: orc.gelu_erf(A @ w["w"]))
+    assert _fails(pins.pin_linear_gelu_bruteforce)
+
+
+def test_mutation_transposed_weight(monkeypatch):
+    monkeypatch.setattr(orc, "cell_linear_gelu", lambda A, w: orc.gelu_erf(A @ w["w"].T + w["b"]))
+    assert _fails(pins.pin_linear_gelu_bruteforce)
+
+
+def test_mutation_gelu_tanh(monkeypatch):
+    def gelu_tanh(z):
+        return 0.5 * z * (1 + np.tanh(np.sqrt(2 / np.pi) * (z + 0.044715 * z ** 3)))
+    assert _fails(pins.pin_gelu, gelu=gelu_tanh)
+
+
+def test_mutation_rope_sign():
+    def rope_bad(x, pos, theta):
+        return orc.rope_rotate_half(x, -pos, theta)
+    assert _fails(pins.pin_rope, rope=rope_bad)
+
+
+def test_mutation_rope_interleaved_pairs():
+    def rope_bad(x, pos, theta):
+        hd = x.shape[-1]
+        perm = np.concatenate([np.arange(0, hd, 2), np.arange(1, hd, 2)])
+        inv = np.argsort(perm)
+        return orc.rope_rotate_half(x[..., perm], pos, theta)[..., inv]
+    assert _fails(pins.pin_rope, rope=rope_bad)
+
+
+def test_rope_position_origin_is_invisible(monkeypatch):
+    """Not a mistake: attention sees only relative positions, so shifting every
+    position by the same amount leaves the block's output unchanged."""
+    real = orc.rope_rotate_half
+    monkeypatch.setattr(orc, "rope_rotate_half", lambda x, pos, theta: real(x, pos + 7, theta))
+    pins.pin_single_segment_against_torch(ri.TINY_LLAMA, tol=1e-10)
+
+
+def test_mutation_rope_on_queries_only(monkeypatch):
+    real = orc.rope_rotate_half
+    calls = []
+
+    def rope_q_only(x, pos, theta):
+        calls.append(1)
+        return real(x, pos, theta) if len(calls) % 2 == 1 else x
+    monkeypatch.setattr(orc, "rope_rotate_half", rope_q_only)
+    assert _fails(pins.pin_single_segment_against_torch, ri.TINY_LLAMA)
+
+
+def test_mutation_attention_not_causal(monkeypatch):
+    def attn(q, k, v):
+        R, Hq, hd = q.shape
+        rep = Hq // k.shape[1]
+        out = np.empty_like(q)
+        for h in range(Hq):
+            s = q[:, h] @ k[:, h // rep].T / np.sqrt(hd)
+            p = np.exp(s - s.max(1, keepdims=True))
+            out[:, h] = (p / p.sum(1, keepdims=True)) @ v[:, h // rep]
+        return out.reshape(R, -1)
+    assert _fails(pins.pin_attention, attn=attn)
+    monkeypatch.setattr(orc, "causal_gqa_attention", attn)
+    assert _fails(pins.pin_single_segment_against_torch, ri.TINY_LLAMA)
+
+
+def test_mutation_gqa_head_map(monkeypatch):
+    real = orc.causal_gqa_attention
+
+    def attn(q, k, v):
+        # head h reads KV head h % Hkv instead of h // (Hq / Hkv)
+        R, Hq, hd = q.shape
+        Hkv = k.shape[1]
+        idx = np.array([h % Hkv for h in range(Hq)])
+        rep = Hq // Hkv
+        order = np.argsort([i * rep + h // Hkv for h, i in enumerate(idx)], kind="stable")
+        out = real(q[:, order], k, v).reshape(R, Hq, hd)
+        return out[:, np.argsort(order)].reshape(R, -1)
+    assert _fails(pins.pin_attention, attn=attn)
+    cfg = dataclasses.replace(ri.TINY_LLAMA, Hq=4, Hkv=2)
+    monkeypatch.setattr(orc, "causal_gqa_attention", attn)
+    assert _fails(pins.pin_single_segment_against_torch, cfg)
+
+
+def test_mutation_rmsnorm_no_eps():
+    assert _fails(pins.pin_rms_norm, rms_norm=lambda x, g, eps: orc.rms_norm(x, g, 0.0) * 1.0
+                  if eps == 0 else orc.rms_norm(x, g, 1e-2))
+
+
+def test_mutation_swapped_gate_up(monkeypatch):
+    monkeypatch.setattr(orc, "swiglu", lambda z, wg, wu, wd: (orc.silu(z @ wu) * (z @ wg)) @ wd)
+    assert _fails(pins.pin_single_segment_against_torch, ri.TINY_SWIGLU)
+    assert _fails(pins.pin_single_segment_against_torch, ri.TINY_LLAMA)
+
+
+def test_mutation_dropped_residual(monkeypatch):
+    monkeypatch.setattr(orc, "cell_norm_swiglu",
+                        lambda A, w, eps: orc.swiglu(orc.rms_norm(A, w["g2"], eps), w["wg"], w["wu"], w["wd"]))
+    assert _fails(pins.pin_shift_register, ri.TINY_SWIGLU)
+    assert _fails(pins.pin_single_segment_against_torch, ri.TINY_SWIGLU)
+
+
+def test_mutation_attention_scale(monkeypatch):
+    real = orc.causal_gqa_attention
+    monkeypatch.setattr(orc, "causal_gqa_attention", lambda q, k, v: real(q * 2.0, k, v))
+    assert _fails(pins.pin_single_segment_against_torch, ri.TINY_LLAMA)
