@@ -1,0 +1,226 @@
+/*
+ * rmt.h -- C ABI of the diagonal-batched recurrent-memory-transformer library
+ * (librmt.so, built for AMD Instinct MI355X / gfx950).
+ *
+ * The method.  A recurrent memory transformer (RMT) reads one long sequence
+ * as S segments of n tokens.  Layer l keeps m memory rows.  Cell (l, s)
+ * consumes A = [M(l, s-1); X(l-1, s)] (m memory rows, then n segment rows)
+ * and produces R = m + n rows Y; rows [0, n) become X(l, s), rows [n, R)
+ * become M(l, s).  Cell (l, s) needs only (l-1, s) and (l, s-1), so all
+ * cells on an anti-diagonal d = l + s are independent and run together, each
+ * with its own layer's weights, as one grouped launch per stage
+ * ("Diagonal Batching for Recurrent Memory Transformers", skill page:
+ * Core Concept; Architecture Overview -- Diagonal Reorganization, Dependency
+ * Preservation, GroupedGEMM Operations, GPU Kernel Optimization).  The
+ * reordering is exact and needs no retraining ("Diagonal Batching Unlocks
+ * Parallelism in Recurrent Memory Transformers for Long Contexts",
+ * abstract).
+ *
+ * Conventions shared by every call:
+ *   - Every call returns RMT_OK (0) or a negative error code; a thread-local
+ *     message describing the last error is returned by rmt_last_error().
+ *   - "device" pointers are HIP device allocations on the current device
+ *     (for example torch tensors' data_ptr()); "host" pointers are CPU memory.
+ *   - The library never takes ownership of caller memory.  Device work is
+ *     queued on the caller's HIP stream and returns before it finishes;
+ *     faults inside kernels surface at the caller's next synchronisation.
+ *   - Matrices are row-major.  Mathematical weights are W[d_in][d_out], so a
+ *     cell computes Y = A W.
+ */
+#ifndef RMT_H
+#define RMT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Error codes. */
+#define RMT_OK 0
+#define RMT_EINVAL (-1)        /* bad argument: sizes, null pointers, ranges      */
+#define RMT_EUNSUPPORTED (-2)  /* valid but not implemented (see each call)       */
+#define RMT_EHIP (-3)          /* a HIP runtime call failed (message has details) */
+#define RMT_ENOMEM (-4)        /* device allocation failed                         */
+
+/* Cell kinds: what one (layer, segment) cell computes on A [R x d].
+ *   LINEAR_GELU  Y = GELU_erf(A W_l + b_l)                        (fp32 only)
+ *   NORM_SWIGLU  Y = A + SwiGLU_l(RMSNorm_l(A))                    (bf16 only)
+ *   LLAMA        H = A + Attn_l(RMSNorm1_l(A)) Wo_l;
+ *                Y = H + SwiGLU_l(RMSNorm2_l(H))                   (bf16 only)
+ * with RMSNorm(x) = x * rsqrt(mean(x^2) + eps) * g,
+ * SwiGLU(z) = (silu(z Wg) * (z Wu)) Wd, and Attn causal over the cell's R
+ * rows with grouped-query heads (query head h reads KV head h / (Hq/Hkv)),
+ * rotate-half RoPE at positions 0..R-1 within the cell, scale 1/sqrt(hd). */
+#define RMT_CELL_LINEAR_GELU 0
+#define RMT_CELL_NORM_SWIGLU 1
+#define RMT_CELL_LLAMA 2
+
+/* Storage / arithmetic types. */
+#define RMT_F32 0
+#define RMT_BF16 1
+
+typedef struct rmt_config {
+  int32_t cell;        /* RMT_CELL_*                                          */
+  int32_t dtype;       /* RMT_F32 (LINEAR_GELU) or RMT_BF16 (the other cells) */
+  int32_t L;           /* layers                                              */
+  int32_t S;           /* segments per forward call                           */
+  int32_t n;           /* segment tokens                                      */
+  int32_t m;           /* memory rows per layer                               */
+  int32_t d;           /* model width                                         */
+  int32_t n_heads;     /* LLAMA: query heads Hq                               */
+  int32_t n_kv_heads;  /* LLAMA: key/value heads Hkv (Hq/Hkv a multiple of 4) */
+  int32_t head_dim;    /* LLAMA: hd, 64 or 128; Hq*hd == d                    */
+  int32_t ffn;         /* NORM_SWIGLU, LLAMA: SwiGLU width F                  */
+  int32_t vocab;       /* LLAMA: embedding rows V                             */
+  float eps;           /* RMSNorm epsilon                                     */
+  float rope_theta;    /* LLAMA: RoPE base                                    */
+} rmt_config;
+
+/* Mathematical-layout weights, stacked over layers (device pointers).  They
+ * are read once by rmt_model_create, which packs them into the library's own
+ * device layout; the caller may free them afterwards -- except `embed`,
+ * which the model keeps borrowing and must outlive it.  Element type of the
+ * matrices: fp32 for RMT_F32 models; bf16 (or fp32, rounded to nearest even
+ * while packing) for RMT_BF16 models, as given by `weight_dtype`.  Gains
+ * g1, g2 and bias b are always fp32.  Unused fields may be NULL.
+ *   LINEAR_GELU: w [L][d][d], b [L][d]
+ *   NORM_SWIGLU: g2 [L][d], wg [L][d][F], wu [L][d][F], wd [L][F][d]
+ *   LLAMA:       g1 [L][d], wqkv [L][d][(Hq+2Hkv)*hd] (columns: Q heads,
+ *                then K heads, then V heads, hd each), wo [L][Hq*hd][d],
+ *                g2, wg, wu, wd as above, embed [V][d] (bf16). */
+typedef struct rmt_weights {
+  int32_t weight_dtype;  /* RMT_F32 or RMT_BF16: element type of w/wqkv/wo/wg/wu/wd */
+  const void* w;
+  const float* b;
+  const float* g1;
+  const void* wqkv;
+  const void* wo;
+  const float* g2;
+  const void* wg;
+  const void* wu;
+  const void* wd;
+  const void* embed;
+} rmt_weights;
+
+/* Outputs of a forward call (device pointers, caller-allocated).
+ *   hidden [S*n][d] fp32: X(L-1, s) for every segment, in segment order.
+ *   mem    [L][m][d] fp32: M(l, S-1), the memory after the last segment;
+ *          it may alias the mem0 argument (in-place state update). */
+typedef struct rmt_output {
+  float* hidden;
+  float* mem;
+} rmt_output;
+
+typedef struct rmt_model rmt_model;
+
+/* Anti-diagonal schedule of the L x S (layer, segment) grid (host only,
+ * thread-safe; skill page, Implementation: the scheduler's enumeration).
+ * Diagonal k (k = 0 .. L+S-2) holds the cells (l, k-l) with 0 <= k-l < S,
+ * layers ascending; diagonal k has min(k+1, L, S, L+S-1-k) cells.
+ *   diag_ptr  host int32 [L+S]: diag_ptr[0] = 0, diag_ptr[k+1] - diag_ptr[k]
+ *             cells in diagonal k, diag_ptr[L+S-1] = L*S.
+ *   cells     host int32 [L*S][3]: (layer, segment, slot), slot = position
+ *             of the cell within its diagonal.
+ * Both pointers NULL: size query only.  Returns the number of diagonals
+ * (L+S-1) on success, RMT_EINVAL if L < 1, S < 1, L*S overflows int32 or
+ * exactly one pointer is NULL. */
+int32_t rmt_diag_schedule(int32_t L, int32_t S, int32_t* diag_ptr, int32_t* cells);
+
+/* Create a model on the current HIP device: validates `cfg`, allocates the
+ * packed weights and a workspace sized for min(L, S) <= L cells per diagonal
+ * (independent of S), packs `w` on `stream` (a hipStream_t; NULL = default
+ * stream) and waits for the packing to finish.  *out receives the handle.
+ * Errors: RMT_EINVAL (bad sizes or NULL weights the cell needs),
+ * RMT_EUNSUPPORTED (Hq/Hkv not a multiple of 4, hd not 64/128, widths not
+ * multiples of 64, ...), RMT_ENOMEM, RMT_EHIP. */
+int32_t rmt_model_create(const rmt_config* cfg, const rmt_weights* w, void* stream,
+                         rmt_model** out);
+
+/* Re-target the model to S segments per forward call (no allocation). */
+int32_t rmt_model_set_segments(rmt_model* model, int32_t S);
+
+/* Queue later forward calls on `stream` (a hipStream_t). */
+int32_t rmt_model_set_stream(rmt_model* model, void* stream);
+
+/* Bytes of device memory the model holds (packed weights + workspace). */
+int32_t rmt_model_device_bytes(const rmt_model* model, size_t* bytes);
+
+/* Diagonal-batched forward pass over one sequence of S*n tokens.
+ *   tokens  device: LLAMA -> int32 token ids [S*n] in [0, V) (ids outside
+ *           that range read a zero embedding row and set the flag reported
+ *           by rmt_model_check); other cells -> input rows X(-1, .) [S*n][d]
+ *           (fp32 for RMT_F32 models, bf16 for RMT_BF16 models).
+ *   mem0    device fp32 [L][m][d]: M(l, -1).
+ *   out     see rmt_output.
+ * For every diagonal k the library launches, on the model's stream, one
+ * grouped kernel per stage covering all of the diagonal's cells (skill page,
+ * Architecture Overview: GroupedGEMM Operations, GPU Kernel Optimization).
+ * Asynchronous.  Errors: RMT_EINVAL (NULL pointers), RMT_EHIP. */
+int32_t rmt_forward_diagonal(rmt_model* model, const void* tokens, const void* mem0,
+                             rmt_output* out);
+
+/* The same computation cell by cell, segment-major (for s: for l:), one cell
+ * per launch: the sequential RMT schedule the diagonal one replaces
+ * (catalogue record, abstract: "sequential RMT implementation").  Same
+ * arguments and results; bitwise equal to rmt_forward_diagonal. */
+int32_t rmt_forward_sequential(rmt_model* model, const void* tokens, const void* mem0,
+                               rmt_output* out);
+
+/* Synchronise the model's stream and report whether any forward call since
+ * the last check read a token id outside [0, V): *bad_tokens = 0 or 1. */
+int32_t rmt_model_check(rmt_model* model, int32_t* bad_tokens);
+
+/* Per-stage GPU timing.  When enabled, forward calls record a HIP event on
+ * the model's stream after every launch (and one before the first), so the
+ * time between consecutive events is one launch's duration on the stream.
+ * rmt_model_stage_times synchronises the stream and returns, for each stage
+ * (RMT_STAGE_*), the summed milliseconds, the number of launches, and the
+ * algorithmic flops and HBM bytes of those launches (compulsory operand and
+ * result traffic, no re-reads), then clears the totals.  Host arrays of
+ * RMT_NUM_STAGES entries; any of them may be NULL. */
+#define RMT_STAGE_GATHER 0
+#define RMT_STAGE_NORM1 1
+#define RMT_STAGE_QKV 2
+#define RMT_STAGE_ATTN 3
+#define RMT_STAGE_OPROJ 4
+#define RMT_STAGE_NORM2 5
+#define RMT_STAGE_GATEUP 6
+#define RMT_STAGE_DOWN 7
+#define RMT_STAGE_LINEAR 8
+#define RMT_NUM_STAGES 9
+int32_t rmt_model_enable_timing(rmt_model* model, int32_t enable);
+int32_t rmt_model_stage_times(rmt_model* model, double* ms, int64_t* launches, double* flops,
+                              double* bytes);
+
+/* Release the model's device memory (the caller's stream is synchronised
+ * first).  NULL is accepted. */
+int32_t rmt_model_destroy(rmt_model* model);
+
+/* Pack mathematical-layout weights src [L][K][N] (fp32 or bf16 per
+ * `src_dtype`, device) into the library's GEMM layout dst [L][N][K] bf16
+ * (device, caller-allocated, L*N*K*2 bytes), on `stream`.  K and N must be
+ * multiples of 8. */
+int32_t rmt_pack_weight(int32_t L, int32_t K, int32_t N, const void* src, int32_t src_dtype,
+                        void* dst, void* stream);
+
+/* The grouped GEMM on its own (Architecture Overview: GroupedGEMM Operations):
+ * C_g = A_g B_{layer[g]} for g < G, in one launch, bf16 MFMA with fp32
+ * accumulation, bf16 result (round to nearest even).
+ *   A           device bf16 [G][M][K]
+ *   B           device bf16 [Lw][N][K] as produced by rmt_pack_weight
+ *   group_layer host int32 [G], each in [0, Lw) (not checked against Lw)
+ *   C           device bf16 [G][M][N]
+ * 1 <= G <= 32 per call, K a multiple of 8, N a multiple of 64. */
+int32_t rmt_grouped_gemm(int32_t G, int32_t M, int32_t N, int32_t K, const void* A,
+                         const void* B, const int32_t* group_layer, void* C, void* stream);
+
+/* Thread-local description of the last error (empty string if none). */
+const char* rmt_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RMT_H */

@@ -1,0 +1,216 @@
+// Row-wise and layout kernels of the diagonal sweep (gfx950): RMSNorm over
+// every cell of a diagonal, the segment-input gather, the fp32 linear+GELU
+// cell, and weight packing.  All of them are HBM-bound; they read and write
+// full 16-byte (or 8-byte) vectors along rows.
+#include "kernels.h"
+
+namespace rmt {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint16_t to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// One wave per row, four rows per workgroup.  Row r of group g comes from
+// in_lo[g] (r < split_in) or in_hi[g]; the normalised row goes to the packed
+// bf16 matrix at row g*R + r.  Requires d % 4 == 0.
+__global__ __launch_bounds__(256) void rmsnorm_kernel(int total_rows, int R, int d, int split_in,
+                                                      GroupTable tab, const float* __restrict__ gamma,
+                                                      float eps, uint16_t* __restrict__ out) {
+  const int lane = (int)threadIdx.x & 63;
+  const int row = (int)blockIdx.x * 4 + ((int)threadIdx.x >> 6);
+  if (row >= total_rows) return;
+  const int g = row / R;
+  const int r = row - g * R;
+  const float* src = r < split_in ? (const float*)tab.in_lo[g] + (size_t)r * d
+                                  : (const float*)tab.in_hi[g] + (size_t)(r - split_in) * d;
+  const float* gm = gamma + (size_t)tab.layer[g] * d;
+  float ss = 0.f;
+  for (int c = lane * 4; c < d; c += 256) {
+    const f32x4 v = *(const f32x4*)(src + c);
+    ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
+  }
+  ss = wave_sum(ss);
+  const float inv = 1.0f / sqrtf(ss / (float)d + eps);
+  uint16_t* dst = out + (size_t)row * d;
+  for (int c = lane * 4; c < d; c += 256) {
+    const f32x4 v = *(const f32x4*)(src + c);
+    const f32x4 w = *(const f32x4*)(gm + c);
+    u16x4 o;
+    o[0] = to_bf16(v[0] * inv * w[0]);
+    o[1] = to_bf16(v[1] * inv * w[1]);
+    o[2] = to_bf16(v[2] * inv * w[2]);
+    o[3] = to_bf16(v[3] * inv * w[3]);
+    *(u16x4*)(dst + c) = o;
+  }
+}
+
+// Embedding lookup of one segment's n token ids into an fp32 slot.  An id
+// outside [0, V) reads as a zero row and raises *bad_flag.
+__global__ __launch_bounds__(256) void gather_tokens_kernel(int d, const int32_t* __restrict__ ids,
+                                                            int V, const uint16_t* __restrict__ embed,
+                                                            float* __restrict__ dst,
+                                                            int32_t* __restrict__ bad_flag) {
+  const int i = (int)blockIdx.x;
+  const int id = ids[i];
+  const bool ok = id >= 0 && id < V;
+  if (!ok && threadIdx.x == 0) *bad_flag = 1;
+  const uint16_t* src = embed + (size_t)(ok ? id : 0) * d;
+  float* o = dst + (size_t)i * d;
+  for (int c = (int)threadIdx.x * 4; c < d; c += 1024) {
+    f32x4 v = {0.f, 0.f, 0.f, 0.f};
+    if (ok) {
+      const u16x4 h = *(const u16x4*)(src + c);
+      v[0] = bf16_to_f32(h[0]);
+      v[1] = bf16_to_f32(h[1]);
+      v[2] = bf16_to_f32(h[2]);
+      v[3] = bf16_to_f32(h[3]);
+    }
+    *(f32x4*)(o + c) = v;
+  }
+}
+
+// bf16 input rows -> fp32 slot (the attention-free cell's segment inputs).
+__global__ __launch_bounds__(256) void copy_rows_bf16_kernel(int d, const uint16_t* __restrict__ src,
+                                                             float* __restrict__ dst) {
+  const size_t base = (size_t)blockIdx.x * d;
+  for (int c = (int)threadIdx.x * 4; c < d; c += 1024) {
+    const u16x4 h = *(const u16x4*)(src + base + c);
+    f32x4 v;
+    v[0] = bf16_to_f32(h[0]);
+    v[1] = bf16_to_f32(h[1]);
+    v[2] = bf16_to_f32(h[2]);
+    v[3] = bf16_to_f32(h[3]);
+    *(f32x4*)(dst + base + c) = v;
+  }
+}
+
+// fp32 linear + bias + exact GELU for one diagonal.  Thread (row, col) of
+// group g sums A[row][k] W[k][col] for k = 0..d-1 in order with fused
+// multiply-adds; rows of A come from in_lo/in_hi, rows of Y go to
+// out_lo/out_hi (X(l, s) and M(l, s)).  W is [L][d][d] in the mathematical
+// layout, so consecutive threads read consecutive columns.
+__global__ __launch_bounds__(256) void linear_gelu_f32_kernel(int R, int d, int split_in, int split_out,
+                                                              GroupTable tab, const float* __restrict__ W,
+                                                              const float* __restrict__ bias) {
+  const int col = (int)blockIdx.x * 64 + ((int)threadIdx.x & 63);
+  const int row = (int)blockIdx.y * 4 + ((int)threadIdx.x >> 6);
+  const int g = (int)blockIdx.z;
+  if (col >= d || row >= R) return;
+  const int l = tab.layer[g];
+  const float* a = row < split_in ? (const float*)tab.in_lo[g] + (size_t)row * d
+                                  : (const float*)tab.in_hi[g] + (size_t)(row - split_in) * d;
+  const float* w = W + (size_t)l * d * d + col;
+  float acc = 0.f;
+  for (int k = 0; k < d; ++k) acc = fmaf(a[k], w[(size_t)k * d], acc);
+  const float z = acc + bias[(size_t)l * d + col];
+  const float y = 0.5f * z * (1.0f + erff(z * 0.70710678118654752f));
+  float* o = row < split_out ? (float*)tab.out_lo[g] + (size_t)row * d
+                             : (float*)tab.out_hi[g] + (size_t)(row - split_out) * d;
+  o[col] = y;
+}
+
+// dst[l][r][k] (bf16) from src[l][k][col(r)] through a 64 x 64 LDS tile.
+template <bool SRC_BF16>
+__global__ __launch_bounds__(256) void pack_kernel(int K, int N_src, const void* __restrict__ src0,
+                                                   const void* __restrict__ src1, int interleave,
+                                                   uint16_t* __restrict__ dst) {
+  __shared__ uint16_t tile[64][65];
+  const int N_dst = interleave ? 2 * N_src : N_src;
+  const int r0 = (int)blockIdx.x * 64;
+  const int k0 = (int)blockIdx.y * 64;
+  const int l = (int)blockIdx.z;
+  const int tx = (int)threadIdx.x & 63;
+  const int ty = (int)threadIdx.x >> 6;
+  // source column and source tensor of destination row r0 + tx
+  const int r = r0 + tx;
+  int col = r;
+  const void* src = src0;
+  if (interleave) {
+    const int blk = r >> 6, j = r & 63;
+    col = blk * 32 + (j & 31);
+    src = j < 32 ? src0 : src1;
+  }
+  for (int i = ty; i < 64; i += 4) {
+    const int k = k0 + i;
+    uint16_t v = 0;
+    if (k < K && r < N_dst) {
+      const size_t idx = ((size_t)l * K + k) * N_src + col;
+      if (SRC_BF16) v = ((const uint16_t*)src)[idx];
+      else v = to_bf16(((const float*)src)[idx]);
+    }
+    tile[i][tx] = v;
+  }
+  __syncthreads();
+  for (int i = ty; i < 64; i += 4) {
+    const int rr = r0 + i;
+    const int k = k0 + tx;
+    if (rr < N_dst && k < K) dst[((size_t)l * N_dst + rr) * K + k] = tile[tx][i];
+  }
+}
+
+}  // namespace
+
+hipError_t launch_rmsnorm(int G, int R, int d, int split_in, const GroupTable& tab,
+                          const float* gamma, float eps, uint16_t* out, hipStream_t stream) {
+  const int rows = G * R;
+  if (rows == 0) return hipSuccess;
+  hipLaunchKernelGGL(rmsnorm_kernel, dim3((rows + 3) / 4), dim3(256), 0, stream, rows, R, d,
+                     split_in, tab, gamma, eps, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_tokens(int n, int d, const int32_t* ids, int V, const uint16_t* embed,
+                                float* dst, int32_t* bad_flag, hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(gather_tokens_kernel, dim3(n), dim3(256), 0, stream, d, ids, V, embed, dst,
+                     bad_flag);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_rows_bf16(int n, int d, const uint16_t* src, float* dst,
+                                 hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(copy_rows_bf16_kernel, dim3(n), dim3(256), 0, stream, d, src, dst);
+  return hipGetLastError();
+}
+
+hipError_t launch_linear_gelu_f32(int G, int R, int d, int split_in, int split_out,
+                                  const GroupTable& tab, const float* W, const float* bias,
+                                  hipStream_t stream) {
+  if (G == 0) return hipSuccess;
+  dim3 grid((d + 63) / 64, (R + 3) / 4, G);
+  hipLaunchKernelGGL(linear_gelu_f32_kernel, grid, dim3(256), 0, stream, R, d, split_in,
+                     split_out, tab, W, bias);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack(int L, int K, int N_src, const void* src0, const void* src1,
+                       int src_is_bf16, int interleave, uint16_t* dst, hipStream_t stream) {
+  const int N_dst = interleave ? 2 * N_src : N_src;
+  dim3 grid((N_dst + 63) / 64, (K + 63) / 64, L);
+  if (src_is_bf16)
+    hipLaunchKernelGGL(pack_kernel<true>, grid, dim3(256), 0, stream, K, N_src, src0, src1,
+                       interleave, dst);
+  else
+    hipLaunchKernelGGL(pack_kernel<false>, grid, dim3(256), 0, stream, K, N_src, src0, src1,
+                       interleave, dst);
+  return hipGetLastError();
+}
+
+}  // namespace rmt

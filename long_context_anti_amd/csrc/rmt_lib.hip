@@ -1,0 +1,617 @@
+// Host runtime of librmt.so: the C ABI declared in include/rmt.h.
+//
+// The diagonal driver walks the anti-diagonals d = l + s of the
+// (layer, segment) grid ("Diagonal Batching for Recurrent Memory
+// Transformers", skill page: Implementation, the scheduler's enumeration;
+// Architecture Overview, Diagonal Reorganization) and, for each diagonal,
+// queues one grouped launch per stage of the cell over all of the diagonal's
+// cells.  The per-cell group table (layer id and row pointers) travels in the
+// kernel arguments, so no device memory depends on the number of segments.
+//
+// Buffers and hazards.  Two facts keep the grouped launches race-free:
+//   * X(l, s) goes to a ping-pong pair: a cell on diagonal k reads slot l of
+//     buffer (k+1) % 2 and writes slot l+1 of buffer k % 2.  Cell (l-1, s+1)
+//     of the same diagonal therefore never overwrites the X(l-1, s) that
+//     cell (l, s) is reading.  Slot 0 holds the segment's input rows.
+//   * M(l, s) goes to one of two memory buffers by the parity of s: the one
+//     the caller asked for (out->mem) when S-1-s is even, the workspace copy
+//     otherwise.  A cell reads M(l, s-1) from one and writes M(l, s) to the
+//     other, so the write-back never lands on rows another tile of the same
+//     launch still reads as its residual, and M(., S-1) ends in out->mem
+//     without a final copy.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/rmt.h"
+#include "kernels.h"
+
+using namespace rmt;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int32_t fail(int32_t code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+#define HIP_TRY(expr)                                                                   \
+  do {                                                                                  \
+    hipError_t e_ = (expr);                                                             \
+    if (e_ != hipSuccess)                                                               \
+      return fail(RMT_EHIP, "%s failed: %s", #expr, hipGetErrorString(e_));             \
+  } while (0)
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace
+
+struct rmt_model {
+  rmt_config cfg{};
+  hipStream_t stream = nullptr;
+  void* block = nullptr;   // the single device allocation
+  size_t bytes = 0;
+
+  // packed weights (bf16, [L][N][K]) and gains (fp32)
+  uint16_t* wqkv = nullptr;
+  uint16_t* wo = nullptr;
+  uint16_t* wgu = nullptr;
+  uint16_t* wd = nullptr;
+  float* g1 = nullptr;
+  float* g2 = nullptr;
+  float* w32 = nullptr;    // LINEAR_GELU: [L][d][d]
+  float* b32 = nullptr;    // LINEAR_GELU: [L][d]
+  const uint16_t* embed = nullptr;  // borrowed
+  float2* rope = nullptr;  // [R][hd/2] (cos, sin)
+
+  // workspace (sized for L cells per diagonal)
+  uint16_t* abuf = nullptr;  // normalised rows, bf16 [L*R][d]
+  uint16_t* qkv = nullptr;   // [L*R][Nqkv]
+  uint16_t* att = nullptr;   // [L*R][Hq*hd]
+  float* hbuf = nullptr;     // [L*R][d]
+  uint16_t* ubuf = nullptr;  // [L*R][F]
+  float* xbuf[2] = {nullptr, nullptr};  // [L][n][d] each
+  float* memw = nullptr;     // [L][m][d]
+  int32_t* flag = nullptr;   // bad-token flag
+
+  // timing
+  bool timing = false;
+  std::vector<hipEvent_t> events;   // pool
+  size_t ev_used = 0;
+  std::vector<int> ev_stage;        // stage of the launch that ends at event i (-1: start marker)
+  std::vector<double> ev_flops, ev_bytes;
+};
+
+namespace {
+
+int nqkv(const rmt_config& c) { return (c.n_heads + 2 * c.n_kv_heads) * c.head_dim; }
+
+int32_t validate_config(const rmt_config* c) {
+  if (!c) return fail(RMT_EINVAL, "config is NULL");
+  if (c->L < 1 || c->S < 1 || c->n < 1 || c->m < 1 || c->d < 1)
+    return fail(RMT_EINVAL, "L, S, n, m, d must be >= 1 (got %d, %d, %d, %d, %d)", c->L, c->S, c->n,
+                c->m, c->d);
+  const int64_t R = (int64_t)c->n + c->m;
+  if (c->cell == RMT_CELL_LINEAR_GELU) {
+    if (c->dtype != RMT_F32) return fail(RMT_EUNSUPPORTED, "LINEAR_GELU cells run in fp32 only");
+    if ((int64_t)c->L * R * c->d > INT32_MAX) return fail(RMT_EINVAL, "sizes overflow int32");
+    return RMT_OK;
+  }
+  if (c->cell != RMT_CELL_NORM_SWIGLU && c->cell != RMT_CELL_LLAMA)
+    return fail(RMT_EINVAL, "unknown cell kind %d", c->cell);
+  if (c->dtype != RMT_BF16) return fail(RMT_EUNSUPPORTED, "this cell kind runs in bf16 only");
+  if (c->d % 64 != 0) return fail(RMT_EUNSUPPORTED, "d must be a multiple of 64 (got %d)", c->d);
+  if (c->ffn < 1 || c->ffn % 32 != 0)
+    return fail(RMT_EUNSUPPORTED, "ffn must be a positive multiple of 32 (got %d)", c->ffn);
+  if (!(c->eps >= 0.f)) return fail(RMT_EINVAL, "eps must be >= 0");
+  int64_t widest = std::max<int64_t>(c->d, c->ffn);
+  if (c->cell == RMT_CELL_LLAMA) {
+    if (c->n_heads < 1 || c->n_kv_heads < 1 || c->n_heads % c->n_kv_heads != 0)
+      return fail(RMT_EINVAL, "n_heads must be a positive multiple of n_kv_heads");
+    if ((c->n_heads / c->n_kv_heads) % 4 != 0)
+      return fail(RMT_EUNSUPPORTED, "n_heads / n_kv_heads must be a multiple of 4");
+    if (c->head_dim != 64 && c->head_dim != 128)
+      return fail(RMT_EUNSUPPORTED, "head_dim must be 64 or 128 (got %d)", c->head_dim);
+    if (c->n_heads * c->head_dim != c->d)
+      return fail(RMT_EUNSUPPORTED, "n_heads * head_dim must equal d");
+    if (c->vocab < 1) return fail(RMT_EINVAL, "vocab must be >= 1");
+    if (!(c->rope_theta > 0.f)) return fail(RMT_EINVAL, "rope_theta must be > 0");
+    widest = std::max<int64_t>(widest, nqkv(*c));
+  }
+  if ((int64_t)c->L * R * 2 * widest > INT32_MAX) return fail(RMT_EINVAL, "sizes overflow int32");
+  if ((int64_t)c->S * c->n * c->d > ((int64_t)1 << 40)) return fail(RMT_EINVAL, "sequence too long");
+  return RMT_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Timing helpers
+// ---------------------------------------------------------------------------
+
+int32_t mark(rmt_model* M, int stage, double flops, double bytes) {
+  if (!M->timing) return RMT_OK;
+  if (M->ev_used == M->events.size()) {
+    hipEvent_t e;
+    HIP_TRY(hipEventCreate(&e));
+    M->events.push_back(e);
+  }
+  HIP_TRY(hipEventRecord(M->events[M->ev_used], M->stream));
+  M->ev_used++;
+  M->ev_stage.push_back(stage);
+  M->ev_flops.push_back(flops);
+  M->ev_bytes.push_back(bytes);
+  return RMT_OK;
+}
+
+#define LAUNCH(expr)                                                                     \
+  do {                                                                                   \
+    hipError_t e_ = (expr);                                                              \
+    if (e_ != hipSuccess) return fail(RMT_EHIP, "%s: %s", #expr, hipGetErrorString(e_)); \
+  } while (0)
+
+#define MARK(stage, fl, by)                          \
+  do {                                               \
+    int32_t r_ = mark(M, (stage), (fl), (by));       \
+    if (r_ != RMT_OK) return r_;                     \
+  } while (0)
+
+struct Cell {
+  int l, s;
+};
+
+// Queue every stage of the cells in `cells` (all on anti-diagonal k, at most
+// kMaxGroups of them).
+int32_t run_cells(rmt_model* M, const Cell* cells, int G, const void* tokens, const rmt_output* out) {
+  const rmt_config& c = M->cfg;
+  const int L = c.L, S = c.S, n = c.n, m = c.m, d = c.d;
+  const int R = n + m;
+  const int k = cells[0].l + cells[0].s;
+  float* xr = M->xbuf[(k + 1) & 1];
+  float* xw = M->xbuf[k & 1];
+  auto slot = [&](float* buf, int l) { return buf + (size_t)l * n * d; };
+  auto mem_buf = [&](int s) { return ((S - 1 - s) % 2 == 0) ? out->mem : M->memw; };
+  const double G_ = G;
+
+  // Cell inputs [M(l, s-1); X(l-1, s)] and outputs X(l, s), M(l, s).
+  const void* in_lo[kMaxGroups];
+  const void* in_hi[kMaxGroups];
+  void* x_out[kMaxGroups];
+  void* m_out[kMaxGroups];
+  for (int g = 0; g < G; ++g) {
+    const int l = cells[g].l, s = cells[g].s;
+    in_lo[g] = mem_buf(s - 1) + (size_t)l * m * d;
+    if (l == 0 && c.cell == RMT_CELL_LINEAR_GELU)
+      in_hi[g] = (const float*)tokens + (size_t)s * n * d;   // fp32 input rows, read in place
+    else
+      in_hi[g] = slot(xr, l);
+    x_out[g] = (l == L - 1) ? (void*)(out->hidden + (size_t)s * n * d) : (void*)slot(xw, l + 1);
+    m_out[g] = mem_buf(s) + (size_t)l * m * d;
+    if (l == 0 && c.cell != RMT_CELL_LINEAR_GELU) {
+      // X(-1, s): this segment's input rows, into slot 0 of the read buffer.
+      if (c.cell == RMT_CELL_LLAMA) {
+        LAUNCH(launch_gather_tokens(n, d, (const int32_t*)tokens + (size_t)s * n, c.vocab, M->embed,
+                                    slot(xr, 0), M->flag, M->stream));
+        MARK(RMT_STAGE_GATHER, 0.0, (double)n * (4 + (size_t)d * 6));
+      } else {
+        LAUNCH(launch_copy_rows_bf16(n, d, (const uint16_t*)tokens + (size_t)s * n * d, slot(xr, 0),
+                                     M->stream));
+        MARK(RMT_STAGE_GATHER, 0.0, (double)n * d * 6);
+      }
+    }
+  }
+
+  GroupTable tab;
+  std::memset(&tab, 0, sizeof(tab));
+  tab.G = G;
+  for (int g = 0; g < G; ++g) tab.layer[g] = cells[g].l;
+  auto set_io = [&](const void* const* lo, const void* const* hi, void* const* olo, void* const* ohi) {
+    for (int g = 0; g < G; ++g) {
+      tab.in_lo[g] = lo ? lo[g] : nullptr;
+      tab.in_hi[g] = hi ? hi[g] : nullptr;
+      tab.out_lo[g] = olo ? olo[g] : nullptr;
+      tab.out_hi[g] = ohi ? ohi[g] : nullptr;
+    }
+  };
+  const double rows = G_ * R;
+
+  if (c.cell == RMT_CELL_LINEAR_GELU) {
+    set_io(in_lo, in_hi, x_out, m_out);
+    LAUNCH(launch_linear_gelu_f32(G, R, d, m, n, tab, M->w32, M->b32, M->stream));
+    MARK(RMT_STAGE_LINEAR, 2.0 * rows * d * d, rows * d * 8 + G_ * d * (d + 1) * 4);
+    return RMT_OK;
+  }
+
+  const int F = c.ffn;
+  const void* packed_lo[kMaxGroups];
+  void* packed_out[kMaxGroups];
+  GemmArgs ga;
+  std::memset(&ga, 0, sizeof(ga));
+
+  if (c.cell == RMT_CELL_LLAMA) {
+    const int hd = c.head_dim, Hq = c.n_heads, Hkv = c.n_kv_heads, NQ = nqkv(c);
+    // RMSNorm 1 of [M(l, s-1); X(l-1, s)]
+    set_io(in_lo, in_hi, nullptr, nullptr);
+    LAUNCH(launch_rmsnorm(G, R, d, m, tab, M->g1, c.eps, M->abuf, M->stream));
+    MARK(RMT_STAGE_NORM1, 0.0, rows * d * 6);
+    // QKV projection + RoPE on Q and K
+    for (int g = 0; g < G; ++g) packed_out[g] = M->qkv + (size_t)g * R * NQ;
+    set_io(nullptr, nullptr, packed_out, nullptr);
+    ga.A = M->abuf; ga.B = M->wqkv; ga.M = R; ga.N = NQ; ga.K = d;
+    ga.split_in = R; ga.split_out = R; ga.ld_res = 0; ga.ld_out = NQ;
+    ga.rope = M->rope; ga.rope_cols = (Hq + Hkv) * hd; ga.hd = hd;
+    LAUNCH(launch_gemm_bf16(EPI_QKV_ROPE, ga, tab, M->stream));
+    MARK(RMT_STAGE_QKV, 2.0 * rows * d * NQ, rows * d * 2 + G_ * NQ * d * 2 + rows * NQ * 2);
+    // causal GQA attention inside each cell
+    LAUNCH(launch_attention(M->qkv, M->att, G, R, Hq, Hkv, hd, M->stream));
+    MARK(RMT_STAGE_ATTN, 2.0 * G_ * Hq * hd * (double)R * (R + 1), rows * NQ * 2 + rows * Hq * hd * 2);
+    // O projection + residual A -> H
+    for (int g = 0; g < G; ++g) packed_out[g] = M->hbuf + (size_t)g * R * d;
+    set_io(in_lo, in_hi, packed_out, nullptr);
+    ga.A = M->att; ga.B = M->wo; ga.M = R; ga.N = d; ga.K = Hq * hd;
+    ga.split_in = m; ga.split_out = R; ga.ld_res = d; ga.ld_out = d;
+    LAUNCH(launch_gemm_bf16(EPI_RESID_F32, ga, tab, M->stream));
+    MARK(RMT_STAGE_OPROJ, 2.0 * rows * Hq * hd * d,
+         rows * Hq * hd * 2 + G_ * d * Hq * hd * 2 + rows * d * 8);
+    // RMSNorm 2 of H
+    for (int g = 0; g < G; ++g) packed_lo[g] = M->hbuf + (size_t)g * R * d;
+    set_io(packed_lo, packed_lo, nullptr, nullptr);
+    LAUNCH(launch_rmsnorm(G, R, d, R, tab, M->g2, c.eps, M->abuf, M->stream));
+    MARK(RMT_STAGE_NORM2, 0.0, rows * d * 6);
+  } else {
+    // NORM_SWIGLU: RMSNorm of [M(l, s-1); X(l-1, s)]
+    set_io(in_lo, in_hi, nullptr, nullptr);
+    LAUNCH(launch_rmsnorm(G, R, d, m, tab, M->g2, c.eps, M->abuf, M->stream));
+    MARK(RMT_STAGE_NORM2, 0.0, rows * d * 6);
+  }
+
+  // gate/up projection + SwiGLU -> U
+  for (int g = 0; g < G; ++g) packed_out[g] = M->ubuf + (size_t)g * R * F;
+  set_io(nullptr, nullptr, packed_out, nullptr);
+  ga.A = M->abuf; ga.B = M->wgu; ga.M = R; ga.N = 2 * F; ga.K = d;
+  ga.split_in = R; ga.split_out = R; ga.ld_res = 0; ga.ld_out = F;
+  LAUNCH(launch_gemm_bf16(EPI_SWIGLU, ga, tab, M->stream));
+  MARK(RMT_STAGE_GATEUP, 2.0 * rows * d * 2 * F, rows * d * 2 + G_ * 2 * F * d * 2 + rows * F * 2);
+
+  // down projection + residual; rows [0, n) -> X(l, s), rows [n, R) -> M(l, s)
+  if (c.cell == RMT_CELL_LLAMA) {
+    for (int g = 0; g < G; ++g) packed_lo[g] = M->hbuf + (size_t)g * R * d;
+    set_io(packed_lo, packed_lo, x_out, m_out);
+    ga.split_in = R;
+  } else {
+    set_io(in_lo, in_hi, x_out, m_out);
+    ga.split_in = m;
+  }
+  ga.A = M->ubuf; ga.B = M->wd; ga.M = R; ga.N = d; ga.K = F;
+  ga.split_out = n; ga.ld_res = d; ga.ld_out = d;
+  LAUNCH(launch_gemm_bf16(EPI_RESID_F32, ga, tab, M->stream));
+  MARK(RMT_STAGE_DOWN, 2.0 * rows * F * d, rows * F * 2 + G_ * d * F * 2 + rows * d * 8);
+  return RMT_OK;
+}
+
+int32_t check_forward_args(rmt_model* M, const void* tokens, const void* mem0, const rmt_output* out) {
+  if (!M) return fail(RMT_EINVAL, "model is NULL");
+  if (!tokens || !mem0 || !out || !out->hidden || !out->mem)
+    return fail(RMT_EINVAL, "tokens, mem0, out, out->hidden and out->mem must be non-NULL");
+  return RMT_OK;
+}
+
+int32_t start_forward(rmt_model* M, const void* mem0, const rmt_output* out) {
+  const rmt_config& c = M->cfg;
+  const size_t mem_bytes = (size_t)c.L * c.m * c.d * sizeof(float);
+  // M(l, -1) lives in the buffer that segment -1 maps to (see the header).
+  float* dst = ((c.S - 1 - (-1)) % 2 == 0) ? out->mem : M->memw;
+  MARK(-1, 0.0, 0.0);
+  if ((const void*)dst != mem0) {
+    HIP_TRY(hipMemcpyAsync(dst, mem0, mem_bytes, hipMemcpyDeviceToDevice, M->stream));
+    MARK(RMT_STAGE_GATHER, 0.0, 2.0 * mem_bytes);
+  }
+  return RMT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* rmt_last_error(void) { return g_last_error.c_str(); }
+
+int32_t rmt_diag_schedule(int32_t L, int32_t S, int32_t* diag_ptr, int32_t* cells) {
+  if (L < 1 || S < 1) return fail(RMT_EINVAL, "L and S must be >= 1 (got %d, %d)", L, S);
+  if ((int64_t)L * S > INT32_MAX || (int64_t)L + S > INT32_MAX)
+    return fail(RMT_EINVAL, "L*S overflows int32");
+  const int32_t ndiag = L + S - 1;
+  if (!diag_ptr && !cells) return ndiag;
+  if (!diag_ptr || !cells) return fail(RMT_EINVAL, "diag_ptr and cells must both be NULL or both set");
+  int32_t idx = 0;
+  diag_ptr[0] = 0;
+  for (int32_t k = 0; k < ndiag; ++k) {
+    const int32_t l_lo = std::max(0, k - S + 1), l_hi = std::min(L - 1, k);
+    int32_t slot = 0;
+    for (int32_t l = l_lo; l <= l_hi; ++l, ++slot, ++idx) {
+      cells[3 * idx + 0] = l;
+      cells[3 * idx + 1] = k - l;
+      cells[3 * idx + 2] = slot;
+    }
+    diag_ptr[k + 1] = idx;
+  }
+  return ndiag;
+}
+
+int32_t rmt_model_create(const rmt_config* cfg, const rmt_weights* w, void* stream,
+                         rmt_model** out) {
+  if (!out) return fail(RMT_EINVAL, "out is NULL");
+  *out = nullptr;
+  int32_t rc = validate_config(cfg);
+  if (rc != RMT_OK) return rc;
+  if (!w) return fail(RMT_EINVAL, "weights are NULL");
+  const rmt_config& c = *cfg;
+  const int L = c.L, n = c.n, m = c.m, d = c.d, R = n + m;
+  if (c.cell == RMT_CELL_LINEAR_GELU) {
+    if (!w->w || !w->b) return fail(RMT_EINVAL, "LINEAR_GELU needs w and b");
+    if (w->weight_dtype != RMT_F32) return fail(RMT_EUNSUPPORTED, "LINEAR_GELU weights must be fp32");
+  } else {
+    if (!w->g2 || !w->wg || !w->wu || !w->wd) return fail(RMT_EINVAL, "g2, wg, wu and wd are required");
+    if (c.cell == RMT_CELL_LLAMA && (!w->g1 || !w->wqkv || !w->wo || !w->embed))
+      return fail(RMT_EINVAL, "LLAMA needs g1, wqkv, wo and embed");
+    if (w->weight_dtype != RMT_F32 && w->weight_dtype != RMT_BF16)
+      return fail(RMT_EINVAL, "weight_dtype must be RMT_F32 or RMT_BF16");
+  }
+
+  rmt_model* M = new rmt_model();
+  M->cfg = c;
+  M->stream = (hipStream_t)stream;
+
+  // Carve one allocation.
+  const size_t F = (size_t)c.ffn;
+  const size_t NQ = c.cell == RMT_CELL_LLAMA ? (size_t)nqkv(c) : 0;
+  const size_t HQD = c.cell == RMT_CELL_LLAMA ? (size_t)c.n_heads * c.head_dim : 0;
+  const size_t rowsL = (size_t)L * R;
+  struct Piece { void** ptr; size_t bytes; };
+  std::vector<Piece> pieces;
+  if (c.cell == RMT_CELL_LINEAR_GELU) {
+    pieces.push_back({(void**)&M->w32, (size_t)L * d * d * 4});
+    pieces.push_back({(void**)&M->b32, (size_t)L * d * 4});
+  } else {
+    pieces.push_back({(void**)&M->wgu, (size_t)L * 2 * F * d * 2});
+    pieces.push_back({(void**)&M->wd, (size_t)L * d * F * 2});
+    pieces.push_back({(void**)&M->g2, (size_t)L * d * 4});
+    pieces.push_back({(void**)&M->abuf, rowsL * d * 2});
+    pieces.push_back({(void**)&M->ubuf, rowsL * F * 2});
+    if (c.cell == RMT_CELL_LLAMA) {
+      pieces.push_back({(void**)&M->wqkv, (size_t)L * NQ * d * 2});
+      pieces.push_back({(void**)&M->wo, (size_t)L * d * HQD * 2});
+      pieces.push_back({(void**)&M->g1, (size_t)L * d * 4});
+      pieces.push_back({(void**)&M->rope, (size_t)R * (c.head_dim / 2) * sizeof(float2)});
+      pieces.push_back({(void**)&M->qkv, rowsL * NQ * 2});
+      pieces.push_back({(void**)&M->att, rowsL * HQD * 2});
+      pieces.push_back({(void**)&M->hbuf, rowsL * d * 4});
+    }
+  }
+  pieces.push_back({(void**)&M->xbuf[0], (size_t)L * n * d * 4});
+  pieces.push_back({(void**)&M->xbuf[1], (size_t)L * n * d * 4});
+  pieces.push_back({(void**)&M->memw, (size_t)L * m * d * 4});
+  pieces.push_back({(void**)&M->flag, 256});
+  size_t total = 0;
+  for (auto& p : pieces) total = align_up(total, 256) + p.bytes;
+  total = align_up(total, 256);
+  hipError_t e = hipMalloc(&M->block, total);
+  if (e != hipSuccess) {
+    delete M;
+    return fail(RMT_ENOMEM, "hipMalloc(%zu) failed: %s", total, hipGetErrorString(e));
+  }
+  M->bytes = total;
+  size_t off = 0;
+  for (auto& p : pieces) {
+    off = align_up(off, 256);
+    *p.ptr = (char*)M->block + off;
+    off += p.bytes;
+  }
+
+  auto bail = [&](int32_t code) {
+    (void)hipFree(M->block);
+    delete M;
+    return code;
+  };
+#define CREATE_TRY(expr)                                                              \
+  do {                                                                                \
+    hipError_t e_ = (expr);                                                           \
+    if (e_ != hipSuccess) return bail(fail(RMT_EHIP, "%s: %s", #expr, hipGetErrorString(e_))); \
+  } while (0)
+
+  hipStream_t st = M->stream;
+  CREATE_TRY(hipMemsetAsync(M->flag, 0, 256, st));
+  if (c.cell == RMT_CELL_LINEAR_GELU) {
+    CREATE_TRY(hipMemcpyAsync(M->w32, w->w, (size_t)L * d * d * 4, hipMemcpyDeviceToDevice, st));
+    CREATE_TRY(hipMemcpyAsync(M->b32, w->b, (size_t)L * d * 4, hipMemcpyDeviceToDevice, st));
+  } else {
+    const int bf = w->weight_dtype == RMT_BF16;
+    CREATE_TRY(launch_pack(L, d, (int)F, w->wg, w->wu, bf, 1, M->wgu, st));
+    CREATE_TRY(launch_pack(L, (int)F, d, w->wd, nullptr, bf, 0, M->wd, st));
+    CREATE_TRY(hipMemcpyAsync(M->g2, w->g2, (size_t)L * d * 4, hipMemcpyDeviceToDevice, st));
+    if (c.cell == RMT_CELL_LLAMA) {
+      CREATE_TRY(launch_pack(L, d, (int)NQ, w->wqkv, nullptr, bf, 0, M->wqkv, st));
+      CREATE_TRY(launch_pack(L, (int)HQD, d, w->wo, nullptr, bf, 0, M->wo, st));
+      CREATE_TRY(hipMemcpyAsync(M->g1, w->g1, (size_t)L * d * 4, hipMemcpyDeviceToDevice, st));
+      M->embed = (const uint16_t*)w->embed;
+      // RoPE table: angle p * theta^(-2i/hd) in double precision.
+      const int half = c.head_dim / 2;
+      std::vector<float2> tab((size_t)R * half);
+      for (int p = 0; p < R; ++p)
+        for (int i = 0; i < half; ++i) {
+          const double ang = (double)p * std::pow((double)c.rope_theta, -2.0 * i / c.head_dim);
+          tab[(size_t)p * half + i] = make_float2((float)std::cos(ang), (float)std::sin(ang));
+        }
+      CREATE_TRY(hipMemcpyAsync(M->rope, tab.data(), tab.size() * sizeof(float2),
+                                hipMemcpyHostToDevice, st));
+      CREATE_TRY(hipStreamSynchronize(st));   // `tab` is host stack memory
+    }
+  }
+  CREATE_TRY(hipStreamSynchronize(st));
+#undef CREATE_TRY
+  *out = M;
+  return RMT_OK;
+}
+
+int32_t rmt_model_set_segments(rmt_model* model, int32_t S) {
+  if (!model) return fail(RMT_EINVAL, "model is NULL");
+  if (S < 1) return fail(RMT_EINVAL, "S must be >= 1");
+  rmt_config c = model->cfg;
+  c.S = S;
+  int32_t rc = validate_config(&c);
+  if (rc != RMT_OK) return rc;
+  model->cfg.S = S;
+  return RMT_OK;
+}
+
+int32_t rmt_model_set_stream(rmt_model* model, void* stream) {
+  if (!model) return fail(RMT_EINVAL, "model is NULL");
+  model->stream = (hipStream_t)stream;
+  return RMT_OK;
+}
+
+int32_t rmt_model_device_bytes(const rmt_model* model, size_t* bytes) {
+  if (!model || !bytes) return fail(RMT_EINVAL, "model and bytes must be non-NULL");
+  *bytes = model->bytes;
+  return RMT_OK;
+}
+
+int32_t rmt_forward_diagonal(rmt_model* M, const void* tokens, const void* mem0, rmt_output* out) {
+  int32_t rc = check_forward_args(M, tokens, mem0, out);
+  if (rc != RMT_OK) return rc;
+  rc = start_forward(M, mem0, out);
+  if (rc != RMT_OK) return rc;
+  const int L = M->cfg.L, S = M->cfg.S;
+  Cell cells[kMaxGroups];
+  for (int k = 0; k < L + S - 1; ++k) {
+    const int l_lo = std::max(0, k - S + 1), l_hi = std::min(L - 1, k);
+    for (int l0 = l_lo; l0 <= l_hi; l0 += kMaxGroups) {
+      const int G = std::min(kMaxGroups, l_hi - l0 + 1);
+      for (int g = 0; g < G; ++g) cells[g] = Cell{l0 + g, k - (l0 + g)};
+      rc = run_cells(M, cells, G, tokens, out);
+      if (rc != RMT_OK) return rc;
+    }
+  }
+  return RMT_OK;
+}
+
+int32_t rmt_forward_sequential(rmt_model* M, const void* tokens, const void* mem0, rmt_output* out) {
+  int32_t rc = check_forward_args(M, tokens, mem0, out);
+  if (rc != RMT_OK) return rc;
+  rc = start_forward(M, mem0, out);
+  if (rc != RMT_OK) return rc;
+  for (int s = 0; s < M->cfg.S; ++s)
+    for (int l = 0; l < M->cfg.L; ++l) {
+      Cell cell{l, s};
+      rc = run_cells(M, &cell, 1, tokens, out);
+      if (rc != RMT_OK) return rc;
+    }
+  return RMT_OK;
+}
+
+int32_t rmt_model_check(rmt_model* M, int32_t* bad_tokens) {
+  if (!M || !bad_tokens) return fail(RMT_EINVAL, "model and bad_tokens must be non-NULL");
+  int32_t v = 0;
+  HIP_TRY(hipMemcpyAsync(&v, M->flag, sizeof(v), hipMemcpyDeviceToHost, M->stream));
+  HIP_TRY(hipStreamSynchronize(M->stream));
+  HIP_TRY(hipMemsetAsync(M->flag, 0, sizeof(v), M->stream));
+  HIP_TRY(hipStreamSynchronize(M->stream));
+  *bad_tokens = v ? 1 : 0;
+  return RMT_OK;
+}
+
+int32_t rmt_model_enable_timing(rmt_model* M, int32_t enable) {
+  if (!M) return fail(RMT_EINVAL, "model is NULL");
+  M->timing = enable != 0;
+  M->ev_used = 0;
+  M->ev_stage.clear();
+  M->ev_flops.clear();
+  M->ev_bytes.clear();
+  return RMT_OK;
+}
+
+int32_t rmt_model_stage_times(rmt_model* M, double* ms, int64_t* launches, double* flops,
+                              double* bytes) {
+  if (!M) return fail(RMT_EINVAL, "model is NULL");
+  HIP_TRY(hipStreamSynchronize(M->stream));
+  double t[RMT_NUM_STAGES] = {0}, f[RMT_NUM_STAGES] = {0}, b[RMT_NUM_STAGES] = {0};
+  int64_t nl[RMT_NUM_STAGES] = {0};
+  for (size_t i = 1; i < M->ev_used; ++i) {
+    const int st = M->ev_stage[i];
+    if (st < 0) continue;   // start marker of the next forward call
+    float dt = 0.f;
+    HIP_TRY(hipEventElapsedTime(&dt, M->events[i - 1], M->events[i]));
+    t[st] += dt;
+    nl[st] += 1;
+    f[st] += M->ev_flops[i];
+    b[st] += M->ev_bytes[i];
+  }
+  for (int i = 0; i < RMT_NUM_STAGES; ++i) {
+    if (ms) ms[i] = t[i];
+    if (launches) launches[i] = nl[i];
+    if (flops) flops[i] = f[i];
+    if (bytes) bytes[i] = b[i];
+  }
+  M->ev_used = 0;
+  M->ev_stage.clear();
+  M->ev_flops.clear();
+  M->ev_bytes.clear();
+  return RMT_OK;
+}
+
+int32_t rmt_model_destroy(rmt_model* M) {
+  if (!M) return RMT_OK;
+  hipError_t e1 = hipStreamSynchronize(M->stream);
+  for (hipEvent_t e : M->events) (void)hipEventDestroy(e);
+  hipError_t e2 = hipFree(M->block);
+  delete M;
+  if (e1 != hipSuccess) return fail(RMT_EHIP, "hipStreamSynchronize: %s", hipGetErrorString(e1));
+  if (e2 != hipSuccess) return fail(RMT_EHIP, "hipFree: %s", hipGetErrorString(e2));
+  return RMT_OK;
+}
+
+int32_t rmt_pack_weight(int32_t L, int32_t K, int32_t N, const void* src, int32_t src_dtype,
+                        void* dst, void* stream) {
+  if (L < 1 || K < 1 || N < 1 || K % 8 != 0 || N % 8 != 0)
+    return fail(RMT_EINVAL, "need L >= 1 and positive K, N that are multiples of 8");
+  if (!src || !dst) return fail(RMT_EINVAL, "src and dst must be non-NULL");
+  if (src_dtype != RMT_F32 && src_dtype != RMT_BF16) return fail(RMT_EINVAL, "bad src_dtype");
+  HIP_TRY(launch_pack(L, K, N, src, nullptr, src_dtype == RMT_BF16, 0, (uint16_t*)dst,
+                      (hipStream_t)stream));
+  return RMT_OK;
+}
+
+int32_t rmt_grouped_gemm(int32_t G, int32_t Mr, int32_t N, int32_t K, const void* A, const void* B,
+                         const int32_t* group_layer, void* C, void* stream) {
+  if (G < 1 || G > kMaxGroups) return fail(RMT_EINVAL, "G must be in [1, %d] (got %d)", kMaxGroups, G);
+  if (Mr < 1 || K < 8 || K % 8 != 0 || N < 64 || N % 64 != 0)
+    return fail(RMT_EINVAL, "need M >= 1, K a positive multiple of 8, N a positive multiple of 64");
+  if ((int64_t)G * Mr * std::max(N, K) > INT32_MAX) return fail(RMT_EINVAL, "sizes overflow int32");
+  if (!A || !B || !C || !group_layer) return fail(RMT_EINVAL, "A, B, C and group_layer must be non-NULL");
+  GroupTable tab;
+  std::memset(&tab, 0, sizeof(tab));
+  tab.G = G;
+  for (int g = 0; g < G; ++g) {
+    if (group_layer[g] < 0) return fail(RMT_EINVAL, "group_layer[%d] < 0", g);
+    tab.layer[g] = group_layer[g];
+    tab.out_lo[g] = (uint16_t*)C + (size_t)g * Mr * N;
+  }
+  GemmArgs ga;
+  std::memset(&ga, 0, sizeof(ga));
+  ga.A = (const uint16_t*)A; ga.B = (const uint16_t*)B; ga.M = Mr; ga.N = N; ga.K = K;
+  ga.split_in = Mr; ga.split_out = Mr; ga.ld_out = N;
+  HIP_TRY(launch_gemm_bf16(EPI_STORE_BF16, ga, tab, (hipStream_t)stream));
+  return RMT_OK;
+}
+
+}  // extern "C"

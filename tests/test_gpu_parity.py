@@ -1,0 +1,125 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle on the
+same seeded inputs.
+
+Tolerances: fp32 (linear-GELU grid) max normwise relative error
+max|g - o| / max|o| <= 1e-4; bf16 cells relative L2 error <= 2e-2 on the final
+hidden states and on the final memory, each measured separately.  The
+diagonal and sequential GPU paths must agree bit for bit."""
+import dataclasses
+
+import numpy as np
+import pytest
+
+import rmt_inputs as ri
+from oracle import rmt_oracle as orc
+
+import gpu_util as gu
+
+pytestmark = [pytest.mark.gpu, gu.needs_gpu]
+
+BF16_TOL = 2e-2
+F32_TOL = 1e-4
+
+
+def _oracle(cfg, run):
+    return orc.forward_sequential(cfg, run.layers, run.x, run.mem0, run.embed)
+
+
+def test_linear_gelu_fp32():
+    cfg = ri.TINY_LINEAR_GELU
+    gu.say(f"[parity] {cfg.name} fp32 diagonal+sequential")
+    run = gu.GpuRun(cfg)
+    hd, md = run.run("diagonal")
+    hs, ms = run.run("sequential")
+    ho, mo = _oracle(cfg, run)
+    assert gu.normwise(hd, ho) <= F32_TOL, gu.normwise(hd, ho)
+    assert gu.normwise(md, mo) <= F32_TOL, gu.normwise(md, mo)
+    assert np.array_equal(hd, hs) and np.array_equal(md, ms)
+    run.close()
+
+
+@pytest.mark.parametrize("cfg", [ri.TINY_SWIGLU, ri.TINY_LLAMA, ri.TINY_LLAMA_HD128],
+                         ids=lambda c: c.name)
+def test_tiny_bf16(cfg):
+    gu.say(f"[parity] {cfg.name} bf16 L={cfg.L} S={cfg.S} R={cfg.R} d={cfg.d}")
+    run = gu.GpuRun(cfg)
+    hd, md = run.run("diagonal")
+    hs, ms = run.run("sequential")
+    ho, mo = _oracle(cfg, run)
+    e_h, e_m = gu.rel_l2(hd, ho), gu.rel_l2(md, mo)
+    gu.say(f"  rel L2 hidden {e_h:.3e} mem {e_m:.3e}")
+    assert e_h <= BF16_TOL and e_m <= BF16_TOL
+    assert np.array_equal(hd, hs) and np.array_equal(md, ms)
+    run.close()
+
+
+@pytest.mark.parametrize("S", [1, 2])
+def test_tiny_llama_short_sequences(S):
+    """S = 1 (one diagonal per layer, no recurrence) and S = 2 (even S: the
+    initial memory starts in the caller's buffer)."""
+    cfg = ri.TINY_LLAMA
+    gu.say(f"[parity] {cfg.name} S={S}")
+    run = gu.GpuRun(cfg, S=S)
+    hd, md = run.run("diagonal")
+    ho, mo = _oracle(cfg, run)
+    assert gu.rel_l2(hd, ho) <= BF16_TOL and gu.rel_l2(md, mo) <= BF16_TOL
+    run.close()
+
+
+def test_memory_in_place_and_resume():
+    """out.mem aliasing mem0 updates the state in place, and running the
+    segments in two calls equals one call, bit for bit."""
+    import torch
+    cfg = ri.TINY_LLAMA
+    gu.say(f"[parity] {cfg.name} in-place memory + resume")
+    full = gu.GpuRun(cfg)
+    h_all, m_all = full.run("diagonal")
+    a = 3
+    import long_context_anti_amd as rmt
+    from rmt_inputs import device as rdev
+    part = rmt.RMTModel(**rdev.model_kwargs(cfg, a), weights=rdev.device_weights(cfg, full.layers, full.embed))
+    state = full.mem0_dev.clone()
+    h1 = torch.empty((a * cfg.n, cfg.d), dtype=torch.float32, device="cuda")
+    part.forward_diagonal(full.tokens[:a * cfg.n], state, h1, state)
+    part.set_segments(cfg.S - a)
+    h2 = torch.empty(((cfg.S - a) * cfg.n, cfg.d), dtype=torch.float32, device="cuda")
+    part.forward_sequential(full.tokens[a * cfg.n:].contiguous(), state, h2, state)
+    torch.cuda.synchronize()
+    assert np.array_equal(torch.cat([h1, h2]).cpu().numpy(), h_all)
+    assert np.array_equal(state.cpu().numpy(), m_all)
+    part.close()
+    full.close()
+
+
+def test_bad_token_ids_are_flagged():
+    import torch
+    cfg = ri.TINY_LLAMA
+    gu.say(f"[parity] {cfg.name} out-of-range token ids")
+    run = gu.GpuRun(cfg, S=1)
+    assert not run.model.bad_tokens()
+    run.tokens[5] = cfg.V + 3
+    run.tokens[7] = -2
+    run.model.forward_diagonal(run.tokens, run.mem0_dev, run.hidden, run.mem)
+    torch.cuda.synchronize()
+    assert run.model.bad_tokens()
+    assert not run.model.bad_tokens()      # the check clears the flag
+    assert torch.isfinite(run.hidden).all()
+    run.close()
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("cfg,S", [(ri.NORM_SWIGLU_1B, 2), (ri.LLAMA_1B, 2)],
+                         ids=["norm_swiglu_1b_S2", "llama1b_S2"])
+def test_full_width_prefix(cfg, S):
+    """The full-width workloads on a prefix of S segments (a prefix is exactly
+    the first S segments of the full run: segment s never reads later ones)."""
+    gu.say(f"[parity] {cfg.name} prefix S={S} (all {cfg.L} layers)")
+    run = gu.GpuRun(cfg, S=S)
+    hd, md = run.run("diagonal")
+    hs, ms = run.run("sequential")
+    ho, mo = _oracle(cfg, run)
+    e_h, e_m = gu.rel_l2(hd, ho), gu.rel_l2(md, mo)
+    gu.say(f"  rel L2 hidden {e_h:.3e} mem {e_m:.3e}")
+    assert e_h <= BF16_TOL and e_m <= BF16_TOL
+    assert np.array_equal(hd, hs) and np.array_equal(md, ms)
+    run.close()

@@ -1,0 +1,129 @@
+"""librmt.so on the CPU: it loads, exports every symbol include/rmt.h
+declares, its host schedule matches the oracle's table bit for bit, and its
+argument checks fire before any device call."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+import rmt_inputs as ri
+from oracle import rmt_oracle as orc
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rmt.h")
+
+
+def _lib():
+    from long_context_anti_amd import _lib as L
+    return L
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(rmt_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ("rmt_diag_schedule", "rmt_forward_diagonal", "rmt_forward_sequential",
+                     "rmt_grouped_gemm", "rmt_model_create", "rmt_last_error"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = _lib()
+    h = C.CDLL(L.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(h, name), name
+    # the binding declares a signature for each of them
+    assert set(declared_functions()) == set(L.SIGNATURES)
+
+
+def _schedule_lib(L_, S):
+    import long_context_anti_amd as rmt
+    return rmt.diag_schedule(L_, S)
+
+
+@pytest.mark.parametrize("L", [1, 2, 3, 5, 8, 12])
+@pytest.mark.parametrize("S", [1, 2, 4, 7, 12])
+def test_schedule_matches_oracle(L, S):
+    dp, cells = _schedule_lib(L, S)
+    dp_o, cells_o = orc.schedule_table(L, S)
+    assert dp.dtype == np.int32 and np.array_equal(dp, dp_o)
+    assert np.array_equal(cells, cells_o)
+
+
+@pytest.mark.parametrize("cfg", [ri.TINY_LINEAR_GELU, ri.NORM_SWIGLU_1B, ri.LLAMA_1B, ri.LLAMA_8B],
+                         ids=lambda c: c.name)
+def test_schedule_matches_oracle_workloads(cfg):
+    dp, cells = _schedule_lib(cfg.L, cfg.S)
+    dp_o, cells_o = orc.schedule_table(cfg.L, cfg.S)
+    assert np.array_equal(dp, dp_o) and np.array_equal(cells, cells_o)
+
+
+def test_schedule_errors():
+    L = _lib()
+    h = L.lib()
+    assert h.rmt_diag_schedule(4, 6, None, None) == 9
+    assert h.rmt_diag_schedule(0, 6, None, None) == L.RMT_EINVAL
+    assert b"L and S" in h.rmt_last_error()
+    assert h.rmt_diag_schedule(4, -1, None, None) == L.RMT_EINVAL
+    buf = (C.c_int32 * 16)()
+    assert h.rmt_diag_schedule(4, 6, buf, None) == L.RMT_EINVAL
+    assert h.rmt_diag_schedule(1 << 20, 1 << 20, None, None) == L.RMT_EINVAL
+
+
+def _cfg(**kw):
+    L = _lib()
+    base = dict(cell=L.RMT_CELL_LLAMA, dtype=L.RMT_BF16, L=2, S=3, n=64, m=16, d=256, n_heads=4,
+                n_kv_heads=1, head_dim=64, ffn=256, vocab=100, eps=1e-5, rope_theta=5e5)
+    base.update(kw)
+    return L.RmtConfig(**base)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(L=0), -1), (dict(n=0), -1), (dict(head_dim=96, n_heads=2, d=192), -2),
+    (dict(n_kv_heads=2), -2), (dict(d=200), -2), (dict(ffn=100), -2), (dict(dtype=0), -2),
+    (dict(cell=7), -1), (dict(vocab=0), -1), (dict(n_heads=3, n_kv_heads=2), -1),
+])
+def test_model_create_rejects_bad_configs(kw, code):
+    L = _lib()
+    cfg = _cfg(**kw)
+    w = L.RmtWeights()
+    handle = C.c_void_p()
+    rc = L.lib().rmt_model_create(C.byref(cfg), C.byref(w), None, C.byref(handle))
+    assert rc == code, L.lib().rmt_last_error()
+    assert not handle.value
+
+
+def test_model_create_rejects_missing_weights():
+    L = _lib()
+    cfg = _cfg()
+    w = L.RmtWeights()     # all NULL
+    handle = C.c_void_p()
+    assert L.lib().rmt_model_create(C.byref(cfg), C.byref(w), None, C.byref(handle)) == L.RMT_EINVAL
+    assert b"LLAMA needs" in L.lib().rmt_last_error() or b"required" in L.lib().rmt_last_error()
+
+
+def test_grouped_gemm_rejects_bad_shapes():
+    L = _lib()
+    h = L.lib()
+    gl = (C.c_int32 * 1)(0)
+    p = C.c_void_p(16)
+    assert h.rmt_grouped_gemm(0, 128, 256, 64, p, p, gl, p, None) == L.RMT_EINVAL
+    assert h.rmt_grouped_gemm(33, 128, 256, 64, p, p, gl, p, None) == L.RMT_EINVAL
+    assert h.rmt_grouped_gemm(1, 128, 250, 64, p, p, gl, p, None) == L.RMT_EINVAL
+    assert h.rmt_grouped_gemm(1, 128, 256, 60, p, p, gl, p, None) == L.RMT_EINVAL
+    assert h.rmt_grouped_gemm(1, 128, 256, 64, None, p, gl, p, None) == L.RMT_EINVAL
+    assert h.rmt_pack_weight(1, 60, 64, p, 0, p, None) == L.RMT_EINVAL
+
+
+def test_forward_rejects_null_model():
+    L = _lib()
+    out = L.RmtOutput(None, None)
+    assert L.lib().rmt_forward_diagonal(None, None, None, C.byref(out)) == L.RMT_EINVAL
+    assert L.lib().rmt_forward_sequential(None, None, None, C.byref(out)) == L.RMT_EINVAL
+    assert L.lib().rmt_model_destroy(None) == L.RMT_OK
