@@ -1,0 +1,250 @@
+"""Benchmark: diagonal-batched inference of one 131,072-token sequence.
+
+Workload: the LLaMA-1B-shaped RMT (16 layers, d = 2048, 32 query / 8 KV heads
+of 64, SwiGLU 8192, segments of 1024 tokens + 128 memory rows, 128 segments),
+bf16 weights and activations with fp32 accumulation and an fp32 residual
+stream, random weights and token ids from a fixed seed.
+
+Prints one JSON line.  `value` is tokens/s of rmt_forward_diagonal over the
+whole sequence with inputs already in HBM.  Alongside: the same GPU's
+sequential per-cell path, per-stage GPU times (HIP events recorded on the
+library's stream between launches), the grouped-GEMM fraction of the MI355X
+bf16 dense MFMA peak, the isolated 1152 x 2048 x 8192 grouped GEMM at
+G = 1, 4, 8, 16, and the CPU oracle timed on a prefix of the sequence.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu] [--no-seq]
+"""
+from __future__ import annotations
+
+import argparse
+import concurrent.futures as cf
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+METRIC = "tokens/s for one 131K-token sequence; grouped-GEMM % of bf16 MFMA peak"
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def gen_layers(cfg, seed=0):
+    import rmt_inputs as ri
+    with cf.ThreadPoolExecutor(max_workers=8) as ex:
+        return list(ex.map(lambda l: ri.layer_weights(cfg, l, seed), range(cfg.L)))
+
+
+def timed_steps(fn, steps, stream):
+    import torch
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(steps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall, e0.elapsed_time(e1) / 1e3
+
+
+def gemm_sweep(steps=20):
+    """Isolated grouped GEMM, 1152 x 2048 x 8192 per group, distinct weights."""
+    import torch
+    import long_context_anti_amd as rmt
+    import rmt_inputs as ri
+    from rmt_inputs import device as rdev
+    gc = ri.GROUPED_GEMM_1B
+    A, B = ri.gemm_operands(gc, G=gc.G_max)
+    A_d = rdev.bf16_tensor(A)
+    W_d = rdev.bf16_tensor(B)
+    B_d = torch.empty((gc.G_max, gc.N, gc.K), dtype=torch.bfloat16, device="cuda")
+    rmt.pack_weight(W_d, B_d)
+    del W_d
+    C_d = torch.empty((gc.G_max, gc.M, gc.N), dtype=torch.bfloat16, device="cuda")
+    out = {}
+    st = torch.cuda.current_stream()
+    for G in gc.G_sweep:
+        fn = lambda: rmt.grouped_gemm(A_d[:G], B_d, list(range(G)), C_d[:G])  # noqa: E731
+        for _ in range(3):
+            fn()
+        _, gpu_s = timed_steps(fn, steps, st)
+        flops = 2.0 * G * gc.M * gc.N * gc.K
+        tf = flops * steps / gpu_s / 1e12
+        out[f"G{G}"] = {"us": round(gpu_s / steps * 1e6, 2), "tflops": round(tf, 1),
+                        "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+    return out
+
+
+def cpu_baseline(cfg, layers, tokens, mem0, embed, gpu_hidden, gpu_mem_prefix_fn, S_prefix):
+    """The CPU oracle as it stands, timed on a prefix of S_prefix segments."""
+    from threadpoolctl import threadpool_info
+    from oracle import rmt_oracle as orc
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                   if i.get("user_api") == "blas"] or [1])
+    t0 = time.perf_counter()
+    h, m = orc.forward_sequential(cfg, layers, tokens[:S_prefix * cfg.n], mem0, embed)
+    dt = time.perf_counter() - t0
+    toks = S_prefix * cfg.n
+    res = {"value": round(toks / dt, 2), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+           "sample": f"first {S_prefix} of {cfg.S} segments through all {cfg.L} layers "
+                     f"({toks} tokens, NumPy fp32, {dt:.1f} s); per-segment cost is constant in s",
+           "seconds": round(dt, 2)}
+    # the same prefix of the GPU's full-sequence run: segment s never reads later segments
+    gh = gpu_hidden[:toks].astype(np.float64)
+    res["parity_rel_l2_hidden_prefix"] = float(np.linalg.norm(gh - h) / np.linalg.norm(h))
+    gm = gpu_mem_prefix_fn()
+    if gm is not None:
+        res["parity_rel_l2_mem_prefix"] = float(np.linalg.norm(gm - m) / np.linalg.norm(m))
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-seq", action="store_true", help="skip the sequential path")
+    ap.add_argument("--no-sweep", action="store_true", help="skip the isolated grouped-GEMM sweep")
+    ap.add_argument("--cpu-segments", type=int, default=2)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: the diagonal sweep is measured on a single "
+              "MI355X (no multi-GPU path is built); use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import long_context_anti_amd as rmt
+    import rmt_inputs as ri
+    from rmt_inputs import device as rdev
+
+    cfg = ri.LLAMA_1B
+    torch.cuda.set_device(0)
+    t0 = time.perf_counter()
+    layers = gen_layers(cfg)
+    embed = ri.embedding(cfg)
+    tokens = ri.tokens(cfg)
+    mem0 = ri.initial_memory(cfg)
+    log(f"[bench] inputs generated in {time.perf_counter() - t0:.1f} s")
+    dw = rdev.device_weights(cfg, layers, embed)
+    model = rmt.RMTModel(**rdev.model_kwargs(cfg), weights=dw)
+    emb_dev = dw["embed"]
+    del dw
+    tok_d = rdev.segment_inputs(cfg, tokens)
+    mem0_d = rdev.f32_tensor(mem0)
+    T = cfg.T
+    hidden = torch.empty((T, cfg.d), dtype=torch.float32, device="cuda")
+    mem = torch.empty((cfg.L, cfg.m, cfg.d), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    log(f"[bench] model on device: {model.device_bytes() / 2**30:.2f} GiB")
+
+    diag = lambda: model.forward_diagonal(tok_d, mem0_d, hidden, mem)  # noqa: E731
+    for i in range(args.warmup):
+        diag()
+    torch.cuda.synchronize()
+    log("[bench] warmup done")
+
+    # timed region: per-launch HIP events on the library's stream
+    model.enable_timing(True)
+    wall, gpu_s = timed_steps(diag, args.steps, stream)
+    stages = model.stage_times()
+    model.enable_timing(False)
+    log(f"[bench] diagonal: {wall / args.steps * 1e3:.1f} ms/step wall")
+    # the same region without the per-launch events
+    wall_ne, _ = timed_steps(diag, args.steps, stream)
+    hidden_np = hidden.cpu().numpy()
+
+    ms_step = wall / args.steps * 1e3
+    tok_s = T * args.steps / wall
+
+    st_out = {}
+    gemm_flops = gemm_ms = 0.0
+    for name, v in stages.items():
+        if v["launches"] == 0:
+            continue
+        ms = v["ms"] / args.steps
+        e = {"ms_per_step": round(ms, 3), "launches_per_step": v["launches"] // args.steps}
+        if v["flops"] > 0:
+            e["tflops"] = round(v["flops"] / (v["ms"] / 1e3) / 1e12, 1)
+            e["frac_bf16_peak"] = round(e["tflops"] / PEAK_BF16_TFLOPS, 4)
+        if v["bytes"] > 0:
+            e["gbs"] = round(v["bytes"] / (v["ms"] / 1e3) / 1e9, 1)
+            e["frac_hbm_peak"] = round(e["gbs"] / PEAK_HBM_GBS, 4)
+        st_out[name] = e
+        if name in ("qkv", "oproj", "gateup", "down"):
+            gemm_flops += v["flops"]
+            gemm_ms += v["ms"]
+    gemm_tf = gemm_flops / (gemm_ms / 1e3) / 1e12 if gemm_ms else 0.0
+
+    gu = stages["gateup"]
+    achieved = gu["flops"] / gu["launches"] / (gu["ms"] / 1e3 / gu["launches"]) / 1e12
+    roofline = {"kernel": "grouped GEMM, gate/up stage + SwiGLU epilogue (gemm_bf16_kernel<2>)",
+                "bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "avg_launch_us": round(gu["ms"] / gu["launches"] * 1e3, 2),
+                "flops_per_launch": gu["flops"] / gu["launches"]}
+
+    result = {
+        "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 2),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded random weights, token ids uniform over the vocabulary)",
+        "config": {"workload": cfg.name, "layers": cfg.L, "segments": cfg.S, "segment_tokens": cfg.n,
+                   "memory_rows": cfg.m, "width": cfg.d, "heads": cfg.Hq, "kv_heads": cfg.Hkv,
+                   "head_dim": cfg.hd, "ffn": cfg.F, "vocab": cfg.V, "tokens": T,
+                   "path": "rmt_forward_diagonal"},
+        "roofline": roofline,
+        "grouped_gemm_stages": {"tflops": round(gemm_tf, 1),
+                                "frac_bf16_peak": round(gemm_tf / PEAK_BF16_TFLOPS, 4)},
+        "ms_per_step_without_stage_events": round(wall_ne / args.steps * 1e3, 2),
+        "stages": st_out,
+    }
+
+    if not args.no_seq:
+        seq = lambda: model.forward_sequential(tok_d, mem0_d, hidden, mem)  # noqa: E731
+        seq()
+        torch.cuda.synchronize()
+        w_s, _ = timed_steps(seq, 1, stream)
+        result["sequential"] = {"value": round(T / w_s, 1), "unit": "tokens/s",
+                                "ms_per_step": round(w_s * 1e3, 2),
+                                "diagonal_speedup": round(w_s / (wall / args.steps), 3)}
+        log(f"[bench] sequential: {w_s * 1e3:.1f} ms/step")
+
+    if not args.no_sweep:
+        result["grouped_gemm_sweep"] = {"workload": ri.GROUPED_GEMM_1B.name, **gemm_sweep()}
+        log("[bench] grouped GEMM sweep done")
+
+    if not args.no_cpu:
+        Sp = args.cpu_segments
+
+        def gpu_mem_prefix():
+            # memory after the prefix: rerun the GPU on exactly that prefix
+            model.set_segments(Sp)
+            mp = torch.empty_like(mem)
+            hp = torch.empty((Sp * cfg.n, cfg.d), dtype=torch.float32, device="cuda")
+            model.forward_diagonal(tok_d, mem0_d, hp, mp)
+            torch.cuda.synchronize()
+            model.set_segments(cfg.S)
+            return mp.cpu().numpy().astype(np.float64)
+
+        log(f"[bench] CPU oracle on {Sp} segments ...")
+        result["cpu_baseline"] = cpu_baseline(cfg, layers, tokens, mem0, embed, hidden_np,
+                                              gpu_mem_prefix, Sp)
+    model.close()
+    del emb_dev
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
