@@ -8,15 +8,25 @@
 // Batching for Recurrent Memory Transformers": one launch covers all cells of
 // a diagonal, whatever their number.
 //
-// Tiling: a workgroup of 4 wave64s computes a 128 x 256 tile; each wave a
-// 64 x 128 sub-tile as 2 x 4 blocks of v_mfma_f32_32x32x16_bf16.  128 divides
-// the cell height R = n + m of the 1B/8B workloads (1152, 2176), so no tile
-// straddles two groups.  K is consumed 64 at a time through LDS (row stride
-// 72 elements: 144 bytes keeps 16-byte reads of 32 consecutive rows free of
-// bank conflicts); the next K slice is fetched into registers while the
-// current one feeds the MFMAs.  Every output element is produced by one
-// thread with the same K order whatever G is, so a cell's result does not
-// depend on which diagonal (or the sequential sweep) it runs in.
+// Design (measured on MI355X; the operand stream from L2, not the MFMA rate,
+// is what limits this kernel, so the tile is as large as LDS allows):
+//   * 256 x 256 output tiles, eight wave64s of 64 x 128 each, as 2 x 4
+//     blocks of v_mfma_f32_32x32x16_bf16; 128 x 256 tiles when a launch is
+//     too small to fill the GPU twice.  A cell (group) never shares a tile
+//     with another; the rows past the cell's end read as zeros and waves that
+//     own only such rows skip their MFMAs.
+//   * K advances 64 at a time through a two-slice LDS ring filled by buffer
+//     loads that write LDS directly (no staging registers).  LDS rows are
+//     unpadded; their 16-byte chunks are XOR-swizzled so MFMA operand reads
+//     of 32 consecutive rows are bank-conflict free.  Buffer resources clip
+//     every load to the tile's valid rows and K, so ragged edges are zeros
+//     without branches.
+//   * Workgroup ids are renumbered so each XCD (ids = x mod 8) receives a
+//     contiguous run of tiles; within a cell the M tile varies fastest, so the
+//     tiles sharing a weight panel run together in one XCD's L2.
+//   * Every output element is produced by one lane with the same K order for
+//     every tile shape and every G, so a cell's result does not depend on
+//     which diagonal (or the sequential sweep) it runs in.
 #include "kernels.h"
 
 namespace rmt {
@@ -26,17 +36,38 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int BM = 128;
 constexpr int BN = 256;
 constexpr int BK = 64;
-constexpr int LDK = BK + 8;
-constexpr int NT = 256;
+constexpr int STAGES = 2;
+constexpr int ROWB = BK * 2;         // bytes per LDS row: unpadded, chunks XOR-swizzled
+constexpr int CPR = BK / 8;          // 16-byte chunks per row
+constexpr int RPI = 64 / CPR;        // rows filled by one wave-wide 1 KiB load
+constexpr int BUF_FLAGS = 0x00020000;        // raw buffer, 32-bit data format
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 __device__ __forceinline__ uint16_t to_bf16(float f) {
   uint32_t u = __float_as_uint(f);
   if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
   u += 0x7fffu + ((u >> 16) & 1u);
   return (uint16_t)(u >> 16);
+}
+
+// Chunk permutation of LDS row r: logical 16-byte chunk c sits at physical
+// position c ^ swz(r).  It depends only on r mod 32, and 16-byte reads of 32
+// consecutive rows at one logical chunk hit distinct banks (checked for both
+// 32 and 64 four-byte banks).
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (CPR == 8) return ((r >> 1) ^ ((r & 1) << 2)) & 7;
+  else return ((r >> 1) + (r >> 3)) & 3;
+}
+
+// s_waitcnt that leaves at most N vector-memory operations outstanding and
+// none of this wave's LDS reads (so no stage is refilled under a reader).
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  static_assert(N < 64, "vmcnt has 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (0 << 8) | ((N >> 4) << 14));
 }
 
 // Workgroups are handed to the 8 XCDs round-robin (id mod 8).  Renumber them
@@ -48,10 +79,21 @@ __device__ __forceinline__ int xcd_remap(int bid, int nb) {
   return xcd * per + (xcd < rem ? xcd : rem) + idx;
 }
 
-template <int EPI>
-__global__ __launch_bounds__(NT, 2) void gemm_bf16_kernel(GemmArgs a, GroupTable tab) {
-  __shared__ __attribute__((aligned(16))) uint16_t sA[BM * LDK];
-  __shared__ __attribute__((aligned(16))) uint16_t sB[BN * LDK];
+// BM x BN output tile per workgroup; WTM x WTN is one wave's sub-tile and the
+// workgroup has one wave per sub-tile.
+template <int EPI, int BM, int WTM, int WTN>
+__global__ __launch_bounds__((BM / WTM) * (BN / WTN) * 64, 1) void gemm_bf16_kernel(
+    GemmArgs a, GroupTable tab) {
+  constexpr int STAGE_BYTES = (BM + BN) * ROWB;
+  constexpr int WAVES_N = BN / WTN;
+  constexpr int NWAVES = (BM / WTM) * WAVES_N;
+  constexpr int MI = WTM / 32;
+  constexpr int NI = WTN / 32;
+  constexpr int A_PER_WAVE = BM / RPI / NWAVES;
+  constexpr int B_PER_WAVE = BN / RPI / NWAVES;
+  constexpr int LOADS_PER_WAVE = A_PER_WAVE + B_PER_WAVE;
+  static_assert(A_PER_WAVE * RPI * NWAVES == BM && B_PER_WAVE * RPI * NWAVES == BN, "load split");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * STAGE_BYTES];
 
   const int tiles_m = (a.M + BM - 1) / BM;
   const int tiles_n = (a.N + BN - 1) / BN;
@@ -64,107 +106,143 @@ __global__ __launch_bounds__(NT, 2) void gemm_bf16_kernel(GemmArgs a, GroupTable
   const int tid = (int)threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave >> 1;
-  const int wn = wave & 1;
+  const int wm = wave / WAVES_N;
+  const int wn = wave % WAVES_N;
 
   const int K = a.K;
-  const uint16_t* Ag = a.A + ((size_t)g * a.M + (size_t)tm * BM) * K;
-  const uint16_t* Bg = a.B + ((size_t)tab.layer[g] * a.N + (size_t)tn * BN) * K;
   const int m_valid = min(BM, a.M - tm * BM);
   const int n_valid = min(BN, a.N - tn * BN);
+  // Buffer resources clipped to the tile's valid rows: the hardware returns
+  // zeros for anything outside, so ragged M / N / K edges need no branches.
+  const uint16_t* Ag = a.A + ((size_t)g * a.M + (size_t)tm * BM) * K;
+  const uint16_t* Bg = a.B + ((size_t)tab.layer[g] * a.N + (size_t)tn * BN) * K;
+  const int a_bytes = m_valid * K * 2;
+  const int b_bytes = n_valid * K * 2;
+  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc((void*)Ag, (short)0, a_bytes, BUF_FLAGS);
+  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc((void*)Bg, (short)0, b_bytes, BUF_FLAGS);
 
-  const int lrow = tid >> 3;
-  const int lk = (tid & 7) * 8;
-  u32x4 ra[BM / 32];
-  u32x4 rb[BN / 32];
-  const u32x4 zero = {0u, 0u, 0u, 0u};
-
-  auto load = [&](int k0) {
-    const bool kin = (k0 + lk) < K;
+  // Global -> LDS without registers: each wave-wide load moves 1 KiB, lane L
+  // landing at byte 16 L of the destination, i.e. row RPI q + L / CPR at
+  // physical chunk L % CPR, which holds logical chunk (L % CPR) ^ swz(row).
+  const int lrow = lane / CPR;
+  const int lp = lane % CPR;
+  auto issue = [&](int kt, int stage) __attribute__((always_inline)) {
+    const int k0 = kt * BK;
+    uint8_t* sbase = smem + stage * STAGE_BYTES;
 #pragma unroll
-    for (int i = 0; i < BM / 32; ++i) {
-      const int r = lrow + 32 * i;
-      ra[i] = (kin && r < m_valid) ? *(const u32x4*)(Ag + (size_t)r * K + k0 + lk) : zero;
+    for (int i = 0; i < A_PER_WAVE; ++i) {
+      const int q = wave * A_PER_WAVE + i;
+      const int row = q * RPI + lrow;
+      const int k = k0 + 8 * (lp ^ swz(row));
+      const int off = k < K ? (row * K + k) * 2 : a_bytes;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(sbase + q * 1024), 16, off, 0, 0, 0);
     }
 #pragma unroll
-    for (int i = 0; i < BN / 32; ++i) {
-      const int r = lrow + 32 * i;
-      rb[i] = (kin && r < n_valid) ? *(const u32x4*)(Bg + (size_t)r * K + k0 + lk) : zero;
+    for (int i = 0; i < B_PER_WAVE; ++i) {
+      const int q = wave * B_PER_WAVE + i;
+      const int row = q * RPI + lrow;
+      const int k = k0 + 8 * (lp ^ swz(row));
+      const int off = k < K ? (row * K + k) * 2 : b_bytes;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(sbase + BM * ROWB + q * 1024), 16, off, 0, 0, 0);
     }
   };
-  auto store = [&]() {
-#pragma unroll
-    for (int i = 0; i < BM / 32; ++i) *(u32x4*)(sA + (lrow + 32 * i) * LDK + lk) = ra[i];
-#pragma unroll
-    for (int i = 0; i < BN / 32; ++i) *(u32x4*)(sB + (lrow + 32 * i) * LDK + lk) = rb[i];
-  };
 
-  f32x16 acc[2][4];
+  f32x16 acc[MI][NI];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int t = 0; t < NI; ++t)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][t][e] = 0.f;
 
   // Lane l feeds row (l % 32) of its A/B blocks with 8 consecutive k values.
-  // Within one 64-wide K slice, lanes 0-31 cover k 0..31 and lanes 32-63 cover
-  // k 32..63 over the four MFMA steps; A and B use the same assignment, so
-  // each MFMA still sums matching k.
+  // Within one K slice lanes 0-31 cover the first half of the slice and lanes
+  // 32-63 the second half, over the slice's MFMA steps; A and B use the same
+  // assignment, so each MFMA still sums matching k.
+  // A wave whose rows all lie past the tile's valid rows (the short last
+  // tile of a cell) has nothing to compute; it still loads and synchronises.
+  const bool wave_live = wm * WTM < m_valid;
   const int r32 = lane & 31;
-  const int kofs = (lane >> 5) * 32;
-  const int nk = (K + BK - 1) / BK;
-  load(0);
-  for (int kt = 0; kt < nk; ++kt) {
-    __syncthreads();
-    store();
-    __syncthreads();
-    if (kt + 1 < nk) load((kt + 1) * BK);
+  const int sw = swz(r32);             // == swz of every row this lane reads
+  const int c0 = (lane >> 5) * (CPR / 2);
+  const int a_row = (wm * WTM + r32) * ROWB;
+  const int b_row = BM * ROWB + (wn * WTN + r32) * ROWB;
+  auto compute = [&](int stage) __attribute__((always_inline)) {
+    const uint8_t* sbase = smem + stage * STAGE_BYTES;
+    bf16x8 af[2][MI], bfr[2][NI];
+    auto frags = [&](int j, int buf) __attribute__((always_inline)) {
+      const int cb = ((c0 + j) ^ sw) * 16;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      bf16x8 af[2], bfr[4];
+      for (int i = 0; i < MI; ++i)
+        af[buf][i] = __builtin_bit_cast(bf16x8, *(const u32x4*)(sbase + a_row + i * 32 * ROWB + cb));
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-        af[i] = __builtin_bit_cast(bf16x8, *(const u32x4*)(sA + (wm * 64 + i * 32 + r32) * LDK + kofs + 8 * j));
+      for (int t = 0; t < NI; ++t)
+        bfr[buf][t] = __builtin_bit_cast(bf16x8, *(const u32x4*)(sbase + b_row + t * 32 * ROWB + cb));
+    };
+    frags(0, 0);
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
-        bfr[t] = __builtin_bit_cast(bf16x8, *(const u32x4*)(sB + (wn * 128 + t * 32 + r32) * LDK + kofs + 8 * j));
+    for (int j = 0; j < CPR / 2; ++j) {
+      if (j + 1 < CPR / 2) frags(j + 1, (j + 1) & 1);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < MI; ++i)
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
-          acc[i][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[t], acc[i][t], 0, 0, 0);
+        for (int t = 0; t < NI; ++t)
+          acc[i][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[j & 1][i], bfr[j & 1][t], acc[i][t], 0, 0, 0);
+      // let the scheduler interleave LDS reads with the MFMA chain
+      __builtin_amdgcn_iglp_opt(1);
     }
+  };
+
+  // Ring of STAGES LDS slices: slice kt+STAGES-1 is requested while the
+  // MFMAs consume slice kt.  One barrier per slice; it also certifies that
+  // every wave has finished reading the stage about to be refilled.
+  const int nk = (K + BK - 1) / BK;
+#pragma unroll
+  for (int s = 0; s < STAGES - 1; ++s)
+    if (s < nk) issue(s, s);
+  for (int kt = 0; kt < nk; ++kt) {
+    const int ahead = min(nk - 1 - kt, STAGES - 2);   // later slices still in flight
+    if (ahead == 0) wait_vmem<0>();
+    else wait_vmem<LOADS_PER_WAVE>();
+    // Each wave has waited for its own LDS-bound loads above; a bare barrier
+    // (no release fence, which would drain every load still in flight) makes
+    // them visible to the whole workgroup.  The empty asm statements keep the
+    // compiler from moving LDS accesses across it.
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1, (kt + STAGES - 1) % STAGES);
+    if (wave_live) compute(kt % STAGES);
   }
 
   // Accumulator layout of a 32x32 block: element e of lane l sits at
   // row 8*(e/4) + 4*(l/32) + e%4, column l%32.
-  const int row_base = tm * BM + wm * 64 + 4 * (lane >> 5);
-  const int col_base = tn * BN + wn * 128 + r32;
+  const int row_base = tm * BM + wm * WTM + 4 * (lane >> 5);
+  const int col_base = tn * BN + wn * WTN + r32;
 
   if constexpr (EPI == EPI_STORE_BF16) {
     uint16_t* C = (uint16_t*)tab.out_lo[g];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int row = row_base + i * 32 + 8 * (e >> 2) + (e & 3);
         if (row >= a.M) continue;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
+        for (int t = 0; t < NI; ++t) {
           const int col = col_base + t * 32;
           if (col < a.N) C[(size_t)row * a.ld_out + col] = to_bf16(acc[i][t][e]);
         }
       }
   } else if constexpr (EPI == EPI_QKV_ROPE) {
-    // The wave's 128 columns start on a head boundary (128 is a multiple of
+    // The wave's WTN columns start on a head boundary (WTN is a multiple of
     // hd), so column c < hd/2 of a head and its partner c + hd/2 sit in the
     // same lane, in blocks t and t + hd/64.
     uint16_t* C = (uint16_t*)tab.out_lo[g];
     const int P = a.hd >> 6;
     const int half = a.hd >> 1;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
+    for (int t = 0; t < NI; ++t) {
       if (((t / P) & 1) != 0) continue;
       const int col = col_base + t * 32;
       if (col >= a.N) continue;
@@ -172,7 +250,7 @@ __global__ __launch_bounds__(NT, 2) void gemm_bf16_kernel(GemmArgs a, GroupTable
       const int hc = col % a.hd;
       const int tp = t + P;
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int row = row_base + i * 32 + 8 * (e >> 2) + (e & 3);
@@ -180,7 +258,7 @@ __global__ __launch_bounds__(NT, 2) void gemm_bf16_kernel(GemmArgs a, GroupTable
           float x1 = acc[i][t][e];
           float x2 = 0.f;
 #pragma unroll
-          for (int q = 0; q < 4; ++q)
+          for (int q = 0; q < NI; ++q)
             if (q == tp) x2 = acc[i][q][e];
           float y1 = x1, y2 = x2;
           if (rot) {
@@ -197,12 +275,12 @@ __global__ __launch_bounds__(NT, 2) void gemm_bf16_kernel(GemmArgs a, GroupTable
     // columns of the same outputs; output column = block * 32 + (l % 32).
     uint16_t* U = (uint16_t*)tab.out_lo[g];
 #pragma unroll
-    for (int t = 0; t < 4; t += 2) {
+    for (int t = 0; t < NI; t += 2) {
       const int col = col_base + t * 32;
       if (col >= a.N) continue;
       const int ocol = (col >> 6) * 32 + r32;
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int row = row_base + i * 32 + 8 * (e >> 2) + (e & 3);
@@ -215,7 +293,7 @@ __global__ __launch_bounds__(NT, 2) void gemm_bf16_kernel(GemmArgs a, GroupTable
     }
   } else {  // EPI_RESID_F32
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int row = row_base + i * 32 + 8 * (e >> 2) + (e & 3);
@@ -227,7 +305,7 @@ __global__ __launch_bounds__(NT, 2) void gemm_bf16_kernel(GemmArgs a, GroupTable
                          ? (float*)tab.out_lo[g] + (size_t)row * a.ld_out
                          : (float*)tab.out_hi[g] + (size_t)(row - a.split_out) * a.ld_out;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
+        for (int t = 0; t < NI; ++t) {
           const int col = col_base + t * 32;
           if (col < a.N) out[col] = acc[i][t][e] + res[col];
         }
@@ -235,28 +313,43 @@ __global__ __launch_bounds__(NT, 2) void gemm_bf16_kernel(GemmArgs a, GroupTable
   }
 }
 
+template <int EPI, int BM, int WTM, int WTN>
+void launch_one(const GemmArgs& a, const GroupTable& tab, hipStream_t stream) {
+  const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN) * tab.G;
+  constexpr int threads = (BM / WTM) * (BN / WTN) * 64;
+  hipLaunchKernelGGL((gemm_bf16_kernel<EPI, BM, WTM, WTN>), dim3(tiles), dim3(threads), 0, stream, a, tab);
+}
+
+// 256 x 256 tiles halve the operand bytes each MFMA needs from L2 compared
+// with 128-row tiles; launches that would leave the 256 CUs with fewer than
+// two rounds of such tiles use 128-row tiles instead.  Both use the same K
+// slicing and lane/k assignment, so a cell's result does not depend on the
+// choice.  Eight waves: 64 x 128 sub-tiles (64 x 64 for 128-row tiles, where
+// RoPE on 128-wide heads takes 32 x 128).
+template <int EPI>
+void launch_epi(const GemmArgs& a, const GroupTable& tab, hipStream_t stream) {
+  const int tiles256 = ((a.M + 255) / 256) * ((a.N + BN - 1) / BN) * tab.G;
+  const bool wide_heads = EPI == EPI_QKV_ROPE && a.hd == 128;
+  if (tiles256 >= 512) {
+    launch_one<EPI, 256, 64, 128>(a, tab, stream);
+  } else if (wide_heads) {
+    launch_one<EPI, 128, 32, 128>(a, tab, stream);
+  } else {
+    launch_one<EPI, 128, 64, 64>(a, tab, stream);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_gemm_bf16(int epilogue, const GemmArgs& a, const GroupTable& tab,
                             hipStream_t stream) {
-  const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN) * tab.G;
-  if (tiles == 0) return hipSuccess;
-  dim3 grid(tiles), block(NT);
+  if (tab.G == 0 || a.M == 0 || a.N == 0) return hipSuccess;
   switch (epilogue) {
-    case EPI_STORE_BF16:
-      hipLaunchKernelGGL(gemm_bf16_kernel<EPI_STORE_BF16>, grid, block, 0, stream, a, tab);
-      break;
-    case EPI_QKV_ROPE:
-      hipLaunchKernelGGL(gemm_bf16_kernel<EPI_QKV_ROPE>, grid, block, 0, stream, a, tab);
-      break;
-    case EPI_SWIGLU:
-      hipLaunchKernelGGL(gemm_bf16_kernel<EPI_SWIGLU>, grid, block, 0, stream, a, tab);
-      break;
-    case EPI_RESID_F32:
-      hipLaunchKernelGGL(gemm_bf16_kernel<EPI_RESID_F32>, grid, block, 0, stream, a, tab);
-      break;
-    default:
-      return hipErrorInvalidValue;
+    case EPI_STORE_BF16: launch_epi<EPI_STORE_BF16>(a, tab, stream); break;
+    case EPI_QKV_ROPE: launch_epi<EPI_QKV_ROPE>(a, tab, stream); break;
+    case EPI_SWIGLU: launch_epi<EPI_SWIGLU>(a, tab, stream); break;
+    case EPI_RESID_F32: launch_epi<EPI_RESID_F32>(a, tab, stream); break;
+    default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
