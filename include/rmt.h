@@ -216,6 +216,19 @@ int32_t rmt_pack_weight(int32_t L, int32_t K, int32_t N, const void* src, int32_
 int32_t rmt_grouped_gemm(int32_t G, int32_t M, int32_t N, int32_t K, const void* A,
                          const void* B, const int32_t* group_layer, void* C, void* stream);
 
+/* Causal grouped-query attention on its own, over G cells of R rows each, in
+ * one launch (the attention stage of the LLAMA cell; see the cell kinds
+ * above): for query head h and row i of cell g,
+ *   out[g][i][h*hd : (h+1)*hd] = sum_{j <= i} softmax_j(q_i . k_j / sqrt(hd)) v_j
+ * with k, v from KV head h / (Hq/Hkv), softmax in fp32, bf16 output.
+ *   qkv  device bf16 [G][R][(Hq+2Hkv)*hd]: per row the Q heads, then the K
+ *        heads, then the V heads (RoPE, if any, already applied)
+ *   out  device bf16 [G][R][Hq*hd]
+ * 1 <= G <= 65535, R >= 1, hd in {64, 128}, Hq/Hkv a positive multiple of 4.
+ * Errors: RMT_EINVAL, RMT_EUNSUPPORTED (hd or head ratio), RMT_EHIP. */
+int32_t rmt_causal_attention(int32_t G, int32_t R, int32_t n_heads, int32_t n_kv_heads,
+                             int32_t head_dim, const void* qkv, void* out, void* stream);
+
 /* Thread-local description of the last error (empty string if none). */
 const char* rmt_last_error(void);
 

@@ -17,7 +17,8 @@ from ._lib import (RMT_BF16, RMT_CELL_LINEAR_GELU, RMT_CELL_LLAMA, RMT_CELL_NORM
                    STAGES, RmtConfig, RmtError, RmtOutput, RmtWeights, check, lib)
 
 __all__ = [
-    "RMTModel", "RmtError", "diag_schedule", "grouped_gemm", "pack_weight", "STAGES",
+    "RMTModel", "RmtError", "diag_schedule", "grouped_gemm", "pack_weight", "causal_attention",
+    "STAGES",
     "RMT_CELL_LINEAR_GELU", "RMT_CELL_NORM_SWIGLU", "RMT_CELL_LLAMA", "RMT_F32", "RMT_BF16",
 ]
 
@@ -64,6 +65,19 @@ def grouped_gemm(A, B, group_layer, C_out, stream=None) -> None:
         assert t.dtype == torch.bfloat16 and t.is_contiguous()
     gl = (C.c_int32 * G)(*[int(x) for x in group_layer])
     check(lib().rmt_grouped_gemm(G, M, N, K, _ptr(A), _ptr(B), gl, _ptr(C_out), _stream(stream)))
+
+
+def causal_attention(qkv, out, n_heads: int, n_kv_heads: int, head_dim: int, stream=None) -> None:
+    """Causal GQA attention over G cells: qkv [G, R, (Hq+2Hkv)*hd] -> out
+    [G, R, Hq*hd], both bf16 device tensors."""
+    import torch
+    G, R, W = qkv.shape
+    assert W == (n_heads + 2 * n_kv_heads) * head_dim
+    assert out.shape == (G, R, n_heads * head_dim)
+    for t in (qkv, out):
+        assert t.dtype == torch.bfloat16 and t.is_contiguous()
+    check(lib().rmt_causal_attention(G, R, n_heads, n_kv_heads, head_dim, _ptr(qkv), _ptr(out),
+                                     _stream(stream)))
 
 
 class RMTModel:

@@ -66,6 +66,8 @@ SIGNATURES = {
                                     C.c_void_p, C.c_void_p]),
     "rmt_grouped_gemm": (C.c_int32, [C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_void_p,
                                      C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p]),
+    "rmt_causal_attention": (C.c_int32, [C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32,
+                                         C.c_void_p, C.c_void_p, C.c_void_p]),
     "rmt_last_error": (C.c_char_p, []),
 }
 

@@ -5,52 +5,59 @@
 // cells of a diagonal are covered by one launch (grid z = cell).
 //
 // One workgroup = 4 wave64s = 4 query heads that share one KV head, over a
-// block of QB query rows.  K and V come through LDS 64 keys at a time and are
-// shared by the 4 heads.  The kernel works on transposed scores
-// S^T = K Q^T (v_mfma_f32_16x16x32_bf16): the accumulator layout of S^T then
-// matches the B-operand layout that O^T += V^T P^T needs, so the
-// probabilities go from the softmax straight into the second MFMA without a
-// trip through LDS.  Online softmax in fp32 with exp2.
+// block of QB query rows.  K and V blocks of 64 keys go through a two-slot LDS
+// ring (the next block is fetched into registers while the current one is
+// used) and are shared by the 4 heads.
+//
+// Per 64-key block each wave computes transposed scores S^T = K Q^T with
+// v_mfma_f32_16x16x32_bf16: the S^T accumulator layout is exactly the
+// B-operand layout that O^T += V^T P^T needs, so probabilities go from the
+// softmax straight into the second MFMA.  V^T operands come from row-major V
+// through the transposing LDS read ds_read_b64_tr_b16.  The softmax is
+// online in fp32 and base 2 (one FMA + one v_exp_f32 per score); the running
+// output is rescaled only when a row maximum grows by more than 2^8, which
+// keeps every probability below 256 and leaves O / l unchanged.
 #include "kernels.h"
 
 namespace rmt {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 
-constexpr int KB = 64;  // keys per LDS block
+constexpr int KB = 64;            // keys per block
+constexpr float RESCALE_LOG2 = 8.0f;
 
-__device__ __forceinline__ uint16_t to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
-
-__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
-  return (uint32_t)to_bf16(lo) | ((uint32_t)to_bf16(hi) << 16);
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  bf16x2 v;
+  v[0] = (__bf16)lo;              // v_cvt_pk_bf16_f32: round to nearest even
+  v[1] = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 template <int HD, int QB>
 __global__ __launch_bounds__(256, 2) void attention_kernel(const uint16_t* __restrict__ qkv,
                                                            uint16_t* __restrict__ out, int R,
                                                            int Hq, int Hkv, float scale_log2) {
-  constexpr int QT = QB / 16;   // query tiles of 16 per wave
-  constexpr int KS = HD / 32;   // k-steps of 32 over the head dimension
-  constexpr int HT = HD / 16;   // head-dimension tiles of 16 in O^T
-  constexpr int LDK = HD + 8;   // sK row stride (elements)
-  constexpr int LDV = KB + 8;   // sVt row stride (elements)
-  __shared__ __attribute__((aligned(16))) uint16_t sK[KB * LDK];
-  __shared__ __attribute__((aligned(16))) uint16_t sVt[HD * LDV];
+  constexpr int QT = QB / 16;     // query tiles of 16 per wave
+  constexpr int KS = HD / 32;     // k-steps of 32 over the head dimension
+  constexpr int HT = HD / 16;     // head-dimension tiles of 16 in O^T
+  constexpr int LDK = HD + 8;     // K row stride: 16-byte reads of 16 rows hit distinct banks
+  constexpr int LDV = HD + 16;    // V row stride: 8-byte transposing reads of 8 rows tile the banks
+  constexpr int CH = HD / 8;      // 16-byte chunks per key row
+  constexpr int LOADS = KB * CH / 256;   // chunks per thread per block, for K and for V
+  __shared__ __attribute__((aligned(16))) uint16_t sK[2][KB * LDK];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[2][KB * LDV];
 
   const int tid = (int)threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int c16 = lane & 15;     // column within a 16-wide tile
-  const int g4 = lane >> 4;      // lane group 0..3
+  const int c16 = lane & 15;      // column within a 16-wide tile
+  const int g4 = lane >> 4;       // lane group 0..3
 
   const int nqb = (R + QB - 1) / QB;
   const int q0 = (nqb - 1 - (int)blockIdx.x) * QB;   // longest blocks first
@@ -82,38 +89,55 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const uint16_t* __res
   for (int ht = 0; ht < HT; ++ht)
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) o[ht][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float mrow[QT], lrow[QT];
+  float mref[QT], lrow[QT];       // mref: reference maximum in the scaled (log2) domain
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
-    mrow[qt] = -INFINITY;
+    mref[qt] = -INFINITY;
     lrow[qt] = 0.f;
   }
 
-  const int kend = min(q0 + QB, R);          // keys needed: [0, kend)
-  const int nkb = (kend + KB - 1) / KB;
-  constexpr int CH = HD / 8;                  // 16-byte chunks per key row
-  for (int kb = 0; kb < nkb; ++kb) {
-    const int k0 = kb * KB;
-    __syncthreads();
-    for (int c = tid; c < KB * CH; c += 256) {
+  // K/V block loads: thread chunk c -> key c / CH, columns (c % CH) * 8.
+  u32x4 rk[LOADS], rv[LOADS];
+  auto fetch = [&](int k0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int c = tid + 256 * i;
       const int r = c / CH;
       const int cc = (c % CH) * 8;
-      u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
+      rk[i] = u32x4{0u, 0u, 0u, 0u};
+      rv[i] = u32x4{0u, 0u, 0u, 0u};
       if (k0 + r < R) {
-        kv = *(const u32x4*)(Kp + (size_t)(k0 + r) * ld + cc);
-        vv = *(const u32x4*)(Vp + (size_t)(k0 + r) * ld + cc);
-      }
-      *(u32x4*)(sK + r * LDK + cc) = kv;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        sVt[(cc + 2 * e) * LDV + r] = (uint16_t)(vv[e] & 0xffffu);
-        sVt[(cc + 2 * e + 1) * LDV + r] = (uint16_t)(vv[e] >> 16);
+        rk[i] = *(const u32x4*)(Kp + (size_t)(k0 + r) * ld + cc);
+        rv[i] = *(const u32x4*)(Vp + (size_t)(k0 + r) * ld + cc);
       }
     }
-    __syncthreads();
+  };
+  auto stash = [&](int slot) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int c = tid + 256 * i;
+      const int r = c / CH;
+      const int cc = (c % CH) * 8;
+      *(u32x4*)(&sK[slot][r * LDK + cc]) = rk[i];
+      *(u32x2*)(&sV[slot][r * LDV + cc]) = u32x2{rv[i][0], rv[i][1]};
+      *(u32x2*)(&sV[slot][r * LDV + cc + 4]) = u32x2{rv[i][2], rv[i][3]};
+    }
+  };
+
+  const int kend = min(q0 + QB, R);          // keys needed: [0, kend)
+  const int nkb = (kend + KB - 1) / KB;
+  fetch(0);
+  stash(0);
+  __syncthreads();
+  for (int kb = 0; kb < nkb; ++kb) {
+    const int slot = kb & 1;
+    const int k0 = kb * KB;
+    if (kb + 1 < nkb) fetch(k0 + KB);
+    const uint16_t* K_ = sK[slot];
+    const uint16_t* V_ = sV[slot];
 
     // S^T block: 64 keys x QB queries.  Lane holds keys 16 kt + 4 g4 + j of
-    // query column 16 qt + c16.
+    // query column 16 qt + c16 (raw, unscaled scores).
     f32x4 s[4][QT];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)
@@ -124,81 +148,109 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const uint16_t* __res
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) {
         const bf16x8 kf = __builtin_bit_cast(
-            bf16x8, *(const u32x4*)(sK + (16 * kt + c16) * LDK + 32 * ks + 8 * g4));
+            bf16x8, *(const u32x4*)(K_ + (16 * kt + c16) * LDK + 32 * ks + 8 * g4));
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt)
           s[kt][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[qt][ks], s[kt][qt], 0, 0, 0);
       }
 
-    const bool need_mask = (k0 + KB - 1 > q0) || (k0 + KB > R);
+    if ((k0 + KB - 1 > q0) || (k0 + KB > R)) {   // block touches the diagonal or the end
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) {
+        const int q = q0 + 16 * qt + c16;
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int key = k0 + 16 * kt + 4 * g4 + j;
+            if (key > q || key >= R) s[kt][qt][j] = -INFINITY;
+          }
+      }
+    }
+
+    bool need_rescale = false;
+    float mnew[QT];
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
-      const int q = q0 + 16 * qt + c16;
       float mx = -INFINITY;
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          float v = s[kt][qt][j] * scale_log2;
-          if (need_mask) {
-            const int key = k0 + 16 * kt + 4 * g4 + j;
-            if (key > q || key >= R) v = -INFINITY;
-          }
-          s[kt][qt][j] = v;
-          mx = fmaxf(mx, v);
-        }
+        mx = fmaxf(mx, fmaxf(fmaxf(s[kt][qt][0], s[kt][qt][1]), fmaxf(s[kt][qt][2], s[kt][qt][3])));
       mx = fmaxf(mx, __shfl_xor(mx, 16));
       mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mnew = fmaxf(mrow[qt], mx);
-      const float corr = exp2f(mrow[qt] - mnew);
+      mnew[qt] = mx * scale_log2;
+      need_rescale |= mnew[qt] > mref[qt] + RESCALE_LOG2;
+    }
+    if (__any(need_rescale)) {
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) {
+        const float m2 = fmaxf(mref[qt], mnew[qt]);
+        const float corr = __builtin_amdgcn_exp2f(mref[qt] - m2);   // 0 on the first block
+        mref[qt] = m2;
+        lrow[qt] *= corr;
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht) o[ht][qt] *= corr;
+      }
+    }
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
       float sum = 0.f;
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const float p = exp2f(s[kt][qt][j] - mnew);
+          const float p = __builtin_amdgcn_exp2f(fmaf(s[kt][qt][j], scale_log2, -mref[qt]));
           s[kt][qt][j] = p;
           sum += p;
         }
       sum += __shfl_xor(sum, 16);
       sum += __shfl_xor(sum, 32);
-      lrow[qt] = lrow[qt] * corr + sum;
-      mrow[qt] = mnew;
-#pragma unroll
-      for (int ht = 0; ht < HT; ++ht) o[ht][qt] *= corr;
+      lrow[qt] += sum;
     }
 
-    // O^T += V^T P^T over two 32-key steps.  In step ks2 lane slot e < 4 is key
-    // 32 ks2 + 4 g4 + e and slot e >= 4 is key 32 ks2 + 16 + 4 g4 + (e - 4),
-    // matching where the S^T accumulator left those probabilities.
+    // O^T += V^T P^T over two 32-key steps.  In step ks2, operand slot e < 4
+    // is key 32 ks2 + 4 g4 + e and slot e >= 4 is key 32 ks2 + 16 + 4 g4 +
+    // (e - 4), matching where the S^T accumulator left those probabilities.
+    // The transposing read: lane j of each 16-lane group points at row
+    // key0 + j / 4, columns 4 (j % 4) .. +3; lane i receives column i of the
+    // four rows.
+    const int tr_row = 4 * g4 + (c16 >> 2);
+    const int tr_col = 4 * (c16 & 3);
 #pragma unroll
     for (int ks2 = 0; ks2 < 2; ++ks2) {
       bf16x8 pf[QT];
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt) {
         u32x4 w;
-        w[0] = pack2(s[2 * ks2][qt][0], s[2 * ks2][qt][1]);
-        w[1] = pack2(s[2 * ks2][qt][2], s[2 * ks2][qt][3]);
-        w[2] = pack2(s[2 * ks2 + 1][qt][0], s[2 * ks2 + 1][qt][1]);
-        w[3] = pack2(s[2 * ks2 + 1][qt][2], s[2 * ks2 + 1][qt][3]);
+        w[0] = pack_bf16(s[2 * ks2][qt][0], s[2 * ks2][qt][1]);
+        w[1] = pack_bf16(s[2 * ks2][qt][2], s[2 * ks2][qt][3]);
+        w[2] = pack_bf16(s[2 * ks2 + 1][qt][0], s[2 * ks2 + 1][qt][1]);
+        w[3] = pack_bf16(s[2 * ks2 + 1][qt][2], s[2 * ks2 + 1][qt][3]);
         pf[qt] = __builtin_bit_cast(bf16x8, w);
       }
 #pragma unroll
       for (int ht = 0; ht < HT; ++ht) {
-        const uint16_t* vrow = sVt + (16 * ht + c16) * LDV + 32 * ks2 + 4 * g4;
+        const uint16_t* v0 = V_ + (32 * ks2 + tr_row) * LDV + 16 * ht + tr_col;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)(v0));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)(v0 + 16 * LDV));
         u32x4 w;
-        const u32x2 lo = *(const u32x2*)(vrow);
-        const u32x2 hi = *(const u32x2*)(vrow + 16);
-        w[0] = lo[0];
-        w[1] = lo[1];
-        w[2] = hi[0];
-        w[3] = hi[1];
+        const u32x2 wl = __builtin_bit_cast(u32x2, lo);
+        const u32x2 wh = __builtin_bit_cast(u32x2, hi);
+        w[0] = wl[0];
+        w[1] = wl[1];
+        w[2] = wh[0];
+        w[3] = wh[1];
         const bf16x8 vf = __builtin_bit_cast(bf16x8, w);
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt)
           o[ht][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[qt], o[ht][qt], 0, 0, 0);
       }
     }
+
+    if (kb + 1 < nkb) stash(slot ^ 1);
+    __syncthreads();
   }
 
   // O^T accumulator: lane holds head dims 16 ht + 4 g4 + j of query 16 qt + c16.
@@ -211,8 +263,8 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const uint16_t* __res
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
       u32x2 w;
-      w[0] = pack2(o[ht][qt][0] * inv, o[ht][qt][1] * inv);
-      w[1] = pack2(o[ht][qt][2] * inv, o[ht][qt][3] * inv);
+      w[0] = pack_bf16(o[ht][qt][0] * inv, o[ht][qt][1] * inv);
+      w[1] = pack_bf16(o[ht][qt][2] * inv, o[ht][qt][3] * inv);
       *(u32x2*)(orow + 16 * ht + 4 * g4) = w;
     }
   }
@@ -226,7 +278,7 @@ hipError_t launch_attention(const uint16_t* qkv, uint16_t* out, int G, int R, in
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)hd);
   const int quads = (Hq / Hkv) / 4;
   if (hd == 64) {
-    constexpr int QB = 64;
+    constexpr int QB = 32;   // measured faster than 64: lower register use, more waves
     dim3 grid((R + QB - 1) / QB, Hkv * quads, G);
     hipLaunchKernelGGL((attention_kernel<64, QB>), grid, dim3(256), 0, stream, qkv, out, R, Hq,
                        Hkv, scale_log2);

@@ -46,12 +46,8 @@ constexpr int BUF_FLAGS = 0x00020000;        // raw buffer, 32-bit data format
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-__device__ __forceinline__ uint16_t to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
+// fp32 -> bf16, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint16_t to_bf16(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 
 // Chunk permutation of LDS row r: logical 16-byte chunk c sits at physical
 // position c ^ swz(r).  It depends only on r mod 32, and 16-byte reads of 32

@@ -614,4 +614,16 @@ int32_t rmt_grouped_gemm(int32_t G, int32_t Mr, int32_t N, int32_t K, const void
   return RMT_OK;
 }
 
+int32_t rmt_causal_attention(int32_t G, int32_t R, int32_t Hq, int32_t Hkv, int32_t hd,
+                             const void* qkv, void* out, void* stream) {
+  if (G < 1 || G > 65535 || R < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0)
+    return fail(RMT_EINVAL, "need 1 <= G <= 65535, R >= 1 and n_heads a multiple of n_kv_heads");
+  if (!qkv || !out) return fail(RMT_EINVAL, "qkv and out must be non-NULL");
+  if (hd != 64 && hd != 128) return fail(RMT_EUNSUPPORTED, "head_dim must be 64 or 128");
+  if ((Hq / Hkv) % 4 != 0) return fail(RMT_EUNSUPPORTED, "n_heads / n_kv_heads must be a multiple of 4");
+  if ((int64_t)G * R * (Hq + 2 * Hkv) * hd > ((int64_t)1 << 40)) return fail(RMT_EINVAL, "sizes too large");
+  HIP_TRY(launch_attention((const uint16_t*)qkv, (uint16_t*)out, G, R, Hq, Hkv, hd, (hipStream_t)stream));
+  return RMT_OK;
+}
+
 }  // extern "C"

@@ -1,0 +1,57 @@
+"""rmt_causal_attention against the oracle's causal grouped-query attention on
+the same bf16 inputs.  The kernel rounds probabilities and the output to
+bf16, so agreement is to bf16 resolution: relative L2 <= 1e-2 and max
+abs error <= 2e-2 of the largest output."""
+import math
+
+import numpy as np
+import pytest
+
+import rmt_inputs as ri
+from oracle import rmt_oracle as orc
+from rmt_inputs import device as rdev
+
+import gpu_util as gu
+
+pytestmark = [pytest.mark.gpu, gu.needs_gpu]
+
+
+def _bf16_to_np(t):
+    import torch
+    bits = t.view(torch.int16).cpu().numpy().view(np.uint16).astype(np.uint32)
+    return (bits << np.uint32(16)).view(np.float32)
+
+
+@pytest.mark.parametrize("G,R,Hq,Hkv,hd", [(1, 1, 4, 1, 64), (3, 100, 8, 2, 64), (2, 240, 4, 1, 128),
+                                           (2, 1152, 8, 2, 64), (1, 129, 8, 1, 128), (2, 200, 16, 2, 64)])
+def test_attention_matches_oracle(G, R, Hq, Hkv, hd):
+    import torch
+    import long_context_anti_amd as rmt
+    gu.say(f"[attention] G={G} R={R} Hq={Hq} Hkv={Hkv} hd={hd}")
+    rng = np.random.default_rng(R * 7 + hd)
+    W = (Hq + 2 * Hkv) * hd
+    qkv = ri.round_bf16((rng.standard_normal((G, R, W)) * 1.5).astype(np.float32))
+    qkv_d = rdev.bf16_tensor(qkv)
+    out_d = torch.empty((G, R, Hq * hd), dtype=torch.bfloat16, device="cuda")
+    rmt.causal_attention(qkv_d, out_d, Hq, Hkv, hd)
+    torch.cuda.synchronize()
+    out = _bf16_to_np(out_d)
+    for g in range(G):
+        q = qkv[g, :, :Hq * hd].reshape(R, Hq, hd)
+        k = qkv[g, :, Hq * hd:(Hq + Hkv) * hd].reshape(R, Hkv, hd)
+        v = qkv[g, :, (Hq + Hkv) * hd:].reshape(R, Hkv, hd)
+        ref = orc.causal_gqa_attention(q.astype(np.float64), k.astype(np.float64), v.astype(np.float64))
+        err = np.linalg.norm(out[g] - ref) / np.linalg.norm(ref)
+        assert err <= 1e-2, err
+        assert np.max(np.abs(out[g] - ref)) <= 2e-2 * np.max(np.abs(ref))
+
+
+def test_attention_rejects_bad_arguments():
+    import ctypes as C
+    from long_context_anti_amd import _lib
+    h = _lib.lib()
+    p = C.c_void_p(256)
+    assert h.rmt_causal_attention(1, 10, 8, 2, 96, p, p, None) == _lib.RMT_EUNSUPPORTED
+    assert h.rmt_causal_attention(1, 10, 6, 2, 64, p, p, None) == _lib.RMT_EUNSUPPORTED
+    assert h.rmt_causal_attention(0, 10, 8, 2, 64, p, p, None) == _lib.RMT_EINVAL
+    assert h.rmt_causal_attention(1, 10, 8, 2, 64, None, p, None) == _lib.RMT_EINVAL
