@@ -35,6 +35,9 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int BN = 256;
 constexpr int BK = 64;
@@ -46,8 +49,13 @@ constexpr int BUF_FLAGS = 0x00020000;        // raw buffer, 32-bit data format
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-// fp32 -> bf16, round to nearest even (v_cvt_pk_bf16_f32).
-__device__ __forceinline__ uint16_t to_bf16(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+// Two fp32 -> packed bf16, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  bf16x2 v;
+  v[0] = (__bf16)lo;
+  v[1] = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, v);
+}
 
 // Chunk permutation of LDS row r: logical 16-byte chunk c sits at physical
 // position c ^ swz(r).  It depends only on r mod 32, and 16-byte reads of 32
@@ -81,6 +89,10 @@ template <int EPI, int BM, int WTM, int WTN>
 __global__ __launch_bounds__((BM / WTM) * (BN / WTN) * 64, 1) void gemm_bf16_kernel(
     GemmArgs a, GroupTable tab) {
   constexpr int STAGE_BYTES = (BM + BN) * ROWB;
+  // The MFMAs take the operands swapped, so the accumulator holds C^T blocks
+  // and every lane owns four consecutive output columns of one row: the
+  // epilogues then move 8- and 16-byte vectors instead of single elements.
+  constexpr bool SWAP = true;
   constexpr int WAVES_N = BN / WTN;
   constexpr int NWAVES = (BM / WTM) * WAVES_N;
   constexpr int MI = WTM / 32;
@@ -183,7 +195,10 @@ __global__ __launch_bounds__((BM / WTM) * (BN / WTN) * 64, 1) void gemm_bf16_ker
       for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int t = 0; t < NI; ++t)
-          acc[i][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[j & 1][i], bfr[j & 1][t], acc[i][t], 0, 0, 0);
+          if constexpr (SWAP)
+            acc[i][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j & 1][t], af[j & 1][i], acc[i][t], 0, 0, 0);
+          else
+            acc[i][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[j & 1][i], bfr[j & 1][t], acc[i][t], 0, 0, 0);
       // let the scheduler interleave LDS reads with the MFMA chain
       __builtin_amdgcn_iglp_opt(1);
     }
@@ -211,25 +226,29 @@ __global__ __launch_bounds__((BM / WTM) * (BN / WTN) * 64, 1) void gemm_bf16_ker
     if (wave_live) compute(kt % STAGES);
   }
 
-  // Accumulator layout of a 32x32 block: element e of lane l sits at
-  // row 8*(e/4) + 4*(l/32) + e%4, column l%32.
-  const int row_base = tm * BM + wm * WTM + 4 * (lane >> 5);
-  const int col_base = tn * BN + wn * WTN + r32;
+  // Accumulator layout (C^T blocks): element e of lane l of block (i, t) is
+  // row i*32 + l%32, column t*32 + 8*(e/4) + 4*(l/32) + e%4 -- four
+  // consecutive columns for each e/4.
+  const int row0 = tm * BM + wm * WTM + r32;
+  const int col0 = tn * BN + wn * WTN + 4 * (lane >> 5);
 
   if constexpr (EPI == EPI_STORE_BF16) {
     uint16_t* C = (uint16_t*)tab.out_lo[g];
 #pragma unroll
-    for (int i = 0; i < MI; ++i)
+    for (int i = 0; i < MI; ++i) {
+      const int row = row0 + i * 32;
+      if (row >= a.M) continue;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int row = row_base + i * 32 + 8 * (e >> 2) + (e & 3);
-        if (row >= a.M) continue;
+      for (int t = 0; t < NI; ++t)
 #pragma unroll
-        for (int t = 0; t < NI; ++t) {
-          const int col = col_base + t * 32;
-          if (col < a.N) C[(size_t)row * a.ld_out + col] = to_bf16(acc[i][t][e]);
+        for (int q = 0; q < 4; ++q) {
+          const int col = col0 + t * 32 + 8 * q;
+          if (col >= a.N) continue;
+          *(u32x2*)(C + (size_t)row * a.ld_out + col) =
+              u32x2{pack_bf16(acc[i][t][4 * q], acc[i][t][4 * q + 1]),
+                    pack_bf16(acc[i][t][4 * q + 2], acc[i][t][4 * q + 3])};
         }
-      }
+    }
   } else if constexpr (EPI == EPI_QKV_ROPE) {
     // The wave's WTN columns start on a head boundary (WTN is a multiple of
     // hd), so column c < hd/2 of a head and its partner c + hd/2 sit in the
@@ -240,72 +259,93 @@ __global__ __launch_bounds__((BM / WTM) * (BN / WTN) * 64, 1) void gemm_bf16_ker
 #pragma unroll
     for (int t = 0; t < NI; ++t) {
       if (((t / P) & 1) != 0) continue;
-      const int col = col_base + t * 32;
-      if (col >= a.N) continue;
-      const bool rot = col < a.rope_cols;
-      const int hc = col % a.hd;
       const int tp = t + P;
 #pragma unroll
-      for (int i = 0; i < MI; ++i)
+      for (int i = 0; i < MI; ++i) {
+        const int row = row0 + i * 32;
+        if (row >= a.M) continue;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int row = row_base + i * 32 + 8 * (e >> 2) + (e & 3);
-          if (row >= a.M) continue;
-          float x1 = acc[i][t][e];
-          float x2 = 0.f;
+        for (int q = 0; q < 4; ++q) {
+          const int col = col0 + t * 32 + 8 * q;
+          if (col >= a.N) continue;
+          float x1[4], x2[4];
 #pragma unroll
-          for (int q = 0; q < NI; ++q)
-            if (q == tp) x2 = acc[i][q][e];
-          float y1 = x1, y2 = x2;
-          if (rot) {
-            const float2 cs = a.rope[(size_t)row * half + hc];
-            y1 = x1 * cs.x - x2 * cs.y;
-            y2 = x2 * cs.x + x1 * cs.y;
+          for (int e = 0; e < 4; ++e) {
+            x1[e] = acc[i][t][4 * q + e];
+            x2[e] = 0.f;
+#pragma unroll
+            for (int u = 0; u < NI; ++u)
+              if (u == tp) x2[e] = acc[i][u][4 * q + e];
           }
-          C[(size_t)row * a.ld_out + col] = to_bf16(y1);
-          C[(size_t)row * a.ld_out + col + half] = to_bf16(y2);
+          if (col < a.rope_cols) {
+            const float2* cs = a.rope + (size_t)row * half + col % a.hd;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float2 c = cs[e];
+              const float y1 = x1[e] * c.x - x2[e] * c.y;
+              const float y2 = x2[e] * c.x + x1[e] * c.y;
+              x1[e] = y1;
+              x2[e] = y2;
+            }
+          }
+          uint16_t* dst = C + (size_t)row * a.ld_out + col;
+          *(u32x2*)dst = u32x2{pack_bf16(x1[0], x1[1]), pack_bf16(x1[2], x1[3])};
+          *(u32x2*)(dst + half) = u32x2{pack_bf16(x2[0], x2[1]), pack_bf16(x2[2], x2[3])};
         }
+      }
     }
   } else if constexpr (EPI == EPI_SWIGLU) {
     // Packed columns come in 64-wide blocks: 32 gate columns then the 32 up
-    // columns of the same outputs; output column = block * 32 + (l % 32).
+    // columns of the same outputs; output column = block * 32 + offset.
     uint16_t* U = (uint16_t*)tab.out_lo[g];
 #pragma unroll
     for (int t = 0; t < NI; t += 2) {
-      const int col = col_base + t * 32;
-      if (col >= a.N) continue;
-      const int ocol = (col >> 6) * 32 + r32;
 #pragma unroll
-      for (int i = 0; i < MI; ++i)
+      for (int i = 0; i < MI; ++i) {
+        const int row = row0 + i * 32;
+        if (row >= a.M) continue;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int row = row_base + i * 32 + 8 * (e >> 2) + (e & 3);
-          if (row >= a.M) continue;
-          const float gt = acc[i][t][e];
-          const float up = acc[i][t + 1][e];
-          const float u = gt / (1.0f + expf(-gt)) * up;
-          U[(size_t)row * a.ld_out + ocol] = to_bf16(u);
+        for (int q = 0; q < 4; ++q) {
+          const int col = col0 + t * 32 + 8 * q;
+          if (col >= a.N) continue;
+          const int ocol = (col >> 6) * 32 + (col & 31);
+          float u[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float gt = acc[i][t][4 * q + e];
+            const float up = acc[i][t + 1][4 * q + e];
+            u[e] = gt / (1.0f + __expf(-gt)) * up;
+          }
+          *(u32x2*)(U + (size_t)row * a.ld_out + ocol) =
+              u32x2{pack_bf16(u[0], u[1]), pack_bf16(u[2], u[3])};
         }
+      }
     }
   } else {  // EPI_RESID_F32
 #pragma unroll
-    for (int i = 0; i < MI; ++i)
+    for (int i = 0; i < MI; ++i) {
+      const int row = row0 + i * 32;
+      if (row >= a.M) continue;
+      const float* res = row < a.split_in
+                             ? (const float*)tab.in_lo[g] + (size_t)row * a.ld_res
+                             : (const float*)tab.in_hi[g] + (size_t)(row - a.split_in) * a.ld_res;
+      float* out = row < a.split_out
+                       ? (float*)tab.out_lo[g] + (size_t)row * a.ld_out
+                       : (float*)tab.out_hi[g] + (size_t)(row - a.split_out) * a.ld_out;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int row = row_base + i * 32 + 8 * (e >> 2) + (e & 3);
-        if (row >= a.M) continue;
-        const float* res = row < a.split_in
-                               ? (const float*)tab.in_lo[g] + (size_t)row * a.ld_res
-                               : (const float*)tab.in_hi[g] + (size_t)(row - a.split_in) * a.ld_res;
-        float* out = row < a.split_out
-                         ? (float*)tab.out_lo[g] + (size_t)row * a.ld_out
-                         : (float*)tab.out_hi[g] + (size_t)(row - a.split_out) * a.ld_out;
+      for (int t = 0; t < NI; ++t)
 #pragma unroll
-        for (int t = 0; t < NI; ++t) {
-          const int col = col_base + t * 32;
-          if (col < a.N) out[col] = acc[i][t][e] + res[col];
+        for (int q = 0; q < 4; ++q) {
+          const int col = col0 + t * 32 + 8 * q;
+          if (col >= a.N) continue;
+          f32x4 r = *(const f32x4*)(res + col);
+          r[0] += acc[i][t][4 * q + 0];
+          r[1] += acc[i][t][4 * q + 1];
+          r[2] += acc[i][t][4 * q + 2];
+          r[3] += acc[i][t][4 * q + 3];
+          *(f32x4*)(out + col) = r;
         }
-      }
+    }
   }
 }
 
