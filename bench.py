@@ -17,7 +17,6 @@ G = 1, 4, 8, 16, and the CPU oracle timed on a prefix of the sequence.
 from __future__ import annotations
 
 import argparse
-import concurrent.futures as cf
 import json
 import os
 import sys
@@ -39,8 +38,7 @@ def log(msg):
 
 def gen_layers(cfg, seed=0):
     import rmt_inputs as ri
-    with cf.ThreadPoolExecutor(max_workers=8) as ex:
-        return list(ex.map(lambda l: ri.layer_weights(cfg, l, seed), range(cfg.L)))
+    return ri.all_weights(cfg, seed, workers=8)
 
 
 def timed_steps(fn, steps, stream):

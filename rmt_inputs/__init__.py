@@ -188,9 +188,15 @@ def layer_weights(cfg: RMTConfig, layer: int, seed: int = 0) -> Dict[str, np.nda
     return out
 
 
-def all_weights(cfg: RMTConfig, seed: int = 0, layers: Optional[range] = None):
+def all_weights(cfg: RMTConfig, seed: int = 0, layers: Optional[range] = None, workers: int = 1):
+    """Per-layer weights.  `workers` > 1 draws layers on a thread pool (each
+    layer has its own generator, so the values do not depend on it)."""
     layers = range(cfg.L) if layers is None else layers
-    return [layer_weights(cfg, l, seed) for l in layers]
+    if workers <= 1:
+        return [layer_weights(cfg, l, seed) for l in layers]
+    import concurrent.futures as cf
+    with cf.ThreadPoolExecutor(max_workers=workers) as ex:
+        return list(ex.map(lambda l: layer_weights(cfg, l, seed), layers))
 
 
 def embedding(cfg: RMTConfig, seed: int = 0) -> np.ndarray:

@@ -30,7 +30,7 @@ def inputs(cfg, S=None, seed=0):
     """Seeded weights, segment inputs, initial memory and embedding of a
     workload prefix of S segments."""
     S = cfg.S if S is None else S
-    w = ri.all_weights(cfg, seed)
+    w = ri.all_weights(cfg, seed, workers=8)
     mem0 = ri.initial_memory(cfg, seed)
     if cfg.cell == ri.CELL_LLAMA:
         return w, ri.tokens(cfg, seed, S=S), mem0, ri.embedding(cfg, seed)
