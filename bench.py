@@ -41,6 +41,24 @@ def gen_layers(cfg, seed=0):
     return ri.all_weights(cfg, seed, workers=8)
 
 
+def measured_traffic():
+    """HBM bytes per gate/up launch from the committed counter summary, used
+    only while the GEMM source is the one the counters were taken on."""
+    import hashlib
+    import re
+    src = os.path.join(ROOT, "long_context_anti_amd", "csrc", "gemm_bf16.hip")
+    summ = os.path.join(ROOT, "profiles", "llama1b_rmt_L16_S128_gateup_hbm_traffic.md")
+    try:
+        text = open(summ).read()
+        h = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+        if f"sha256 prefix: {h}" not in text:
+            return None
+        m = re.search(r"traffic \(bench roofline field\) = ([0-9.]+) GB \+ ([0-9.]+) GB", text)
+        return round((float(m.group(1)) + float(m.group(2))) * 1e9) if m else None
+    except OSError:
+        return None
+
+
 def timed_steps(fn, steps, stream):
     import torch
     torch.cuda.synchronize()
@@ -116,6 +134,8 @@ def main():
     ap.add_argument("--no-seq", action="store_true", help="skip the sequential path")
     ap.add_argument("--no-sweep", action="store_true", help="skip the isolated grouped-GEMM sweep")
     ap.add_argument("--cpu-segments", type=int, default=2)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 1 GiB device copy, the reference for HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: the diagonal sweep is measured on a single "
@@ -185,11 +205,12 @@ def main():
             gemm_ms += v["ms"]
     gemm_tf = gemm_flops / (gemm_ms / 1e3) / 1e12 if gemm_ms else 0.0
 
+    traffic = measured_traffic()
     gu = stages["gateup"]
     achieved = gu["flops"] / gu["launches"] / (gu["ms"] / 1e3 / gu["launches"]) / 1e12
     roofline = {"kernel": "grouped GEMM, gate/up stage + SwiGLU epilogue (gemm_bf16_kernel<2>)",
                 "bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                 "avg_launch_us": round(gu["ms"] / gu["launches"] * 1e3, 2),
                 "flops_per_launch": gu["flops"] / gu["launches"]}
 
@@ -239,6 +260,13 @@ def main():
         log(f"[bench] CPU oracle on {Sp} segments ...")
         result["cpu_baseline"] = cpu_baseline(cfg, layers, tokens, mem0, embed, hidden_np,
                                               gpu_mem_prefix, Sp)
+    if args.calibrate_copy:
+        src = torch.ones(256 * 2**20, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     model.close()
     del emb_dev
     print(json.dumps(result), flush=True)
