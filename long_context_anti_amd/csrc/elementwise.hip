@@ -24,7 +24,10 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 // One wave per row, four rows per workgroup.  Row r of group g comes from
 // in_lo[g] (r < split_in) or in_hi[g]; the normalised row goes to the packed
-// bf16 matrix at row g*R + r.  Requires d % 4 == 0.
+// bf16 matrix at row g*R + r.  Rows of up to 64*4*VPL elements stay in
+// registers between the sum of squares and the scaling, so each input byte
+// is read once; wider rows take a second pass.  Requires d % 4 == 0.
+template <int VPL>
 __global__ __launch_bounds__(256) void rmsnorm_kernel(int total_rows, int R, int d, int split_in,
                                                       GroupTable tab, const float* __restrict__ gamma,
                                                       float eps, uint16_t* __restrict__ out) {
@@ -36,24 +39,36 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(int total_rows, int R, int
   const float* src = r < split_in ? (const float*)tab.in_lo[g] + (size_t)r * d
                                   : (const float*)tab.in_hi[g] + (size_t)(r - split_in) * d;
   const float* gm = gamma + (size_t)tab.layer[g] * d;
+  uint16_t* dst = out + (size_t)row * d;
+  f32x4 v[VPL];
   float ss = 0.f;
-  for (int c = lane * 4; c < d; c += 256) {
-    const f32x4 v = *(const f32x4*)(src + c);
-    ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
+#pragma unroll
+  for (int j = 0; j < VPL; ++j) {
+    const int c = (lane + 64 * j) * 4;
+    v[j] = c < d ? *(const f32x4*)(src + c) : f32x4{0.f, 0.f, 0.f, 0.f};
+    ss += v[j][0] * v[j][0] + v[j][1] * v[j][1] + v[j][2] * v[j][2] + v[j][3] * v[j][3];
+  }
+  for (int c = (lane + 64 * VPL) * 4; c < d; c += 256) {
+    const f32x4 x = *(const f32x4*)(src + c);
+    ss += x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3];
   }
   ss = wave_sum(ss);
   const float inv = 1.0f / sqrtf(ss / (float)d + eps);
-  uint16_t* dst = out + (size_t)row * d;
-  for (int c = lane * 4; c < d; c += 256) {
-    const f32x4 v = *(const f32x4*)(src + c);
+  auto emit = [&](int c, const f32x4& x) __attribute__((always_inline)) {
     const f32x4 w = *(const f32x4*)(gm + c);
     u16x4 o;
-    o[0] = to_bf16(v[0] * inv * w[0]);
-    o[1] = to_bf16(v[1] * inv * w[1]);
-    o[2] = to_bf16(v[2] * inv * w[2]);
-    o[3] = to_bf16(v[3] * inv * w[3]);
+    o[0] = to_bf16(x[0] * inv * w[0]);
+    o[1] = to_bf16(x[1] * inv * w[1]);
+    o[2] = to_bf16(x[2] * inv * w[2]);
+    o[3] = to_bf16(x[3] * inv * w[3]);
     *(u16x4*)(dst + c) = o;
+  };
+#pragma unroll
+  for (int j = 0; j < VPL; ++j) {
+    const int c = (lane + 64 * j) * 4;
+    if (c < d) emit(c, v[j]);
   }
+  for (int c = (lane + 64 * VPL) * 4; c < d; c += 256) emit(c, *(const f32x4*)(src + c));
 }
 
 // Embedding lookup of one segment's n token ids into an fp32 slot.  An id
@@ -166,7 +181,8 @@ hipError_t launch_rmsnorm(int G, int R, int d, int split_in, const GroupTable& t
                           const float* gamma, float eps, uint16_t* out, hipStream_t stream) {
   const int rows = G * R;
   if (rows == 0) return hipSuccess;
-  hipLaunchKernelGGL(rmsnorm_kernel, dim3((rows + 3) / 4), dim3(256), 0, stream, rows, R, d,
+  // 16 float4 per lane keep rows of up to 4096 elements in registers
+  hipLaunchKernelGGL(rmsnorm_kernel<16>, dim3((rows + 3) / 4), dim3(256), 0, stream, rows, R, d,
                      split_in, tab, gamma, eps, out);
   return hipGetLastError();
 }
