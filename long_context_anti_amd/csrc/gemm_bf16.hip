@@ -9,12 +9,12 @@
 // a diagonal, whatever their number.
 //
 // Design (measured on MI355X; the operand stream from L2, not the MFMA rate,
-// is what limits this kernel, so the tile is as large as LDS allows):
-//   * 256 x 256 output tiles, eight wave64s of 64 x 128 each, as 2 x 4
-//     blocks of v_mfma_f32_32x32x16_bf16; 128 x 256 tiles when a launch is
-//     too small to fill the GPU twice.  A cell (group) never shares a tile
-//     with another; the rows past the cell's end read as zeros and waves that
-//     own only such rows skip their MFMAs.
+// is what limits this kernel, so tiles are as large as LDS allows):
+//   * Output tiles of 288 x 256, 256 x 256 or 128 x 256, chosen per launch
+//     by a cost model of whole rounds of one tile per CU (see launch_epi);
+//     waves compute 32 x 32 blocks with v_mfma_f32_32x32x16_bf16.  A cell
+//     (group) never shares a tile with another; the rows past the cell's end
+//     read as zeros and waves that own only such rows skip their MFMAs.
 //   * K advances 64 at a time through a two-slice LDS ring filled by buffer
 //     loads that write LDS directly (no staging registers).  LDS rows are
 //     unpadded; their 16-byte chunks are XOR-swizzled so MFMA operand reads
@@ -97,10 +97,14 @@ __global__ __launch_bounds__((BM / WTM) * (BN / WTN) * 64, 1) void gemm_bf16_ker
   constexpr int NWAVES = (BM / WTM) * WAVES_N;
   constexpr int MI = WTM / 32;
   constexpr int NI = WTN / 32;
-  constexpr int A_PER_WAVE = BM / RPI / NWAVES;
-  constexpr int B_PER_WAVE = BN / RPI / NWAVES;
-  constexpr int LOADS_PER_WAVE = A_PER_WAVE + B_PER_WAVE;
-  static_assert(A_PER_WAVE * RPI * NWAVES == BM && B_PER_WAVE * RPI * NWAVES == BN, "load split");
+  // The (BM + BN) / RPI wave-wide loads of a K slice are dealt round-robin
+  // to the waves; the count per wave differs by at most one.
+  constexpr int A_LOADS = BM / RPI;
+  constexpr int ALL_LOADS = (BM + BN) / RPI;
+  constexpr int LOADS_PER_WAVE = (ALL_LOADS + NWAVES - 1) / NWAVES;
+  static_assert(A_LOADS * RPI == BM && ALL_LOADS * RPI == BM + BN, "load split");
+  // vmcnt-based waits for slices still in flight need the same count per wave
+  static_assert(STAGES == 2 || ALL_LOADS % NWAVES == 0, "uneven load split needs a two-slice ring");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * STAGE_BYTES];
 
   const int tiles_m = (a.M + BM - 1) / BM;
@@ -138,20 +142,17 @@ __global__ __launch_bounds__((BM / WTM) * (BN / WTN) * 64, 1) void gemm_bf16_ker
     const int k0 = kt * BK;
     uint8_t* sbase = smem + stage * STAGE_BYTES;
 #pragma unroll
-    for (int i = 0; i < A_PER_WAVE; ++i) {
-      const int q = wave * A_PER_WAVE + i;
-      const int row = q * RPI + lrow;
+    for (int i = 0; i < LOADS_PER_WAVE; ++i) {
+      const int q = wave + i * NWAVES;          // wave-uniform
+      if (ALL_LOADS % NWAVES != 0 && q >= ALL_LOADS) break;
+      // i is a constant after unrolling: the operand is known at compile time
+      // unless the A/B boundary falls inside this round of loads
+      const bool is_a = (i + 1) * NWAVES <= A_LOADS ? true : i * NWAVES >= A_LOADS ? false : q < A_LOADS;
+      const int row = (is_a ? q : q - A_LOADS) * RPI + lrow;
       const int k = k0 + 8 * (lp ^ swz(row));
-      const int off = k < K ? (row * K + k) * 2 : a_bytes;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(sbase + q * 1024), 16, off, 0, 0, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < B_PER_WAVE; ++i) {
-      const int q = wave * B_PER_WAVE + i;
-      const int row = q * RPI + lrow;
-      const int k = k0 + 8 * (lp ^ swz(row));
-      const int off = k < K ? (row * K + k) * 2 : b_bytes;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(sbase + BM * ROWB + q * 1024), 16, off, 0, 0, 0);
+      const int nbytes = is_a ? a_bytes : b_bytes;
+      const int off = k < K ? (row * K + k) * 2 : nbytes;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(is_a ? ra : rb, (lds_ptr_t)(sbase + q * 1024), 16, off, 0, 0, 0);
     }
   };
 
@@ -356,17 +357,47 @@ void launch_one(const GemmArgs& a, const GroupTable& tab, hipStream_t stream) {
   hipLaunchKernelGGL((gemm_bf16_kernel<EPI, BM, WTM, WTN>), dim3(tiles), dim3(threads), 0, stream, a, tab);
 }
 
-// 256 x 256 tiles halve the operand bytes each MFMA needs from L2 compared
-// with 128-row tiles; launches that would leave the 256 CUs with fewer than
-// two rounds of such tiles use 128-row tiles instead.  Both use the same K
-// slicing and lane/k assignment, so a cell's result does not depend on the
-// choice.  Eight waves: 64 x 128 sub-tiles (64 x 64 for 128-row tiles, where
-// RoPE on 128-wide heads takes 32 x 128).
+// Tile shapes.  The operand bytes a tile pulls from L2 per MFMA fall as the
+// tile grows, but a launch runs in rounds of one tile per CU, so the rows a
+// tile leaves empty at a cell's end and a last round that is only partly
+// filled cost as much as useful work.  Each launch takes the shape with the
+// smallest estimated time, rounds x rows per tile / relative speed, the
+// speeds measured on MI355X for 256-CU rounds:
+//   288 x 256: twelve waves of 96 x 64 (3 x 2 blocks); a 1152-row cell is
+//              exactly four tiles.                              speed 1.00
+//   256 x 256: eight waves of 64 x 128 (2 x 4 blocks).           speed 0.95
+//   128 x 256: eight waves of 64 x 64; 32 x 128 for RoPE over
+//              128-wide heads.                                  speed 0.72
+// RoPE needs both halves of a head in one wave's columns, so 128-wide heads
+// exclude the 64-column waves of the 288-row shape.  Every shape uses the
+// same K slicing and lane/k assignment, so a cell's result does not depend on
+// the choice.
+int num_cus() {
+  static const int n = [] {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+      v = 256;
+    return v;
+  }();
+  return n;
+}
+
+double tile_cost(const GemmArgs& a, int G, int bm, double speed) {
+  const long tiles = (long)((a.M + bm - 1) / bm) * ((a.N + BN - 1) / BN) * G;
+  const long rounds = (tiles + num_cus() - 1) / num_cus();
+  return (double)rounds * bm / speed;
+}
+
 template <int EPI>
 void launch_epi(const GemmArgs& a, const GroupTable& tab, hipStream_t stream) {
-  const int tiles256 = ((a.M + 255) / 256) * ((a.N + BN - 1) / BN) * tab.G;
   const bool wide_heads = EPI == EPI_QKV_ROPE && a.hd == 128;
-  if (tiles256 >= 512) {
+  const double c288 = wide_heads ? 1e300 : tile_cost(a, tab.G, 288, 1.00);
+  const double c256 = tile_cost(a, tab.G, 256, 0.95);
+  const double c128 = tile_cost(a, tab.G, 128, 0.72);
+  if (c288 <= c256 && c288 <= c128) {
+    launch_one<EPI, 288, 96, 64>(a, tab, stream);
+  } else if (c256 <= c128) {
     launch_one<EPI, 256, 64, 128>(a, tab, stream);
   } else if (wide_heads) {
     launch_one<EPI, 128, 32, 128>(a, tab, stream);
