@@ -29,6 +29,8 @@
 //     which diagonal (or the sequential sweep) it runs in.
 #include "kernels.h"
 
+#include <type_traits>
+
 namespace rmt {
 namespace {
 
@@ -227,105 +229,47 @@ __global__ __launch_bounds__((BM / WTM) * (BN / WTN) * 64, 1) void gemm_bf16_ker
     if (wave_live) compute(kt % STAGES);
   }
 
+  // ---- Epilogue ----
   // Accumulator layout (C^T blocks): element e of lane l of block (i, t) is
-  // row i*32 + l%32, column t*32 + 8*(e/4) + 4*(l/32) + e%4 -- four
-  // consecutive columns for each e/4.
-  const int row0 = tm * BM + wm * WTM + r32;
-  const int col0 = tn * BN + wn * WTN + 4 * (lane >> 5);
+  // row i*32 + l%32, column t*32 + 8*(e/4) + 4*(l/32) + e%4.  A wave-wide
+  // access straight from that layout touches 32 rows at 16-32 bytes each, so
+  // the bf16 epilogues send every 32 x 64 piece (two 32-column blocks)
+  // through a private LDS region of the wave and read it back row-major, so
+  // their stores cover whole row segments.  RoPE and SwiGLU pair their two
+  // blocks inside one piece.
+  if constexpr (EPI != EPI_RESID_F32) {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();      // the ring is free once every wave is past its last slice
+    asm volatile("" ::: "memory");
+  }
+  constexpr int EP_LD = 68;            // floats per staged row: 64 + 4 of padding
+  static_assert(NWAVES * 32 * EP_LD * 4 <= STAGES * STAGE_BYTES, "epilogue staging fits the ring");
+  static_assert(NI % 2 == 0, "pieces are pairs of 32-column blocks");
+  float* ep = (float*)smem + wave * 32 * EP_LD;
+  const int wrow0 = tm * BM + wm * WTM;        // first row of the wave's sub-tile
+  const int wcol0 = tn * BN + wn * WTN;        // first column of the wave's sub-tile
+  const int half_lane = 4 * (lane >> 5);
 
-  if constexpr (EPI == EPI_STORE_BF16) {
-    uint16_t* C = (uint16_t*)tab.out_lo[g];
+  // Wave-local LDS hand-off: all of this wave's LDS accesses issued so far
+  // have completed, and the compiler keeps later ones after this point.
+  auto lds_sync = [&]() __attribute__((always_inline)) {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  };
+  // Block (i, t) of the accumulator -> columns [32 slot, 32 slot + 32) of the piece.
+  auto stage = [&](const f32x16& blk, int slot) __attribute__((always_inline)) {
+#pragma unroll
+    for (int e4 = 0; e4 < 4; ++e4)
+      *(f32x4*)(ep + r32 * EP_LD + slot * 32 + 8 * e4 + half_lane) =
+          f32x4{blk[4 * e4], blk[4 * e4 + 1], blk[4 * e4 + 2], blk[4 * e4 + 3]};
+  };
+
+  if constexpr (EPI == EPI_RESID_F32) {
+    // Straight from the accumulator layout: every residual load of the tile
+    // can be in flight at once, which outweighs the wider accesses staging
+    // would give this read-modify-write.
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
-      const int row = row0 + i * 32;
-      if (row >= a.M) continue;
-#pragma unroll
-      for (int t = 0; t < NI; ++t)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int col = col0 + t * 32 + 8 * q;
-          if (col >= a.N) continue;
-          *(u32x2*)(C + (size_t)row * a.ld_out + col) =
-              u32x2{pack_bf16(acc[i][t][4 * q], acc[i][t][4 * q + 1]),
-                    pack_bf16(acc[i][t][4 * q + 2], acc[i][t][4 * q + 3])};
-        }
-    }
-  } else if constexpr (EPI == EPI_QKV_ROPE) {
-    // The wave's WTN columns start on a head boundary (WTN is a multiple of
-    // hd), so column c < hd/2 of a head and its partner c + hd/2 sit in the
-    // same lane, in blocks t and t + hd/64.
-    uint16_t* C = (uint16_t*)tab.out_lo[g];
-    const int P = a.hd >> 6;
-    const int half = a.hd >> 1;
-#pragma unroll
-    for (int t = 0; t < NI; ++t) {
-      if (((t / P) & 1) != 0) continue;
-      const int tp = t + P;
-#pragma unroll
-      for (int i = 0; i < MI; ++i) {
-        const int row = row0 + i * 32;
-        if (row >= a.M) continue;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int col = col0 + t * 32 + 8 * q;
-          if (col >= a.N) continue;
-          float x1[4], x2[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            x1[e] = acc[i][t][4 * q + e];
-            x2[e] = 0.f;
-#pragma unroll
-            for (int u = 0; u < NI; ++u)
-              if (u == tp) x2[e] = acc[i][u][4 * q + e];
-          }
-          if (col < a.rope_cols) {
-            const float2* cs = a.rope + (size_t)row * half + col % a.hd;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const float2 c = cs[e];
-              const float y1 = x1[e] * c.x - x2[e] * c.y;
-              const float y2 = x2[e] * c.x + x1[e] * c.y;
-              x1[e] = y1;
-              x2[e] = y2;
-            }
-          }
-          uint16_t* dst = C + (size_t)row * a.ld_out + col;
-          *(u32x2*)dst = u32x2{pack_bf16(x1[0], x1[1]), pack_bf16(x1[2], x1[3])};
-          *(u32x2*)(dst + half) = u32x2{pack_bf16(x2[0], x2[1]), pack_bf16(x2[2], x2[3])};
-        }
-      }
-    }
-  } else if constexpr (EPI == EPI_SWIGLU) {
-    // Packed columns come in 64-wide blocks: 32 gate columns then the 32 up
-    // columns of the same outputs; output column = block * 32 + offset.
-    uint16_t* U = (uint16_t*)tab.out_lo[g];
-#pragma unroll
-    for (int t = 0; t < NI; t += 2) {
-#pragma unroll
-      for (int i = 0; i < MI; ++i) {
-        const int row = row0 + i * 32;
-        if (row >= a.M) continue;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int col = col0 + t * 32 + 8 * q;
-          if (col >= a.N) continue;
-          const int ocol = (col >> 6) * 32 + (col & 31);
-          float u[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float gt = acc[i][t][4 * q + e];
-            const float up = acc[i][t + 1][4 * q + e];
-            u[e] = gt / (1.0f + __expf(-gt)) * up;
-          }
-          *(u32x2*)(U + (size_t)row * a.ld_out + ocol) =
-              u32x2{pack_bf16(u[0], u[1]), pack_bf16(u[2], u[3])};
-        }
-      }
-    }
-  } else {  // EPI_RESID_F32
-#pragma unroll
-    for (int i = 0; i < MI; ++i) {
-      const int row = row0 + i * 32;
+      const int row = wrow0 + i * 32 + r32;
       if (row >= a.M) continue;
       const float* res = row < a.split_in
                              ? (const float*)tab.in_lo[g] + (size_t)row * a.ld_res
@@ -337,7 +281,7 @@ __global__ __launch_bounds__((BM / WTM) * (BN / WTN) * 64, 1) void gemm_bf16_ker
       for (int t = 0; t < NI; ++t)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int col = col0 + t * 32 + 8 * q;
+          const int col = wcol0 + t * 32 + 8 * q + half_lane;
           if (col >= a.N) continue;
           f32x4 r = *(const f32x4*)(res + col);
           r[0] += acc[i][t][4 * q + 0];
@@ -346,6 +290,105 @@ __global__ __launch_bounds__((BM / WTM) * (BN / WTN) * 64, 1) void gemm_bf16_ker
           r[3] += acc[i][t][4 * q + 3];
           *(f32x4*)(out + col) = r;
         }
+    }
+  } else if constexpr (EPI == EPI_STORE_BF16) {
+    // Row-major read-back: 16 lanes per 64-column row, 4 rows per access.
+    const int lr = lane >> 4;
+    const int lc = 4 * (lane & 15);
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int t = 0; t < NI; t += 2) {
+        stage(acc[i][t], 0);
+        stage(acc[i][t + 1], 1);
+        lds_sync();
+        const int col = wcol0 + t * 32 + lc;
+        uint16_t* C = (uint16_t*)tab.out_lo[g];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int r = 4 * j + lr;
+          const int row = wrow0 + i * 32 + r;
+          const f32x4 v = *(const f32x4*)(ep + r * EP_LD + lc);
+          if (row >= a.M || col >= a.N) continue;
+          *(u32x2*)(C + (size_t)row * a.ld_out + col) = u32x2{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
+        }
+        lds_sync();
+      }
+  } else {
+    // Paired read-back: 8 lanes per row, each with 4 columns of the first
+    // block and the same 4 columns of the second; 8 rows per access.
+    const int lr = lane >> 3;
+    const int lc = 4 * (lane & 7);
+    auto paired = [&](int i, int t, int t2) __attribute__((always_inline)) {
+      lds_sync();
+      const int col = wcol0 + t * 32 + lc;     // column of the first block's values
+      const int col2 = wcol0 + t2 * 32 + lc;   // column of the second block's values
+      uint16_t* C = (uint16_t*)tab.out_lo[g];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = 8 * j + lr;
+        const int row = wrow0 + i * 32 + r;
+        f32x4 x1 = *(const f32x4*)(ep + r * EP_LD + lc);
+        f32x4 x2 = *(const f32x4*)(ep + r * EP_LD + 32 + lc);
+        if (row >= a.M || col >= a.N) continue;
+        if constexpr (EPI == EPI_SWIGLU) {
+          // 64-column packed blocks: 32 gate columns then the 32 up columns
+          // of the same outputs; output column = block * 32 + offset.
+          const int ocol = (col >> 6) * 32 + (col & 31);
+          float u[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) u[e] = x1[e] / (1.0f + __expf(-x1[e])) * x2[e];
+          *(u32x2*)(C + (size_t)row * a.ld_out + ocol) =
+              u32x2{pack_bf16(u[0], u[1]), pack_bf16(u[2], u[3])};
+        } else {
+          // RoPE, rotate-half: column c < hd/2 of a head pairs with c + hd/2.
+          if (col < a.rope_cols) {
+            const float2* cs = a.rope + (size_t)row * (a.hd >> 1) + col % a.hd;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float2 c = cs[e];
+              const float y1 = x1[e] * c.x - x2[e] * c.y;
+              const float y2 = x2[e] * c.x + x1[e] * c.y;
+              x1[e] = y1;
+              x2[e] = y2;
+            }
+          }
+          *(u32x2*)(C + (size_t)row * a.ld_out + col) = u32x2{pack_bf16(x1[0], x1[1]), pack_bf16(x1[2], x1[3])};
+          *(u32x2*)(C + (size_t)row * a.ld_out + col2) = u32x2{pack_bf16(x2[0], x2[1]), pack_bf16(x2[2], x2[3])};
+        }
+      }
+      lds_sync();
+    };
+    if constexpr (EPI == EPI_SWIGLU) {
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int t = 0; t < NI; t += 2) {
+          stage(acc[i][t], 0);
+          stage(acc[i][t + 1], 1);
+          paired(i, t, t + 1);
+        }
+    } else {  // EPI_QKV_ROPE: the wave's columns start on a head boundary
+      // (WTN is a multiple of hd), so block t pairs with t + P, P = hd / 64.
+      auto rope_pieces = [&](auto pc) __attribute__((always_inline)) {
+        constexpr int P = decltype(pc)::value;
+        static_assert(NI % (2 * P) == 0, "heads must not straddle a wave's columns");
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+          for (int t = 0; t < NI; ++t) {
+            if ((t / P) % 2 != 0) continue;
+            stage(acc[i][t], 0);
+            stage(acc[i][t + P], 1);
+            paired(i, t, t + P);
+          }
+      };
+      if constexpr (WTN >= 128) {
+        if (a.hd == 128) rope_pieces(std::integral_constant<int, 2>{});
+        else rope_pieces(std::integral_constant<int, 1>{});
+      } else {
+        rope_pieces(std::integral_constant<int, 1>{});
+      }
     }
   }
 }
