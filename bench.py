@@ -13,6 +13,13 @@ bf16 dense MFMA peak, the isolated 1152 x 2048 x 8192 grouped GEMM at
 G = 1, 4, 8, 16, and the CPU oracle timed on a prefix of the sequence.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu] [--no-seq]
+                    [--workload llama1b|llama8b|norm_swiglu_1b]
+
+The default workload is the 1B-shaped one above; --workload selects the
+8B-shaped RMT (32 layers, d = 4096, segments of 2048 + 128 rows, 64 segments,
+131,072 tokens) or the attention-free 1B-width stack (32 segments, 32,768
+tokens) instead.  Every GPU stage is also split into full diagonals (all
+min(L, S) cells active) and ramp diagonals.
 """
 from __future__ import annotations
 
@@ -30,6 +37,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 METRIC = "tokens/s for one 131K-token sequence; grouped-GEMM % of bf16 MFMA peak"
+WORKLOADS = {"llama1b": "LLAMA_1B", "llama8b": "LLAMA_8B", "norm_swiglu_1b": "NORM_SWIGLU_1B"}
 
 
 def log(msg):
@@ -134,6 +142,7 @@ def main():
     ap.add_argument("--no-seq", action="store_true", help="skip the sequential path")
     ap.add_argument("--no-sweep", action="store_true", help="skip the isolated grouped-GEMM sweep")
     ap.add_argument("--cpu-segments", type=int, default=2)
+    ap.add_argument("--workload", default="llama1b", choices=sorted(WORKLOADS))
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy, the reference for HBM byte counters")
     args = ap.parse_args()
@@ -147,17 +156,18 @@ def main():
     import rmt_inputs as ri
     from rmt_inputs import device as rdev
 
-    cfg = ri.LLAMA_1B
+    cfg = getattr(ri, WORKLOADS[args.workload])
+    llama = cfg.cell == ri.CELL_LLAMA
     torch.cuda.set_device(0)
     t0 = time.perf_counter()
     layers = gen_layers(cfg)
-    embed = ri.embedding(cfg)
-    tokens = ri.tokens(cfg)
+    embed = ri.embedding(cfg) if llama else None
+    tokens = ri.tokens(cfg) if llama else ri.input_embeddings(cfg)
     mem0 = ri.initial_memory(cfg)
-    log(f"[bench] inputs generated in {time.perf_counter() - t0:.1f} s")
+    log(f"[bench] {cfg.name}: inputs generated in {time.perf_counter() - t0:.1f} s")
     dw = rdev.device_weights(cfg, layers, embed)
     model = rmt.RMTModel(**rdev.model_kwargs(cfg), weights=dw)
-    emb_dev = dw["embed"]
+    emb_dev = dw.get("embed")
     del dw
     tok_d = rdev.segment_inputs(cfg, tokens)
     mem0_d = rdev.f32_tensor(mem0)
@@ -173,39 +183,58 @@ def main():
     torch.cuda.synchronize()
     log("[bench] warmup done")
 
-    # timed region: per-launch HIP events on the library's stream
-    model.enable_timing(True)
+    # timed region: the forward pass alone
     wall, gpu_s = timed_steps(diag, args.steps, stream)
+    log(f"[bench] diagonal: {wall / args.steps * 1e3:.1f} ms/step wall")
+    # the same steps again with per-launch HIP events on the library's stream
+    model.enable_timing(True)
+    wall_ev, _ = timed_steps(diag, args.steps, stream)
+    g_full = min(cfg.L, cfg.S)
+    full = model.stage_times(groups=(g_full, g_full))
+    ramp = model.stage_times(groups=(1, g_full - 1))
     stages = model.stage_times()
     model.enable_timing(False)
-    log(f"[bench] diagonal: {wall / args.steps * 1e3:.1f} ms/step wall")
-    # the same region without the per-launch events
-    wall_ne, _ = timed_steps(diag, args.steps, stream)
     hidden_np = hidden.cpu().numpy()
 
     ms_step = wall / args.steps * 1e3
     tok_s = T * args.steps / wall
 
+    def rates(v):
+        e = {"ms_per_step": round(v["ms"] / args.steps, 3), "launches_per_step": v["launches"] // args.steps}
+        if v["ms"] > 0 and v["flops"] > 0:
+            e["tflops"] = round(v["flops"] / (v["ms"] / 1e3) / 1e12, 1)
+            e["frac_bf16_peak"] = round(e["tflops"] / PEAK_BF16_TFLOPS, 4)
+        if v["ms"] > 0 and v["bytes"] > 0:
+            e["gbs"] = round(v["bytes"] / (v["ms"] / 1e3) / 1e9, 1)
+            e["frac_hbm_peak"] = round(e["gbs"] / PEAK_HBM_GBS, 4)
+        return e
+
     st_out = {}
-    gemm_flops = gemm_ms = 0.0
+    gemm = {k: {"ms": 0.0, "flops": 0.0, "launches": 0, "bytes": 0.0} for k in ("all", "full", "ramp")}
     for name, v in stages.items():
         if v["launches"] == 0:
             continue
-        ms = v["ms"] / args.steps
-        e = {"ms_per_step": round(ms, 3), "launches_per_step": v["launches"] // args.steps}
-        if v["flops"] > 0:
-            e["tflops"] = round(v["flops"] / (v["ms"] / 1e3) / 1e12, 1)
-            e["frac_bf16_peak"] = round(e["tflops"] / PEAK_BF16_TFLOPS, 4)
-        if v["bytes"] > 0:
-            e["gbs"] = round(v["bytes"] / (v["ms"] / 1e3) / 1e9, 1)
-            e["frac_hbm_peak"] = round(e["gbs"] / PEAK_HBM_GBS, 4)
+        e = rates(v)
+        if full[name]["launches"]:
+            e["full_diagonals"] = rates(full[name])
+        if ramp[name]["launches"]:
+            e["ramp_diagonals"] = rates(ramp[name])
         st_out[name] = e
         if name in ("qkv", "oproj", "gateup", "down"):
-            gemm_flops += v["flops"]
-            gemm_ms += v["ms"]
-    gemm_tf = gemm_flops / (gemm_ms / 1e3) / 1e12 if gemm_ms else 0.0
+            for key, src in (("all", v), ("full", full[name]), ("ramp", ramp[name])):
+                for f in ("ms", "flops", "launches"):
+                    gemm[key][f] += src[f]
+    gemm_out = {}
+    for key, v in gemm.items():
+        if v["ms"] > 0:
+            tf = v["flops"] / (v["ms"] / 1e3) / 1e12
+            gemm_out[key if key != "all" else "all_diagonals"] = {
+                "tflops": round(tf, 1), "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+    gemm_out["full_diagonals"] = gemm_out.pop("full", None)
+    gemm_out["ramp_diagonals"] = gemm_out.pop("ramp", None)
 
-    traffic = measured_traffic()
+    # the committed counter summary covers the 1B-shaped workload only
+    traffic = measured_traffic() if args.workload == "llama1b" else None
     gu = stages["gateup"]
     achieved = gu["flops"] / gu["launches"] / (gu["ms"] / 1e3 / gu["launches"]) / 1e12
     roofline = {"kernel": "grouped GEMM, gate/up stage + SwiGLU epilogue (gemm_bf16_kernel<2>)",
@@ -214,19 +243,24 @@ def main():
                 "avg_launch_us": round(gu["ms"] / gu["launches"] * 1e3, 2),
                 "flops_per_launch": gu["flops"] / gu["launches"]}
 
+    config = {"workload": cfg.name, "layers": cfg.L, "segments": cfg.S, "segment_tokens": cfg.n,
+              "memory_rows": cfg.m, "width": cfg.d}
+    if llama:
+        config.update({"heads": cfg.Hq, "kv_heads": cfg.Hkv, "head_dim": cfg.hd})
+    config.update({"ffn": cfg.F, "tokens": T, "path": "rmt_forward_diagonal"})
+    if llama:
+        config["vocab"] = cfg.V
+    data = ("synthetic (seeded random weights, token ids uniform over the vocabulary)" if llama
+            else "synthetic (seeded random weights and input embeddings)")
     result = {
         "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 2),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-        "data": "synthetic (seeded random weights, token ids uniform over the vocabulary)",
-        "config": {"workload": cfg.name, "layers": cfg.L, "segments": cfg.S, "segment_tokens": cfg.n,
-                   "memory_rows": cfg.m, "width": cfg.d, "heads": cfg.Hq, "kv_heads": cfg.Hkv,
-                   "head_dim": cfg.hd, "ffn": cfg.F, "vocab": cfg.V, "tokens": T,
-                   "path": "rmt_forward_diagonal"},
+        "data": data,
+        "config": config,
         "roofline": roofline,
-        "grouped_gemm_stages": {"tflops": round(gemm_tf, 1),
-                                "frac_bf16_peak": round(gemm_tf / PEAK_BF16_TFLOPS, 4)},
-        "ms_per_step_without_stage_events": round(wall_ne / args.steps * 1e3, 2),
+        "grouped_gemm_stages": gemm_out,
+        "ms_per_step_with_stage_events": round(wall_ev / args.steps * 1e3, 2),
         "stages": st_out,
     }
 

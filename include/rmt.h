@@ -194,6 +194,16 @@ int32_t rmt_model_enable_timing(rmt_model* model, int32_t enable);
 int32_t rmt_model_stage_times(rmt_model* model, double* ms, int64_t* launches, double* flops,
                               double* bytes);
 
+/* The same per-stage totals restricted to the launches that covered between
+ * g_lo and g_hi cells (inclusive) -- e.g. g_lo = g_hi = min(L, S) selects the
+ * full diagonals, 1 .. min(L, S) - 1 the ramps of the "Diagonal
+ * Reorganization" sweep in the Architecture Overview of the skill page.  The
+ * one-off copy of mem0 counts as 0 cells.  Synchronises the stream; does not
+ * clear the totals (call rmt_model_stage_times for that).  Errors: RMT_EINVAL
+ * (NULL model, g_lo > g_hi), RMT_EHIP. */
+int32_t rmt_model_stage_times_groups(rmt_model* model, int32_t g_lo, int32_t g_hi, double* ms,
+                                     int64_t* launches, double* flops, double* bytes);
+
 /* Release the model's device memory (the caller's stream is synchronised
  * first).  NULL is accepted. */
 int32_t rmt_model_destroy(rmt_model* model);

@@ -138,13 +138,20 @@ class RMTModel:
     def enable_timing(self, on: bool = True) -> None:
         check(lib().rmt_model_enable_timing(self._handle, 1 if on else 0))
 
-    def stage_times(self) -> Dict[str, dict]:
+    def stage_times(self, groups=None) -> Dict[str, dict]:
+        """Per-stage totals of the timed launches since timing was enabled.
+        With groups=(lo, hi), only launches that covered lo..hi cells, and the
+        totals are kept; without, all launches, and the totals are cleared."""
         n = len(STAGES)
         ms = (C.c_double * n)()
         nl = (C.c_int64 * n)()
         fl = (C.c_double * n)()
         by = (C.c_double * n)()
-        check(lib().rmt_model_stage_times(self._handle, ms, nl, fl, by))
+        if groups is None:
+            check(lib().rmt_model_stage_times(self._handle, ms, nl, fl, by))
+        else:
+            lo, hi = groups
+            check(lib().rmt_model_stage_times_groups(self._handle, int(lo), int(hi), ms, nl, fl, by))
         return {name: {"ms": ms[i], "launches": nl[i], "flops": fl[i], "bytes": by[i]}
                 for i, name in enumerate(STAGES)}
 

@@ -61,6 +61,8 @@ SIGNATURES = {
     "rmt_model_check": (C.c_int32, [C.c_void_p, C.POINTER(C.c_int32)]),
     "rmt_model_enable_timing": (C.c_int32, [C.c_void_p, C.c_int32]),
     "rmt_model_stage_times": (C.c_int32, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p]),
+    "rmt_model_stage_times_groups": (C.c_int32, [C.c_void_p, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p,
+                                                 C.c_void_p, C.c_void_p]),
     "rmt_model_destroy": (C.c_int32, [C.c_void_p]),
     "rmt_pack_weight": (C.c_int32, [C.c_int32, C.c_int32, C.c_int32, C.c_void_p, C.c_int32,
                                     C.c_void_p, C.c_void_p]),

@@ -93,6 +93,8 @@ struct rmt_model {
   size_t ev_used = 0;
   std::vector<int> ev_stage;        // stage of the launch that ends at event i (-1: start marker)
   std::vector<double> ev_flops, ev_bytes;
+  std::vector<int> ev_groups;       // cells covered by that launch (0: not a per-diagonal launch)
+  int cur_groups = 0;               // cells of the launches being queued
 };
 
 namespace {
@@ -152,6 +154,7 @@ int32_t mark(rmt_model* M, int stage, double flops, double bytes) {
   M->ev_stage.push_back(stage);
   M->ev_flops.push_back(flops);
   M->ev_bytes.push_back(bytes);
+  M->ev_groups.push_back(M->cur_groups);
   return RMT_OK;
 }
 
@@ -183,6 +186,7 @@ int32_t run_cells(rmt_model* M, const Cell* cells, int G, const void* tokens, co
   auto slot = [&](float* buf, int l) { return buf + (size_t)l * n * d; };
   auto mem_buf = [&](int s) { return ((S - 1 - s) % 2 == 0) ? out->mem : M->memw; };
   const double G_ = G;
+  M->cur_groups = G;
 
   // Cell inputs [M(l, s-1); X(l-1, s)] and outputs X(l, s), M(l, s).
   const void* in_lo[kMaxGroups];
@@ -312,6 +316,7 @@ int32_t start_forward(rmt_model* M, const void* mem0, const rmt_output* out) {
   const size_t mem_bytes = (size_t)c.L * c.m * c.d * sizeof(float);
   // M(l, -1) lives in the buffer that segment -1 maps to (see the header).
   float* dst = ((c.S - 1 - (-1)) % 2 == 0) ? out->mem : M->memw;
+  M->cur_groups = 0;
   MARK(-1, 0.0, 0.0);
   if ((const void*)dst != mem0) {
     HIP_TRY(hipMemcpyAsync(dst, mem0, mem_bytes, hipMemcpyDeviceToDevice, M->stream));
@@ -537,18 +542,22 @@ int32_t rmt_model_enable_timing(rmt_model* M, int32_t enable) {
   M->ev_stage.clear();
   M->ev_flops.clear();
   M->ev_bytes.clear();
+  M->ev_groups.clear();
   return RMT_OK;
 }
 
-int32_t rmt_model_stage_times(rmt_model* M, double* ms, int64_t* launches, double* flops,
-                              double* bytes) {
-  if (!M) return fail(RMT_EINVAL, "model is NULL");
+namespace {
+
+// Per-stage sums over the recorded launches that covered g_lo..g_hi cells.
+int32_t sum_stage_times(rmt_model* M, int g_lo, int g_hi, double* ms, int64_t* launches,
+                        double* flops, double* bytes) {
   HIP_TRY(hipStreamSynchronize(M->stream));
   double t[RMT_NUM_STAGES] = {0}, f[RMT_NUM_STAGES] = {0}, b[RMT_NUM_STAGES] = {0};
   int64_t nl[RMT_NUM_STAGES] = {0};
   for (size_t i = 1; i < M->ev_used; ++i) {
     const int st = M->ev_stage[i];
     if (st < 0) continue;   // start marker of the next forward call
+    if (M->ev_groups[i] < g_lo || M->ev_groups[i] > g_hi) continue;
     float dt = 0.f;
     HIP_TRY(hipEventElapsedTime(&dt, M->events[i - 1], M->events[i]));
     t[st] += dt;
@@ -562,11 +571,29 @@ int32_t rmt_model_stage_times(rmt_model* M, double* ms, int64_t* launches, doubl
     if (flops) flops[i] = f[i];
     if (bytes) bytes[i] = b[i];
   }
+  return RMT_OK;
+}
+
+}  // namespace
+
+int32_t rmt_model_stage_times(rmt_model* M, double* ms, int64_t* launches, double* flops,
+                              double* bytes) {
+  if (!M) return fail(RMT_EINVAL, "model is NULL");
+  const int32_t rc = sum_stage_times(M, INT32_MIN, INT32_MAX, ms, launches, flops, bytes);
+  if (rc != RMT_OK) return rc;
   M->ev_used = 0;
   M->ev_stage.clear();
   M->ev_flops.clear();
   M->ev_bytes.clear();
+  M->ev_groups.clear();
   return RMT_OK;
+}
+
+int32_t rmt_model_stage_times_groups(rmt_model* M, int32_t g_lo, int32_t g_hi, double* ms,
+                                     int64_t* launches, double* flops, double* bytes) {
+  if (!M) return fail(RMT_EINVAL, "model is NULL");
+  if (g_lo > g_hi) return fail(RMT_EINVAL, "g_lo (%d) > g_hi (%d)", g_lo, g_hi);
+  return sum_stage_times(M, g_lo, g_hi, ms, launches, flops, bytes);
 }
 
 int32_t rmt_model_destroy(rmt_model* M) {
