@@ -16,7 +16,12 @@
 // through the transposing LDS read ds_read_b64_tr_b16.  The softmax is
 // online in fp32 and base 2 (one FMA + one v_exp_f32 per score); the running
 // output is rescaled only when a row maximum grows by more than 2^8, which
-// keeps every probability below 256 and leaves O / l unchanged.
+// keeps every probability below 256 and leaves O / l unchanged.  The VALU,
+// not the MFMA, bounds this kernel at head_dim 64 (v_exp_f32 issues at a
+// quarter of the FMA rate), so the row sums l come from one more MFMA per
+// step against a row of ones -- the sum of exactly the bf16 probabilities
+// that multiply V -- and the row maxima cross lane groups with
+// v_permlane16/32_swap instead of LDS permutes.
 #include "kernels.h"
 
 namespace rmt {
@@ -37,6 +42,15 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   v[0] = (__bf16)lo;              // v_cvt_pk_bf16_f32: round to nearest even
   v[1] = (__bf16)hi;
   return __builtin_bit_cast(uint32_t, v);
+}
+
+// Maximum over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (the four lane groups
+// that hold one query column), with the gfx950 cross-row lane swaps.
+__device__ __forceinline__ float max_over_groups(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
 template <int HD, int QB>
@@ -89,12 +103,19 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const uint16_t* __res
   for (int ht = 0; ht < HT; ++ht)
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) o[ht][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float mref[QT], lrow[QT];       // mref: reference maximum in the scaled (log2) domain
+  // mref: reference maximum in the scaled (log2) domain.  osum: row sums of
+  // the bf16 probabilities, from one more MFMA per step whose A operand has a
+  // row of ones (row 0, i.e. lanes c16 == 0): element 0 of lane c16 < 16
+  // holds the sum for query 16 qt + c16, and the rescaling treats it like O.
+  float mref[QT];
+  f32x4 osum[QT];
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
     mref[qt] = -INFINITY;
-    lrow[qt] = 0.f;
+    osum[qt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
+  const uint32_t one2 = c16 == 0 ? 0x3F803F80u : 0u;   // two bf16 ones, or zeros
+  const bf16x8 ones_row = __builtin_bit_cast(bf16x8, u32x4{one2, one2, one2, one2});
 
   // K/V block loads: thread chunk c -> key c / CH, columns (c % CH) * 8.
   u32x4 rk[LOADS], rv[LOADS];
@@ -174,11 +195,11 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const uint16_t* __res
     for (int qt = 0; qt < QT; ++qt) {
       float mx = -INFINITY;
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-        mx = fmaxf(mx, fmaxf(fmaxf(s[kt][qt][0], s[kt][qt][1]), fmaxf(s[kt][qt][2], s[kt][qt][3])));
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      mnew[qt] = mx * scale_log2;
+      for (int kt = 0; kt < 4; ++kt) {   // three-input maxima (v_max3_f32)
+        mx = fmaxf(fmaxf(mx, s[kt][qt][0]), s[kt][qt][1]);
+        mx = fmaxf(fmaxf(mx, s[kt][qt][2]), s[kt][qt][3]);
+      }
+      mnew[qt] = max_over_groups(mx) * scale_log2;
       need_rescale |= mnew[qt] > mref[qt] + RESCALE_LOG2;
     }
     if (__any(need_rescale)) {
@@ -187,26 +208,18 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const uint16_t* __res
         const float m2 = fmaxf(mref[qt], mnew[qt]);
         const float corr = __builtin_amdgcn_exp2f(mref[qt] - m2);   // 0 on the first block
         mref[qt] = m2;
-        lrow[qt] *= corr;
+        osum[qt] *= corr;
 #pragma unroll
         for (int ht = 0; ht < HT; ++ht) o[ht][qt] *= corr;
       }
     }
 #pragma unroll
-    for (int qt = 0; qt < QT; ++qt) {
-      float sum = 0.f;
+    for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(s[kt][qt][j], scale_log2, -mref[qt]));
-          s[kt][qt][j] = p;
-          sum += p;
-        }
-      sum += __shfl_xor(sum, 16);
-      sum += __shfl_xor(sum, 32);
-      lrow[qt] += sum;
-    }
+        for (int j = 0; j < 4; ++j)
+          s[kt][qt][j] = __builtin_amdgcn_exp2f(fmaf(s[kt][qt][j], scale_log2, -mref[qt]));
 
     // O^T += V^T P^T over two 32-key steps.  In step ks2, operand slot e < 4
     // is key 32 ks2 + 4 g4 + e and slot e >= 4 is key 32 ks2 + 16 + 4 g4 +
@@ -227,6 +240,7 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const uint16_t* __res
         w[2] = pack_bf16(s[2 * ks2 + 1][qt][0], s[2 * ks2 + 1][qt][1]);
         w[3] = pack_bf16(s[2 * ks2 + 1][qt][2], s[2 * ks2 + 1][qt][3]);
         pf[qt] = __builtin_bit_cast(bf16x8, w);
+        osum[qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones_row, pf[qt], osum[qt], 0, 0, 0);
       }
 #pragma unroll
       for (int ht = 0; ht < HT; ++ht) {
@@ -257,8 +271,9 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const uint16_t* __res
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
     const int q = q0 + 16 * qt + c16;
+    const float lsum = __shfl(osum[qt][0], c16);   // from lane c16 (lane group 0)
     if (q >= R) continue;
-    const float inv = 1.0f / lrow[qt];
+    const float inv = 1.0f / lsum;
     uint16_t* orow = out + ((size_t)g * R + q) * (size_t)(Hq * HD) + (size_t)h * HD;
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
