@@ -40,35 +40,40 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(int total_rows, int R, int
                                   : (const float*)tab.in_hi[g] + (size_t)(r - split_in) * d;
   const float* gm = gamma + (size_t)tab.layer[g] * d;
   uint16_t* dst = out + (size_t)row * d;
-  f32x4 v[VPL];
+  f32x4 v[VPL], w[VPL];
   float ss = 0.f;
+  // the row and its gamma are requested together, so the gamma latency
+  // overlaps the row's instead of following the reduction
 #pragma unroll
   for (int j = 0; j < VPL; ++j) {
     const int c = (lane + 64 * j) * 4;
     v[j] = c < d ? *(const f32x4*)(src + c) : f32x4{0.f, 0.f, 0.f, 0.f};
-    ss += v[j][0] * v[j][0] + v[j][1] * v[j][1] + v[j][2] * v[j][2] + v[j][3] * v[j][3];
+    w[j] = c < d ? *(const f32x4*)(gm + c) : f32x4{0.f, 0.f, 0.f, 0.f};
   }
+#pragma unroll
+  for (int j = 0; j < VPL; ++j)
+    ss += v[j][0] * v[j][0] + v[j][1] * v[j][1] + v[j][2] * v[j][2] + v[j][3] * v[j][3];
   for (int c = (lane + 64 * VPL) * 4; c < d; c += 256) {
     const f32x4 x = *(const f32x4*)(src + c);
     ss += x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3];
   }
   ss = wave_sum(ss);
   const float inv = 1.0f / sqrtf(ss / (float)d + eps);
-  auto emit = [&](int c, const f32x4& x) __attribute__((always_inline)) {
-    const f32x4 w = *(const f32x4*)(gm + c);
+  auto emit = [&](int c, const f32x4& x, const f32x4& gw) __attribute__((always_inline)) {
     u16x4 o;
-    o[0] = to_bf16(x[0] * inv * w[0]);
-    o[1] = to_bf16(x[1] * inv * w[1]);
-    o[2] = to_bf16(x[2] * inv * w[2]);
-    o[3] = to_bf16(x[3] * inv * w[3]);
+    o[0] = to_bf16(x[0] * inv * gw[0]);
+    o[1] = to_bf16(x[1] * inv * gw[1]);
+    o[2] = to_bf16(x[2] * inv * gw[2]);
+    o[3] = to_bf16(x[3] * inv * gw[3]);
     *(u16x4*)(dst + c) = o;
   };
 #pragma unroll
   for (int j = 0; j < VPL; ++j) {
     const int c = (lane + 64 * j) * 4;
-    if (c < d) emit(c, v[j]);
+    if (c < d) emit(c, v[j], w[j]);
   }
-  for (int c = (lane + 64 * VPL) * 4; c < d; c += 256) emit(c, *(const f32x4*)(src + c));
+  for (int c = (lane + 64 * VPL) * 4; c < d; c += 256)
+    emit(c, *(const f32x4*)(src + c), *(const f32x4*)(gm + c));
 }
 
 // Embedding lookup of one segment's n token ids into an fp32 slot.  An id
@@ -181,9 +186,14 @@ hipError_t launch_rmsnorm(int G, int R, int d, int split_in, const GroupTable& t
                           const float* gamma, float eps, uint16_t* out, hipStream_t stream) {
   const int rows = G * R;
   if (rows == 0) return hipSuccess;
-  // 16 float4 per lane keep rows of up to 4096 elements in registers
-  hipLaunchKernelGGL(rmsnorm_kernel<16>, dim3((rows + 3) / 4), dim3(256), 0, stream, rows, R, d,
-                     split_in, tab, gamma, eps, out);
+  // 8 (16) float4 per lane keep rows of up to 2048 (4096) elements in
+  // registers; the smaller variant leaves room for more waves per SIMD
+  if (d <= 2048)
+    hipLaunchKernelGGL(rmsnorm_kernel<8>, dim3((rows + 3) / 4), dim3(256), 0, stream, rows, R, d,
+                       split_in, tab, gamma, eps, out);
+  else
+    hipLaunchKernelGGL(rmsnorm_kernel<16>, dim3((rows + 3) / 4), dim3(256), 0, stream, rows, R, d,
+                       split_in, tab, gamma, eps, out);
   return hipGetLastError();
 }
 
