@@ -264,9 +264,10 @@ __global__ __launch_bounds__((BM / WTM) * (BN / WTN) * 64, 1) void gemm_bf16_ker
   };
 
   if constexpr (EPI == EPI_RESID_F32) {
-    // Straight from the accumulator layout: every residual load of the tile
-    // can be in flight at once, which outweighs the wider accesses staging
-    // would give this read-modify-write.
+    // Straight from the accumulator layout.  All residual loads of a 32-row
+    // block are issued before any of its stores: the compiler cannot prove
+    // that `out` does not alias `res`, and would otherwise wait out one full
+    // memory round trip per load.
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
       const int row = wrow0 + i * 32 + r32;
@@ -277,13 +278,21 @@ __global__ __launch_bounds__((BM / WTM) * (BN / WTN) * 64, 1) void gemm_bf16_ker
       float* out = row < a.split_out
                        ? (float*)tab.out_lo[g] + (size_t)row * a.ld_out
                        : (float*)tab.out_hi[g] + (size_t)(row - a.split_out) * a.ld_out;
+      f32x4 rv[NI][4];
+#pragma unroll
+      for (int t = 0; t < NI; ++t)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int col = wcol0 + t * 32 + 8 * q + half_lane;
+          rv[t][q] = col < a.N ? *(const f32x4*)(res + col) : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
 #pragma unroll
       for (int t = 0; t < NI; ++t)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int col = wcol0 + t * 32 + 8 * q + half_lane;
           if (col >= a.N) continue;
-          f32x4 r = *(const f32x4*)(res + col);
+          f32x4 r = rv[t][q];
           r[0] += acc[i][t][4 * q + 0];
           r[1] += acc[i][t][4 * q + 1];
           r[2] += acc[i][t][4 * q + 2];
