@@ -143,6 +143,9 @@ def main():
     ap.add_argument("--no-sweep", action="store_true", help="skip the isolated grouped-GEMM sweep")
     ap.add_argument("--cpu-segments", type=int, default=2)
     ap.add_argument("--workload", default="llama1b", choices=sorted(WORKLOADS))
+    ap.add_argument("--batch", type=int, default=1,
+                    help="B sequences through the same diagonals (rmt_model_set_batch); "
+                         "tokens/s then counts all B sequences")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy, the reference for HBM byte counters")
     args = ap.parse_args()
@@ -162,18 +165,28 @@ def main():
     t0 = time.perf_counter()
     layers = gen_layers(cfg)
     embed = ri.embedding(cfg) if llama else None
-    tokens = ri.tokens(cfg) if llama else ri.input_embeddings(cfg)
-    mem0 = ri.initial_memory(cfg)
+    B = args.batch
+    # sequence 0 uses seed 0 (the one-sequence workload); sequence b seed b
+    toks_b = [ri.tokens(cfg, b) if llama else ri.input_embeddings(cfg, b) for b in range(B)]
+    mems_b = [ri.initial_memory(cfg, b) for b in range(B)]
+    tokens, mem0 = toks_b[0], mems_b[0]
     log(f"[bench] {cfg.name}: inputs generated in {time.perf_counter() - t0:.1f} s")
     dw = rdev.device_weights(cfg, layers, embed)
     model = rmt.RMTModel(**rdev.model_kwargs(cfg), weights=dw)
     emb_dev = dw.get("embed")
     del dw
-    tok_d = rdev.segment_inputs(cfg, tokens)
-    mem0_d = rdev.f32_tensor(mem0)
+    if B == 1:
+        tok_d = rdev.segment_inputs(cfg, tokens)
+        mem0_d = rdev.f32_tensor(mem0)
+    else:
+        model.set_batch(B)
+        tok_d = torch.stack([rdev.segment_inputs(cfg, x) for x in toks_b]).contiguous()
+        mem0_d = rdev.f32_tensor(np.stack(mems_b))
+    del toks_b, mems_b
     T = cfg.T
-    hidden = torch.empty((T, cfg.d), dtype=torch.float32, device="cuda")
-    mem = torch.empty((cfg.L, cfg.m, cfg.d), dtype=torch.float32, device="cuda")
+    hidden = torch.empty((B, T, cfg.d) if B > 1 else (T, cfg.d), dtype=torch.float32, device="cuda")
+    mem = torch.empty((B, cfg.L, cfg.m, cfg.d) if B > 1 else (cfg.L, cfg.m, cfg.d),
+                      dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
     log(f"[bench] model on device: {model.device_bytes() / 2**30:.2f} GiB")
 
@@ -190,14 +203,17 @@ def main():
     model.enable_timing(True)
     wall_ev, _ = timed_steps(diag, args.steps, stream)
     g_full = min(cfg.L, cfg.S)
-    full = model.stage_times(groups=(g_full, g_full))
-    ramp = model.stage_times(groups=(1, g_full - 1))
+    if B == 1:      # with B > 1 launches mix ramp and full cells, so no split
+        full = model.stage_times(groups=(g_full, g_full))
+        ramp = model.stage_times(groups=(1, g_full - 1))
+    else:
+        full = ramp = {k: {"ms": 0.0, "launches": 0, "flops": 0.0, "bytes": 0.0} for k in rmt._lib.STAGES}
     stages = model.stage_times()
     model.enable_timing(False)
-    hidden_np = hidden.cpu().numpy()
+    hidden_np = (hidden[0] if B > 1 else hidden).cpu().numpy()
 
     ms_step = wall / args.steps * 1e3
-    tok_s = T * args.steps / wall
+    tok_s = B * T * args.steps / wall
 
     def rates(v):
         e = {"ms_per_step": round(v["ms"] / args.steps, 3), "launches_per_step": v["launches"] // args.steps}
@@ -248,6 +264,8 @@ def main():
     if llama:
         config.update({"heads": cfg.Hq, "kv_heads": cfg.Hkv, "head_dim": cfg.hd})
     config.update({"ffn": cfg.F, "tokens": T, "path": "rmt_forward_diagonal"})
+    if B > 1:
+        config["sequences"] = B
     if llama:
         config["vocab"] = cfg.V
     data = ("synthetic (seeded random weights, token ids uniform over the vocabulary)" if llama
@@ -269,7 +287,7 @@ def main():
         seq()
         torch.cuda.synchronize()
         w_s, _ = timed_steps(seq, 1, stream)
-        result["sequential"] = {"value": round(T / w_s, 1), "unit": "tokens/s",
+        result["sequential"] = {"value": round(B * T / w_s, 1), "unit": "tokens/s",
                                 "ms_per_step": round(w_s * 1e3, 2),
                                 "diagonal_speedup": round(w_s / (wall / args.steps), 3)}
         log(f"[bench] sequential: {w_s * 1e3:.1f} ms/step")
@@ -278,7 +296,9 @@ def main():
         result["grouped_gemm_sweep"] = {"workload": ri.GROUPED_GEMM_1B.name, **gemm_sweep()}
         log("[bench] grouped GEMM sweep done")
 
-    if not args.no_cpu:
+    if not args.no_cpu and B > 1:
+        log("[bench] the CPU oracle leg runs at one sequence only; skipped for --batch > 1")
+    elif not args.no_cpu:
         Sp = args.cpu_segments
 
         def gpu_mem_prefix():

@@ -104,9 +104,10 @@ typedef struct rmt_weights {
   const void* embed;
 } rmt_weights;
 
-/* Outputs of a forward call (device pointers, caller-allocated).
- *   hidden [S*n][d] fp32: X(L-1, s) for every segment, in segment order.
- *   mem    [L][m][d] fp32: M(l, S-1), the memory after the last segment;
+/* Outputs of a forward call (device pointers, caller-allocated), for each of
+ * the B sequences (B = 1 unless set by rmt_model_set_batch):
+ *   hidden [B][S*n][d] fp32: X(L-1, s) for every segment, in segment order.
+ *   mem    [B][L][m][d] fp32: M(l, S-1), the memory after the last segment;
  *          it may alias the mem0 argument (in-place state update). */
 typedef struct rmt_output {
   float* hidden;
@@ -129,9 +130,10 @@ typedef struct rmt_model rmt_model;
 int32_t rmt_diag_schedule(int32_t L, int32_t S, int32_t* diag_ptr, int32_t* cells);
 
 /* Create a model on the current HIP device: validates `cfg`, allocates the
- * packed weights and a workspace sized for min(L, S) <= L cells per diagonal
- * (independent of S), packs `w` on `stream` (a hipStream_t; NULL = default
- * stream) and waits for the packing to finish.  *out receives the handle.
+ * packed weights and a workspace for one sequence (per-launch buffers for up
+ * to min(32, L) cells, independent of S), packs `w` on `stream` (a
+ * hipStream_t; NULL = default stream) and waits for the packing to finish.
+ * *out receives the handle.
  * Errors: RMT_EINVAL (bad sizes or NULL weights the cell needs),
  * RMT_EUNSUPPORTED (Hq/Hkv not a multiple of 4, hd not 64/128, widths not
  * multiples of 64, ...), RMT_ENOMEM, RMT_EHIP. */
@@ -141,19 +143,33 @@ int32_t rmt_model_create(const rmt_config* cfg, const rmt_weights* w, void* stre
 /* Re-target the model to S segments per forward call (no allocation). */
 int32_t rmt_model_set_segments(rmt_model* model, int32_t S);
 
+/* Process B >= 1 independent sequences per forward call (default 1): the
+ * batch dimension of the skill page's Implementation sketch.  Every diagonal
+ * then covers the cells of all B sequences -- layer-major, sequence fastest,
+ * in launches of at most 32 cells -- so B sequences fill the ramp diagonals
+ * that one sequence leaves short of L cells.  The forward calls' buffers gain
+ * a leading [B]: tokens [B][S*n] (or [B][S*n][d]), mem0 and out->mem
+ * [B][L][m][d], out->hidden [B][S*n][d]; sequence b's results equal a B = 1
+ * run on its inputs, bit for bit.  Synchronises the model's stream and
+ * reallocates the workspace (hipMalloc / hipFree) when B changes.
+ * Errors: RMT_EINVAL (NULL model, B < 1, sizes too large), RMT_ENOMEM,
+ * RMT_EHIP. */
+int32_t rmt_model_set_batch(rmt_model* model, int32_t B);
+
 /* Queue later forward calls on `stream` (a hipStream_t). */
 int32_t rmt_model_set_stream(rmt_model* model, void* stream);
 
 /* Bytes of device memory the model holds (packed weights + workspace). */
 int32_t rmt_model_device_bytes(const rmt_model* model, size_t* bytes);
 
-/* Diagonal-batched forward pass over one sequence of S*n tokens.
- *   tokens  device: LLAMA -> int32 token ids [S*n] in [0, V) (ids outside
+/* Diagonal-batched forward pass over B sequences (rmt_model_set_batch;
+ * B = 1 unless set) of S*n tokens each.
+ *   tokens  device: LLAMA -> int32 token ids [B][S*n] in [0, V) (ids outside
  *           that range read a zero embedding row and set the flag reported
- *           by rmt_model_check); other cells -> input rows X(-1, .) [S*n][d]
- *           (fp32 for RMT_F32 models, bf16 for RMT_BF16 models).
- *   mem0    device fp32 [L][m][d]: M(l, -1).
- *   out     see rmt_output.
+ *           by rmt_model_check); other cells -> input rows X(-1, .)
+ *           [B][S*n][d] (fp32 for RMT_F32 models, bf16 for RMT_BF16 models).
+ *   mem0    device fp32 [B][L][m][d]: M(l, -1) of each sequence.
+ *   out     see rmt_output (hidden [B][S*n][d], mem [B][L][m][d]).
  * For every diagonal k the library launches, on the model's stream, one
  * grouped kernel per stage covering all of the diagonal's cells (skill page,
  * Architecture Overview: GroupedGEMM Operations, GPU Kernel Optimization).
@@ -161,10 +177,10 @@ int32_t rmt_model_device_bytes(const rmt_model* model, size_t* bytes);
 int32_t rmt_forward_diagonal(rmt_model* model, const void* tokens, const void* mem0,
                              rmt_output* out);
 
-/* The same computation cell by cell, segment-major (for s: for l:), one cell
- * per launch: the sequential RMT schedule the diagonal one replaces
- * (catalogue record, abstract: "sequential RMT implementation").  Same
- * arguments and results; bitwise equal to rmt_forward_diagonal. */
+/* The same computation cell by cell, segment-major (for b: for s: for l:),
+ * one cell per launch: the sequential RMT schedule that the abstract of the
+ * catalogue record compares diagonal batching against.  Same arguments and
+ * results; bitwise equal to rmt_forward_diagonal. */
 int32_t rmt_forward_sequential(rmt_model* model, const void* tokens, const void* mem0,
                                rmt_output* out);
 

@@ -110,6 +110,11 @@ class RMTModel:
         check(lib().rmt_model_set_segments(self._handle, S))
         self.cfg.S = S
 
+    def set_batch(self, B: int) -> None:
+        """B sequences per forward call: inputs and outputs gain a leading [B]."""
+        check(lib().rmt_model_set_batch(self._handle, B))
+        self.batch = B
+
     def set_stream(self, stream=None) -> None:
         check(lib().rmt_model_set_stream(self._handle, _stream(stream)))
 

@@ -19,6 +19,10 @@
 //     other, so the write-back never lands on rows another tile of the same
 //     launch still reads as its residual, and M(., S-1) ends in out->mem
 //     without a final copy.
+// With B sequences (rmt_model_set_batch) every sequence has its own X
+// ping-pong pair and memory buffers, and a diagonal's launches cover the
+// cells of all B sequences (layer-major, sequence fastest, so cells of one
+// layer sit next to each other and share weight panels in L2).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -62,8 +66,11 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 struct rmt_model {
   rmt_config cfg{};
   hipStream_t stream = nullptr;
-  void* block = nullptr;   // the single device allocation
+  void* block = nullptr;   // weights, tables, flag
   size_t bytes = 0;
+  void* ws = nullptr;      // workspace, sized for the batch
+  size_t ws_bytes = 0;
+  int batch = 1;           // sequences per forward call
 
   // packed weights (bf16, [L][N][K]) and gains (fp32)
   uint16_t* wqkv = nullptr;
@@ -77,14 +84,15 @@ struct rmt_model {
   const uint16_t* embed = nullptr;  // borrowed
   float2* rope = nullptr;  // [R][hd/2] (cos, sin)
 
-  // workspace (sized for L cells per diagonal)
-  uint16_t* abuf = nullptr;  // normalised rows, bf16 [L*R][d]
-  uint16_t* qkv = nullptr;   // [L*R][Nqkv]
-  uint16_t* att = nullptr;   // [L*R][Hq*hd]
-  float* hbuf = nullptr;     // [L*R][d]
-  uint16_t* ubuf = nullptr;  // [L*R][F]
-  float* xbuf[2] = {nullptr, nullptr};  // [L][n][d] each
-  float* memw = nullptr;     // [L][m][d]
+  // workspace: per-launch buffers for up to C = min(kMaxGroups, B*L) cells,
+  // and per-sequence X ping-pong and memory buffers
+  uint16_t* abuf = nullptr;  // normalised rows, bf16 [C*R][d]
+  uint16_t* qkv = nullptr;   // [C*R][Nqkv]
+  uint16_t* att = nullptr;   // [C*R][Hq*hd]
+  float* hbuf = nullptr;     // [C*R][d]
+  uint16_t* ubuf = nullptr;  // [C*R][F]
+  float* xbuf[2] = {nullptr, nullptr};  // [B][L][n][d] each
+  float* memw = nullptr;     // [B][L][m][d]
   int32_t* flag = nullptr;   // bad-token flag
 
   // timing
@@ -171,7 +179,7 @@ int32_t mark(rmt_model* M, int stage, double flops, double bytes) {
   } while (0)
 
 struct Cell {
-  int l, s;
+  int l, s, b;   // layer, segment, sequence
 };
 
 // Queue every stage of the cells in `cells` (all on anti-diagonal k, at most
@@ -181,10 +189,14 @@ int32_t run_cells(rmt_model* M, const Cell* cells, int G, const void* tokens, co
   const int L = c.L, S = c.S, n = c.n, m = c.m, d = c.d;
   const int R = n + m;
   const int k = cells[0].l + cells[0].s;
+  const size_t T = (size_t)S * n;
   float* xr = M->xbuf[(k + 1) & 1];
   float* xw = M->xbuf[k & 1];
-  auto slot = [&](float* buf, int l) { return buf + (size_t)l * n * d; };
-  auto mem_buf = [&](int s) { return ((S - 1 - s) % 2 == 0) ? out->mem : M->memw; };
+  // slot l of sequence b's X buffer; sequence b's memory buffer for segment s
+  auto slot = [&](float* buf, int b, int l) { return buf + ((size_t)b * L + l) * n * d; };
+  auto mem_buf = [&](int b, int s) {
+    return (((S - 1 - s) % 2 == 0) ? out->mem : M->memw) + (size_t)b * L * m * d;
+  };
   const double G_ = G;
   M->cur_groups = G;
 
@@ -194,22 +206,23 @@ int32_t run_cells(rmt_model* M, const Cell* cells, int G, const void* tokens, co
   void* x_out[kMaxGroups];
   void* m_out[kMaxGroups];
   for (int g = 0; g < G; ++g) {
-    const int l = cells[g].l, s = cells[g].s;
-    in_lo[g] = mem_buf(s - 1) + (size_t)l * m * d;
+    const int l = cells[g].l, s = cells[g].s, b = cells[g].b;
+    const size_t tok0 = (size_t)b * T + (size_t)s * n;   // first token of segment s of sequence b
+    in_lo[g] = mem_buf(b, s - 1) + (size_t)l * m * d;
     if (l == 0 && c.cell == RMT_CELL_LINEAR_GELU)
-      in_hi[g] = (const float*)tokens + (size_t)s * n * d;   // fp32 input rows, read in place
+      in_hi[g] = (const float*)tokens + tok0 * d;   // fp32 input rows, read in place
     else
-      in_hi[g] = slot(xr, l);
-    x_out[g] = (l == L - 1) ? (void*)(out->hidden + (size_t)s * n * d) : (void*)slot(xw, l + 1);
-    m_out[g] = mem_buf(s) + (size_t)l * m * d;
+      in_hi[g] = slot(xr, b, l);
+    x_out[g] = (l == L - 1) ? (void*)(out->hidden + tok0 * d) : (void*)slot(xw, b, l + 1);
+    m_out[g] = mem_buf(b, s) + (size_t)l * m * d;
     if (l == 0 && c.cell != RMT_CELL_LINEAR_GELU) {
       // X(-1, s): this segment's input rows, into slot 0 of the read buffer.
       if (c.cell == RMT_CELL_LLAMA) {
-        LAUNCH(launch_gather_tokens(n, d, (const int32_t*)tokens + (size_t)s * n, c.vocab, M->embed,
-                                    slot(xr, 0), M->flag, M->stream));
+        LAUNCH(launch_gather_tokens(n, d, (const int32_t*)tokens + tok0, c.vocab, M->embed,
+                                    slot(xr, b, 0), M->flag, M->stream));
         MARK(RMT_STAGE_GATHER, 0.0, (double)n * (4 + (size_t)d * 6));
       } else {
-        LAUNCH(launch_copy_rows_bf16(n, d, (const uint16_t*)tokens + (size_t)s * n * d, slot(xr, 0),
+        LAUNCH(launch_copy_rows_bf16(n, d, (const uint16_t*)tokens + tok0 * d, slot(xr, b, 0),
                                      M->stream));
         MARK(RMT_STAGE_GATHER, 0.0, (double)n * d * 6);
       }
@@ -304,6 +317,55 @@ int32_t run_cells(rmt_model* M, const Cell* cells, int G, const void* tokens, co
   return RMT_OK;
 }
 
+struct Piece {
+  void** ptr;
+  size_t bytes;
+};
+
+// (Re)allocate the workspace for B sequences: per-launch buffers for up to
+// min(kMaxGroups, B*L) cells, and per-sequence X ping-pong and memory buffers.
+int32_t alloc_workspace(rmt_model* M, int B) {
+  const rmt_config& c = M->cfg;
+  const size_t L = c.L, n = c.n, m = c.m, d = c.d, R = n + m, F = c.ffn;
+  const size_t cells = std::min<size_t>(kMaxGroups, (size_t)B * L);
+  const size_t rows = cells * R;
+  std::vector<Piece> pieces;
+  if (c.cell != RMT_CELL_LINEAR_GELU) {
+    pieces.push_back({(void**)&M->abuf, rows * d * 2});
+    pieces.push_back({(void**)&M->ubuf, rows * F * 2});
+    if (c.cell == RMT_CELL_LLAMA) {
+      pieces.push_back({(void**)&M->qkv, rows * nqkv(c) * 2});
+      pieces.push_back({(void**)&M->att, rows * (size_t)c.n_heads * c.head_dim * 2});
+      pieces.push_back({(void**)&M->hbuf, rows * d * 4});
+    }
+  }
+  pieces.push_back({(void**)&M->xbuf[0], (size_t)B * L * n * d * 4});
+  pieces.push_back({(void**)&M->xbuf[1], (size_t)B * L * n * d * 4});
+  pieces.push_back({(void**)&M->memw, (size_t)B * L * m * d * 4});
+  size_t total = 0;
+  for (auto& p : pieces) total = align_up(total, 256) + p.bytes;
+  total = align_up(total, 256);
+  if (M->ws) {
+    HIP_TRY(hipStreamSynchronize(M->stream));
+    HIP_TRY(hipFree(M->ws));
+    M->ws = nullptr;
+    M->ws_bytes = 0;
+  }
+  void* ws = nullptr;
+  hipError_t e = hipMalloc(&ws, total);
+  if (e != hipSuccess) return fail(RMT_ENOMEM, "hipMalloc(%zu) failed: %s", total, hipGetErrorString(e));
+  M->ws = ws;
+  M->ws_bytes = total;
+  size_t off = 0;
+  for (auto& p : pieces) {
+    off = align_up(off, 256);
+    *p.ptr = (char*)ws + off;
+    off += p.bytes;
+  }
+  M->batch = B;
+  return RMT_OK;
+}
+
 int32_t check_forward_args(rmt_model* M, const void* tokens, const void* mem0, const rmt_output* out) {
   if (!M) return fail(RMT_EINVAL, "model is NULL");
   if (!tokens || !mem0 || !out || !out->hidden || !out->mem)
@@ -313,7 +375,7 @@ int32_t check_forward_args(rmt_model* M, const void* tokens, const void* mem0, c
 
 int32_t start_forward(rmt_model* M, const void* mem0, const rmt_output* out) {
   const rmt_config& c = M->cfg;
-  const size_t mem_bytes = (size_t)c.L * c.m * c.d * sizeof(float);
+  const size_t mem_bytes = (size_t)M->batch * c.L * c.m * c.d * sizeof(float);
   // M(l, -1) lives in the buffer that segment -1 maps to (see the header).
   float* dst = ((c.S - 1 - (-1)) % 2 == 0) ? out->mem : M->memw;
   M->cur_groups = 0;
@@ -381,8 +443,6 @@ int32_t rmt_model_create(const rmt_config* cfg, const rmt_weights* w, void* stre
   const size_t F = (size_t)c.ffn;
   const size_t NQ = c.cell == RMT_CELL_LLAMA ? (size_t)nqkv(c) : 0;
   const size_t HQD = c.cell == RMT_CELL_LLAMA ? (size_t)c.n_heads * c.head_dim : 0;
-  const size_t rowsL = (size_t)L * R;
-  struct Piece { void** ptr; size_t bytes; };
   std::vector<Piece> pieces;
   if (c.cell == RMT_CELL_LINEAR_GELU) {
     pieces.push_back({(void**)&M->w32, (size_t)L * d * d * 4});
@@ -391,21 +451,13 @@ int32_t rmt_model_create(const rmt_config* cfg, const rmt_weights* w, void* stre
     pieces.push_back({(void**)&M->wgu, (size_t)L * 2 * F * d * 2});
     pieces.push_back({(void**)&M->wd, (size_t)L * d * F * 2});
     pieces.push_back({(void**)&M->g2, (size_t)L * d * 4});
-    pieces.push_back({(void**)&M->abuf, rowsL * d * 2});
-    pieces.push_back({(void**)&M->ubuf, rowsL * F * 2});
     if (c.cell == RMT_CELL_LLAMA) {
       pieces.push_back({(void**)&M->wqkv, (size_t)L * NQ * d * 2});
       pieces.push_back({(void**)&M->wo, (size_t)L * d * HQD * 2});
       pieces.push_back({(void**)&M->g1, (size_t)L * d * 4});
       pieces.push_back({(void**)&M->rope, (size_t)R * (c.head_dim / 2) * sizeof(float2)});
-      pieces.push_back({(void**)&M->qkv, rowsL * NQ * 2});
-      pieces.push_back({(void**)&M->att, rowsL * HQD * 2});
-      pieces.push_back({(void**)&M->hbuf, rowsL * d * 4});
     }
   }
-  pieces.push_back({(void**)&M->xbuf[0], (size_t)L * n * d * 4});
-  pieces.push_back({(void**)&M->xbuf[1], (size_t)L * n * d * 4});
-  pieces.push_back({(void**)&M->memw, (size_t)L * m * d * 4});
   pieces.push_back({(void**)&M->flag, 256});
   size_t total = 0;
   for (auto& p : pieces) total = align_up(total, 256) + p.bytes;
@@ -425,9 +477,11 @@ int32_t rmt_model_create(const rmt_config* cfg, const rmt_weights* w, void* stre
 
   auto bail = [&](int32_t code) {
     (void)hipFree(M->block);
+    (void)hipFree(M->ws);
     delete M;
     return code;
   };
+  if (int32_t rc_ws = alloc_workspace(M, 1); rc_ws != RMT_OK) return bail(rc_ws);
 #define CREATE_TRY(expr)                                                              \
   do {                                                                                \
     hipError_t e_ = (expr);                                                           \
@@ -479,6 +533,16 @@ int32_t rmt_model_set_segments(rmt_model* model, int32_t S) {
   return RMT_OK;
 }
 
+int32_t rmt_model_set_batch(rmt_model* model, int32_t B) {
+  if (!model) return fail(RMT_EINVAL, "model is NULL");
+  if (B < 1) return fail(RMT_EINVAL, "B must be >= 1 (got %d)", B);
+  const rmt_config& c = model->cfg;
+  if ((int64_t)B * c.S * c.n > ((int64_t)1 << 40) / std::max(1, c.d))
+    return fail(RMT_EINVAL, "B * S * n * d is too large");
+  if (B == model->batch) return RMT_OK;
+  return alloc_workspace(model, B);
+}
+
 int32_t rmt_model_set_stream(rmt_model* model, void* stream) {
   if (!model) return fail(RMT_EINVAL, "model is NULL");
   model->stream = (hipStream_t)stream;
@@ -487,7 +551,7 @@ int32_t rmt_model_set_stream(rmt_model* model, void* stream) {
 
 int32_t rmt_model_device_bytes(const rmt_model* model, size_t* bytes) {
   if (!model || !bytes) return fail(RMT_EINVAL, "model and bytes must be non-NULL");
-  *bytes = model->bytes;
+  *bytes = model->bytes + model->ws_bytes;
   return RMT_OK;
 }
 
@@ -496,14 +560,16 @@ int32_t rmt_forward_diagonal(rmt_model* M, const void* tokens, const void* mem0,
   if (rc != RMT_OK) return rc;
   rc = start_forward(M, mem0, out);
   if (rc != RMT_OK) return rc;
-  const int L = M->cfg.L, S = M->cfg.S;
-  Cell cells[kMaxGroups];
+  const int L = M->cfg.L, S = M->cfg.S, B = M->batch;
+  std::vector<Cell> diag;
   for (int k = 0; k < L + S - 1; ++k) {
     const int l_lo = std::max(0, k - S + 1), l_hi = std::min(L - 1, k);
-    for (int l0 = l_lo; l0 <= l_hi; l0 += kMaxGroups) {
-      const int G = std::min(kMaxGroups, l_hi - l0 + 1);
-      for (int g = 0; g < G; ++g) cells[g] = Cell{l0 + g, k - (l0 + g)};
-      rc = run_cells(M, cells, G, tokens, out);
+    diag.clear();
+    for (int l = l_lo; l <= l_hi; ++l)
+      for (int b = 0; b < B; ++b) diag.push_back(Cell{l, k - l, b});
+    for (size_t c0 = 0; c0 < diag.size(); c0 += kMaxGroups) {
+      const int G = (int)std::min<size_t>(kMaxGroups, diag.size() - c0);
+      rc = run_cells(M, diag.data() + c0, G, tokens, out);
       if (rc != RMT_OK) return rc;
     }
   }
@@ -515,12 +581,13 @@ int32_t rmt_forward_sequential(rmt_model* M, const void* tokens, const void* mem
   if (rc != RMT_OK) return rc;
   rc = start_forward(M, mem0, out);
   if (rc != RMT_OK) return rc;
-  for (int s = 0; s < M->cfg.S; ++s)
-    for (int l = 0; l < M->cfg.L; ++l) {
-      Cell cell{l, s};
-      rc = run_cells(M, &cell, 1, tokens, out);
-      if (rc != RMT_OK) return rc;
-    }
+  for (int b = 0; b < M->batch; ++b)
+    for (int s = 0; s < M->cfg.S; ++s)
+      for (int l = 0; l < M->cfg.L; ++l) {
+        Cell cell{l, s, b};
+        rc = run_cells(M, &cell, 1, tokens, out);
+        if (rc != RMT_OK) return rc;
+      }
   return RMT_OK;
 }
 
@@ -601,6 +668,10 @@ int32_t rmt_model_destroy(rmt_model* M) {
   hipError_t e1 = hipStreamSynchronize(M->stream);
   for (hipEvent_t e : M->events) (void)hipEventDestroy(e);
   hipError_t e2 = hipFree(M->block);
+  if (M->ws) {
+    const hipError_t e3 = hipFree(M->ws);
+    if (e2 == hipSuccess) e2 = e3;
+  }
   delete M;
   if (e1 != hipSuccess) return fail(RMT_EHIP, "hipStreamSynchronize: %s", hipGetErrorString(e1));
   if (e2 != hipSuccess) return fail(RMT_EHIP, "hipFree: %s", hipGetErrorString(e2));
