@@ -19,10 +19,15 @@ Recurrent Memory Transformers for Long Contexts" (catalogue record, abstract).
   rows Y; the first n rows become X(l, s), the last m rows become M(l, s).
 * The (layer, segment) grid is swept along anti-diagonals d = l + s
   (*Implementation*, the scheduler's diagonal enumeration; *Architecture
-  Overview*, "Diagonal Reorganization").  Every cell of a diagonal depends
+  Overview*, Diagonal Reorganization).  Every cell of a diagonal depends
   only on (l-1, s) and (l, s-1), so the reordering is exact (*Architecture
-  Overview*, "Dependency Preservation"; abstract, "preserving exact
-  recurrence", "purely a run-time computation reordering").
+  Overview*, Dependency Preservation; the abstract states that the
+  recurrence stays exact and only the run-time order of the computation
+  changes).
+* A sequence whose length T is not a multiple of n ends in a shorter
+  segment of n' = T - (S-1) n rows (the *Implementation* sketch rounds the
+  segment count up): its cells have m + n' rows, the first n' become X and
+  the last m become M, the same split rule as every other cell.
 
 Readings where the pages are silent (each is listed in the design doc):
   - the cell function is the one each workload defines: linear+GELU (tiny
@@ -205,8 +210,9 @@ def _cast_weights(weights: Sequence[Dict[str, np.ndarray]], dtype) -> List[Dict[
 
 
 def segment_input(cfg, inputs: np.ndarray, s: int, embed, dtype) -> np.ndarray:
-    """X(-1, s): the segment's n input rows.  For the LLaMA cell ``inputs``
-    are token ids looked up in ``embed``; otherwise they are rows [T, d]."""
+    """X(-1, s): the segment's input rows -- n of them, fewer for a short last
+    segment.  For the LLaMA cell ``inputs`` are token ids looked up in
+    ``embed``; otherwise they are rows [T, d]."""
     n = cfg.n
     if cfg.cell == CELL_LLAMA:
         return np.asarray(embed[inputs[s * n:(s + 1) * n]], dtype=dtype)
@@ -214,17 +220,18 @@ def segment_input(cfg, inputs: np.ndarray, s: int, embed, dtype) -> np.ndarray:
 
 
 def _num_segments(cfg, inputs) -> int:
+    """ceil(T / n): a length that is not a multiple of n ends in a short segment."""
     T = inputs.shape[0]
-    if T % cfg.n != 0:
-        raise ValueError("sequence length must be a whole number of segments")
-    return T // cfg.n
+    if T < 1:
+        raise ValueError("empty sequence")
+    return -(-T // cfg.n)
 
 
 def forward_sequential(cfg, weights, inputs, mem0, embed=None, dtype=np.float32):
     """Segment by segment, then layer by layer.
 
-    Returns (hidden [S*n, d] = X(L-1, .), memory [L, m, d] = M(., S-1)).
-    The number of segments is taken from ``inputs``."""
+    Returns (hidden [T, d] = X(L-1, .), memory [L, m, d] = M(., S-1)).
+    The number of segments, ceil(T / n), is taken from ``inputs``."""
     S = _num_segments(cfg, inputs)
     L, n = cfg.L, cfg.n
     ws = _cast_weights(weights, dtype)
@@ -232,10 +239,11 @@ def forward_sequential(cfg, weights, inputs, mem0, embed=None, dtype=np.float32)
     hidden = []
     for s in range(S):
         x = segment_input(cfg, inputs, s, embed, dtype)
+        ns = x.shape[0]                      # n, or n' for a short last segment
         for l in range(L):
             A = np.concatenate([M[l], x], axis=0)
             Y = cell(cfg, ws[l], A)
-            x, M[l] = Y[:n], Y[n:]
+            x, M[l] = Y[:ns], Y[ns:]
         hidden.append(x)
     return np.concatenate(hidden, axis=0), np.stack(M)
 
@@ -262,10 +270,11 @@ def forward_diagonal(cfg, weights, inputs, mem0, embed=None, dtype=np.float32):
         next_x = {}
         for (l, s), A in zip(diag, A_list):
             Y = cell(cfg, ws[l], A)
-            next_x[(l, s)] = Y[:n]
-            M[l] = Y[n:]
+            ns = A.shape[0] - cfg.m          # the segment's rows: n, or n' at the end
+            next_x[(l, s)] = Y[:ns]
+            M[l] = Y[ns:]
             if l == L - 1:
-                hidden[s] = Y[:n]
+                hidden[s] = Y[:ns]
         prev_x = next_x
     return np.concatenate(hidden, axis=0), np.stack(M)
 
@@ -280,18 +289,31 @@ def forward_diagonal(cfg, weights, inputs, mem0, embed=None, dtype=np.float32):
 # ---------------------------------------------------------------------------
 
 def bruteforce_linear_gelu(cfg, weights, x0, mem0):
+    """As above, for T = S_full * n + r rows: the r < n rows of a short last
+    segment form one more, smaller product per layer.  Its memory comes from
+    rows r .. r+m-1 of that cell's [M(l, S-2); X(l-1, S-1)], i.e. the last
+    m - r rows of M(l, S-2) followed by its r input rows when r < m."""
     assert cfg.cell == CELL_LINEAR_GELU and cfg.m <= cfg.n
     L, n, m, d = cfg.L, cfg.n, cfg.m, cfg.d
-    S = x0.shape[0] // n
-    X = np.asarray(x0, np.float64).reshape(S, n, d)
+    T = x0.shape[0]
+    S, r = T // n, T % n                     # whole segments, rows of the short one
+    x0 = np.asarray(x0, np.float64)
+    X = x0[:S * n].reshape(S, n, d)
+    Xr = x0[S * n:]                          # [r, d]
     mem_last = []
     for l in range(L):
         W = np.asarray(weights[l]["w"], np.float64)
         b = np.asarray(weights[l]["b"], np.float64)
         f = lambda rows: gelu_erf(rows @ W + b)  # noqa: E731
-        M_all = f(X[:, n - m:, :].reshape(S * m, d)).reshape(S, m, d)
-        M_prev = np.concatenate([np.asarray(mem0[l], np.float64)[None], M_all[:-1]], axis=0)
-        A = np.concatenate([M_prev, X], axis=1).reshape(S * (m + n), d)
-        X = f(A).reshape(S, m + n, d)[:, :n, :]
-        mem_last.append(M_all[-1])
-    return X.reshape(S * n, d), np.stack(mem_last)
+        last = np.asarray(mem0[l], np.float64)
+        if S:
+            M_all = f(X[:, n - m:, :].reshape(S * m, d)).reshape(S, m, d)
+            M_prev = np.concatenate([last[None], M_all[:-1]], axis=0)
+            A = np.concatenate([M_prev, X], axis=1).reshape(S * (m + n), d)
+            X = f(A).reshape(S, m + n, d)[:, :n, :]
+            last = M_all[-1]
+        if r:
+            Yr = f(np.concatenate([last, Xr], axis=0))   # the short cell, m + r rows
+            Xr, last = Yr[:r], Yr[r:]
+        mem_last.append(last)
+    return np.concatenate([X.reshape(S * n, d), Xr], axis=0), np.stack(mem_last)

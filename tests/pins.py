@@ -281,3 +281,54 @@ def pin_attention(attn=orc.causal_gqa_attention):
     out = attn(q, k, v).reshape(R, Hq, hd)
     for h in range(Hq):
         assert np.allclose(out[0, h], v[0, h * Hkv // Hq], atol=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# A short last segment (T not a multiple of n)
+# ---------------------------------------------------------------------------
+
+def ragged_inputs(cfg, T, seed=0):
+    """The first T rows (or ids) of the workload's draw, with its weights,
+    initial memory and embedding."""
+    w = ri.all_weights(cfg, seed)
+    mem0 = ri.initial_memory(cfg, seed)
+    if cfg.cell == ri.CELL_LLAMA:
+        return w, ri.tokens(cfg, seed)[:T].copy(), mem0, ri.embedding(cfg, seed)
+    return w, ri.input_embeddings(cfg, seed)[:T].copy(), mem0, None
+
+
+def pin_linear_gelu_bruteforce_ragged(T, forward=orc.forward_sequential, tol=1e-13):
+    """fp64 sweep against the fp64 whole-sequence products with a short tail."""
+    cfg = ri.TINY_LINEAR_GELU
+    w, x0, mem0, _ = ragged_inputs(cfg, T)
+    hid, mem = forward(cfg, w, x0, mem0, dtype=np.float64)
+    hid_bf, mem_bf = orc.bruteforce_linear_gelu(cfg, w, x0, mem0)
+    assert hid.shape == (T, cfg.d)
+    assert normwise(hid, hid_bf) <= tol, normwise(hid, hid_bf)
+    assert normwise(mem, mem_bf) <= tol, normwise(mem, mem_bf)
+
+
+def pin_shift_register_ragged(cfg, T, forward=orc.forward_sequential):
+    """Identity cells: the closed form holds for any segment lengths (the
+    concatenated [M(l,-1); input stream] is cut into consecutive pieces)."""
+    ws = identity_weights(cfg)
+    _, x, mem0, emb = ragged_inputs(cfg, T)
+    hid, mem = forward(cfg, ws, x, mem0, emb)
+    x_stream = emb[x] if cfg.cell == ri.CELL_LLAMA else x
+    exp_hid, exp_mem = shift_register_closed_form(cfg, x_stream, mem0)
+    assert np.array_equal(hid.astype(np.float64), exp_hid)
+    assert np.array_equal(mem.astype(np.float64), exp_mem)
+
+
+def pin_short_single_segment_against_torch(cfg, n_short, forward=orc.forward_sequential, tol=1e-11):
+    """S = 1, L = 1 with n' < n input rows: one pre-norm block over m + n' rows."""
+    import dataclasses
+    c1 = dataclasses.replace(cfg, L=1, S=1)
+    w, x, mem0, emb = ragged_inputs(c1, n_short)
+    hid, mem = forward(c1, w, x, mem0, emb, dtype=np.float64)
+    rows = emb[x] if c1.cell == ri.CELL_LLAMA else x
+    A = np.concatenate([mem0[0], rows], axis=0)
+    Y = torch_llama_block(A, w[0], c1) if c1.cell == ri.CELL_LLAMA else torch_norm_swiglu_block(A, w[0], c1)
+    assert hid.shape[0] == n_short
+    assert normwise(hid, Y[:n_short]) <= tol, normwise(hid, Y[:n_short])
+    assert normwise(mem[0], Y[n_short:]) <= tol, normwise(mem[0], Y[n_short:])

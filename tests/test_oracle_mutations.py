@@ -170,3 +170,44 @@ def test_mutation_attention_scale(monkeypatch):
     real = orc.causal_gqa_attention
     monkeypatch.setattr(orc, "causal_gqa_attention", lambda q, k, v: real(q * 2.0, k, v))
     assert _fails(pins.pin_single_segment_against_torch, ri.TINY_LLAMA)
+
+
+def _forward_short_tail_mistake(keep_memory_on_tail=False, pad_tail=False):
+    """A sweep that mishandles a short last segment: either the short cells
+    leave the memory as it was, or the short segment is padded with zero rows
+    up to n before the cells run."""
+    def fwd(cfg, weights, inputs, mem0, embed=None, dtype=np.float32):
+        T = inputs.shape[0]
+        S = -(-T // cfg.n)
+        L, n = cfg.L, cfg.n
+        ws = [{k: np.asarray(v, dtype) for k, v in w.items()} for w in weights]
+        M = [np.array(mem0[l], dtype) for l in range(L)]
+        hidden = []
+        for s in range(S):
+            x = orc.segment_input(cfg, inputs, s, embed, dtype)
+            ns = x.shape[0]
+            if pad_tail and ns < n:
+                x = np.concatenate([x, np.zeros((n - ns, x.shape[1]), dtype)])
+            for l in range(L):
+                Y = orc.cell(cfg, ws[l], np.concatenate([M[l], x]))
+                rows = x.shape[0]
+                x = Y[:rows]
+                if not (keep_memory_on_tail and ns < n):
+                    M[l] = Y[rows:]
+            hidden.append(x[:ns])
+        return np.concatenate(hidden), np.stack(M)
+    return fwd
+
+
+@pytest.mark.parametrize("T", [5 * 16 + 2, 5 * 16 + 7])
+def test_mutation_short_tail_keeps_memory(T):
+    bad = _forward_short_tail_mistake(keep_memory_on_tail=True)
+    assert _fails(pins.pin_linear_gelu_bruteforce_ragged, T,
+                  forward=lambda *a, **k: bad(*a, **{**k, "dtype": np.float64}))
+
+
+@pytest.mark.parametrize("T", [5 * 16 + 2, 5 * 16 + 7])
+def test_mutation_short_tail_zero_padded(T):
+    bad = _forward_short_tail_mistake(pad_tail=True)
+    assert _fails(pins.pin_linear_gelu_bruteforce_ragged, T,
+                  forward=lambda *a, **k: bad(*a, **{**k, "dtype": np.float64}))

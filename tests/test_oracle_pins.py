@@ -143,3 +143,44 @@ def test_inplace_diagonal_sweep_is_wrong():
     assert not np.array_equal(h, h_bad)
     with pytest.raises(AssertionError):
         assert pins.normwise(h_bad, h) <= 1e-5
+
+
+# ---- a short last segment ---------------------------------------------------
+
+N_LG = ri.TINY_LINEAR_GELU.n     # 16 rows per segment, m = 4
+
+
+@pytest.mark.parametrize("T", [5 * N_LG + 2, 5 * N_LG + 7, 5 * N_LG + 15, 9, 1])
+def test_linear_gelu_bruteforce_ragged(T):
+    """short tails with r < m, r >= m, r = n - 1, and sequences of one short segment"""
+    pins.pin_linear_gelu_bruteforce_ragged(T)
+    fwd = lambda *a, **k: orc.forward_diagonal(*a, **k)  # noqa: E731
+    pins.pin_linear_gelu_bruteforce_ragged(T, forward=fwd)
+
+
+@pytest.mark.parametrize("cfg", TINY_RESIDUAL, ids=lambda c: c.name)
+def test_shift_register_ragged(cfg):
+    T = (cfg.S - 1) * cfg.n + cfg.n // 3
+    pins.pin_shift_register_ragged(cfg, T)
+    pins.pin_shift_register_ragged(cfg, T, forward=orc.forward_diagonal)
+
+
+@pytest.mark.parametrize("cfg", TINY_RESIDUAL, ids=lambda c: c.name)
+def test_short_single_segment_against_torch(cfg):
+    pins.pin_short_single_segment_against_torch(cfg, cfg.n // 3 + 1)
+
+
+@pytest.mark.parametrize("cfg", [ri.TINY_LINEAR_GELU, ri.TINY_LLAMA], ids=lambda c: c.name)
+def test_ragged_run_extends_the_whole_segment_prefix(cfg):
+    """Segments never read later ones: the whole segments of a ragged run
+    equal the run over just those segments, bit for bit."""
+    S_full = cfg.S - 1
+    T = S_full * cfg.n + cfg.n // 2
+    w, x, mem0, emb = pins.ragged_inputs(cfg, T)
+    h, _ = orc.forward_sequential(cfg, w, x, mem0, emb)
+    hp, _ = orc.forward_sequential(cfg, w, x[:S_full * cfg.n], mem0, emb)
+    assert h.shape[0] == T
+    assert np.array_equal(h[:S_full * cfg.n], hp)
+    hd, md = orc.forward_diagonal(cfg, w, x, mem0, emb)
+    hs, ms = orc.forward_sequential(cfg, w, x, mem0, emb)
+    assert np.array_equal(hd, hs) and np.array_equal(md, ms)
