@@ -106,7 +106,7 @@ typedef struct rmt_weights {
 
 /* Outputs of a forward call (device pointers, caller-allocated), for each of
  * the B sequences (B = 1 unless set by rmt_model_set_batch):
- *   hidden [B][S*n][d] fp32: X(L-1, s) for every segment, in segment order.
+ *   hidden [B][T][d] fp32: X(L-1, s) for every segment, in segment order.
  *   mem    [B][L][m][d] fp32: M(l, S-1), the memory after the last segment;
  *          it may alias the mem0 argument (in-place state update). */
 typedef struct rmt_output {
@@ -140,16 +140,27 @@ int32_t rmt_diag_schedule(int32_t L, int32_t S, int32_t* diag_ptr, int32_t* cell
 int32_t rmt_model_create(const rmt_config* cfg, const rmt_weights* w, void* stream,
                          rmt_model** out);
 
-/* Re-target the model to S segments per forward call (no allocation). */
+/* Re-target the model to S whole segments (T = S*n tokens) per forward call
+ * (no allocation). */
 int32_t rmt_model_set_segments(rmt_model* model, int32_t S);
+
+/* Re-target the model to T >= 1 tokens per sequence and forward call (no
+ * allocation): S = ceil(T / n) segments, the last of n' = T - (S-1) n rows
+ * when T is not a multiple of n (the skill page's Implementation sketch
+ * rounds the segment count up).  A short segment's cells have m + n' rows;
+ * their first n' output rows become X(l, S-1) and the last m become
+ * M(l, S-1), as for every other cell; they run in launches of their own.
+ * The forward calls' token, input-row and hidden buffers then hold T rows per
+ * sequence.  Errors: RMT_EINVAL (NULL model, T < 1, T too large). */
+int32_t rmt_model_set_tokens(rmt_model* model, int64_t T);
 
 /* Process B >= 1 independent sequences per forward call (default 1): the
  * batch dimension of the skill page's Implementation sketch.  Every diagonal
  * then covers the cells of all B sequences -- layer-major, sequence fastest,
  * in launches of at most 32 cells -- so B sequences fill the ramp diagonals
  * that one sequence leaves short of L cells.  The forward calls' buffers gain
- * a leading [B]: tokens [B][S*n] (or [B][S*n][d]), mem0 and out->mem
- * [B][L][m][d], out->hidden [B][S*n][d]; sequence b's results equal a B = 1
+ * a leading [B]: tokens [B][T] (or [B][T][d]), mem0 and out->mem
+ * [B][L][m][d], out->hidden [B][T][d]; sequence b's results equal a B = 1
  * run on its inputs, bit for bit.  Synchronises the model's stream and
  * reallocates the workspace (hipMalloc / hipFree) when B changes.
  * Errors: RMT_EINVAL (NULL model, B < 1, sizes too large), RMT_ENOMEM,
@@ -163,11 +174,12 @@ int32_t rmt_model_set_stream(rmt_model* model, void* stream);
 int32_t rmt_model_device_bytes(const rmt_model* model, size_t* bytes);
 
 /* Diagonal-batched forward pass over B sequences (rmt_model_set_batch;
- * B = 1 unless set) of S*n tokens each.
- *   tokens  device: LLAMA -> int32 token ids [B][S*n] in [0, V) (ids outside
+ * B = 1 unless set) of T tokens each (T = S*n unless rmt_model_set_tokens
+ * set another length).
+ *   tokens  device: LLAMA -> int32 token ids [B][T] in [0, V) (ids outside
  *           that range read a zero embedding row and set the flag reported
  *           by rmt_model_check); other cells -> input rows X(-1, .)
- *           [B][S*n][d] (fp32 for RMT_F32 models, bf16 for RMT_BF16 models).
+ *           [B][T][d] (fp32 for RMT_F32 models, bf16 for RMT_BF16 models).
  *   mem0    device fp32 [B][L][m][d]: M(l, -1) of each sequence.
  *   out     see rmt_output (hidden [B][S*n][d], mem [B][L][m][d]).
  * For every diagonal k the library launches, on the model's stream, one

@@ -110,6 +110,12 @@ class RMTModel:
         check(lib().rmt_model_set_segments(self._handle, S))
         self.cfg.S = S
 
+    def set_tokens(self, T: int) -> None:
+        """T tokens per sequence: ceil(T / n) segments, the last one short when
+        T is not a multiple of n."""
+        check(lib().rmt_model_set_tokens(self._handle, T))
+        self.cfg.S = -(-T // self.cfg.n)
+
     def set_batch(self, B: int) -> None:
         """B sequences per forward call: inputs and outputs gain a leading [B]."""
         check(lib().rmt_model_set_batch(self._handle, B))

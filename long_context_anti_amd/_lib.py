@@ -56,6 +56,7 @@ SIGNATURES = {
     "rmt_model_set_segments": (C.c_int32, [C.c_void_p, C.c_int32]),
     "rmt_model_set_stream": (C.c_int32, [C.c_void_p, C.c_void_p]),
     "rmt_model_set_batch": (C.c_int32, [C.c_void_p, C.c_int32]),
+    "rmt_model_set_tokens": (C.c_int32, [C.c_void_p, C.c_int64]),
     "rmt_model_device_bytes": (C.c_int32, [C.c_void_p, C.POINTER(C.c_size_t)]),
     "rmt_forward_diagonal": (C.c_int32, [C.c_void_p, C.c_void_p, C.c_void_p, C.POINTER(RmtOutput)]),
     "rmt_forward_sequential": (C.c_int32, [C.c_void_p, C.c_void_p, C.c_void_p, C.POINTER(RmtOutput)]),

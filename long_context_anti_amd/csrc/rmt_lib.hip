@@ -71,6 +71,7 @@ struct rmt_model {
   void* ws = nullptr;      // workspace, sized for the batch
   size_t ws_bytes = 0;
   int batch = 1;           // sequences per forward call
+  int n_last = 0;          // rows of the last segment: n, or fewer when T is not a multiple of n
 
   // packed weights (bf16, [L][N][K]) and gains (fp32)
   uint16_t* wqkv = nullptr;
@@ -187,9 +188,12 @@ struct Cell {
 int32_t run_cells(rmt_model* M, const Cell* cells, int G, const void* tokens, const rmt_output* out) {
   const rmt_config& c = M->cfg;
   const int L = c.L, S = c.S, n = c.n, m = c.m, d = c.d;
-  const int R = n + m;
+  // Every cell of one launch has the same number of segment rows: n, or
+  // n_last for the cells of a short last segment (the driver keeps them apart).
+  const int ns = cells[0].s == S - 1 ? M->n_last : n;
+  const int R = ns + m;
   const int k = cells[0].l + cells[0].s;
-  const size_t T = (size_t)S * n;
+  const size_t T = (size_t)(S - 1) * n + M->n_last;   // tokens per sequence
   float* xr = M->xbuf[(k + 1) & 1];
   float* xw = M->xbuf[k & 1];
   // slot l of sequence b's X buffer; sequence b's memory buffer for segment s
@@ -218,13 +222,13 @@ int32_t run_cells(rmt_model* M, const Cell* cells, int G, const void* tokens, co
     if (l == 0 && c.cell != RMT_CELL_LINEAR_GELU) {
       // X(-1, s): this segment's input rows, into slot 0 of the read buffer.
       if (c.cell == RMT_CELL_LLAMA) {
-        LAUNCH(launch_gather_tokens(n, d, (const int32_t*)tokens + tok0, c.vocab, M->embed,
+        LAUNCH(launch_gather_tokens(ns, d, (const int32_t*)tokens + tok0, c.vocab, M->embed,
                                     slot(xr, b, 0), M->flag, M->stream));
-        MARK(RMT_STAGE_GATHER, 0.0, (double)n * (4 + (size_t)d * 6));
+        MARK(RMT_STAGE_GATHER, 0.0, (double)ns * (4 + (size_t)d * 6));
       } else {
-        LAUNCH(launch_copy_rows_bf16(n, d, (const uint16_t*)tokens + tok0 * d, slot(xr, b, 0),
+        LAUNCH(launch_copy_rows_bf16(ns, d, (const uint16_t*)tokens + tok0 * d, slot(xr, b, 0),
                                      M->stream));
-        MARK(RMT_STAGE_GATHER, 0.0, (double)n * d * 6);
+        MARK(RMT_STAGE_GATHER, 0.0, (double)ns * d * 6);
       }
     }
   }
@@ -245,7 +249,7 @@ int32_t run_cells(rmt_model* M, const Cell* cells, int G, const void* tokens, co
 
   if (c.cell == RMT_CELL_LINEAR_GELU) {
     set_io(in_lo, in_hi, x_out, m_out);
-    LAUNCH(launch_linear_gelu_f32(G, R, d, m, n, tab, M->w32, M->b32, M->stream));
+    LAUNCH(launch_linear_gelu_f32(G, R, d, m, ns, tab, M->w32, M->b32, M->stream));
     MARK(RMT_STAGE_LINEAR, 2.0 * rows * d * d, rows * d * 8 + G_ * d * (d + 1) * 4);
     return RMT_OK;
   }
@@ -311,7 +315,7 @@ int32_t run_cells(rmt_model* M, const Cell* cells, int G, const void* tokens, co
     ga.split_in = m;
   }
   ga.A = M->ubuf; ga.B = M->wd; ga.M = R; ga.N = d; ga.K = F;
-  ga.split_out = n; ga.ld_res = d; ga.ld_out = d;
+  ga.split_out = ns; ga.ld_res = d; ga.ld_out = d;
   LAUNCH(launch_gemm_bf16(EPI_RESID_F32, ga, tab, M->stream));
   MARK(RMT_STAGE_DOWN, 2.0 * rows * F * d, rows * F * 2 + G_ * d * F * 2 + rows * d * 8);
   return RMT_OK;
@@ -437,6 +441,7 @@ int32_t rmt_model_create(const rmt_config* cfg, const rmt_weights* w, void* stre
 
   rmt_model* M = new rmt_model();
   M->cfg = c;
+  M->n_last = c.n;
   M->stream = (hipStream_t)stream;
 
   // Carve one allocation.
@@ -530,6 +535,22 @@ int32_t rmt_model_set_segments(rmt_model* model, int32_t S) {
   int32_t rc = validate_config(&c);
   if (rc != RMT_OK) return rc;
   model->cfg.S = S;
+  model->n_last = model->cfg.n;
+  return RMT_OK;
+}
+
+int32_t rmt_model_set_tokens(rmt_model* model, int64_t T) {
+  if (!model) return fail(RMT_EINVAL, "model is NULL");
+  if (T < 1) return fail(RMT_EINVAL, "T must be >= 1");
+  const int64_t n = model->cfg.n;
+  const int64_t S = (T + n - 1) / n;
+  if (S > INT32_MAX) return fail(RMT_EINVAL, "T is too large");
+  rmt_config c = model->cfg;
+  c.S = (int32_t)S;
+  int32_t rc = validate_config(&c);
+  if (rc != RMT_OK) return rc;
+  model->cfg.S = (int32_t)S;
+  model->n_last = (int)(T - (S - 1) * n);
   return RMT_OK;
 }
 
@@ -567,11 +588,17 @@ int32_t rmt_forward_diagonal(rmt_model* M, const void* tokens, const void* mem0,
     diag.clear();
     for (int l = l_lo; l <= l_hi; ++l)
       for (int b = 0; b < B; ++b) diag.push_back(Cell{l, k - l, b});
-    for (size_t c0 = 0; c0 < diag.size(); c0 += kMaxGroups) {
-      const int G = (int)std::min<size_t>(kMaxGroups, diag.size() - c0);
-      rc = run_cells(M, diag.data() + c0, G, tokens, out);
-      if (rc != RMT_OK) return rc;
-    }
+    // cells of a short last segment have fewer rows: they get launches of their own
+    const auto short_cell = [&](const Cell& x) { return x.s == S - 1 && M->n_last != M->cfg.n; };
+    std::stable_partition(diag.begin(), diag.end(), [&](const Cell& x) { return !short_cell(x); });
+    const size_t n_regular =
+        (size_t)std::count_if(diag.begin(), diag.end(), [&](const Cell& x) { return !short_cell(x); });
+    for (const auto& part : {std::make_pair((size_t)0, n_regular), std::make_pair(n_regular, diag.size())})
+      for (size_t c0 = part.first; c0 < part.second; c0 += kMaxGroups) {
+        const int G = (int)std::min<size_t>(kMaxGroups, part.second - c0);
+        rc = run_cells(M, diag.data() + c0, G, tokens, out);
+        if (rc != RMT_OK) return rc;
+      }
   }
   return RMT_OK;
 }

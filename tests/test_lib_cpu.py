@@ -129,3 +129,4 @@ def test_forward_rejects_null_model():
     assert L.lib().rmt_model_destroy(None) == L.RMT_OK
     assert L.lib().rmt_model_stage_times_groups(None, 1, 2, None, None, None, None) == L.RMT_EINVAL
     assert L.lib().rmt_model_set_batch(None, 2) == L.RMT_EINVAL
+    assert L.lib().rmt_model_set_tokens(None, 100) == L.RMT_EINVAL
