@@ -10,7 +10,7 @@
 //
 // Design (measured on MI355X; the operand stream from L2, not the MFMA rate,
 // is what limits this kernel, so tiles are as large as LDS allows):
-//   * Output tiles of 288 x 256, 256 x 256 or 128 x 256, chosen per launch
+//   * Output tiles of 288, 256, 192 or 128 rows x 256 columns, chosen per launch
 //     by a cost model of whole rounds of one tile per CU (see launch_epi);
 //     waves compute 32 x 32 blocks with v_mfma_f32_32x32x16_bf16.  A cell
 //     (group) never shares a tile with another; the rows past the cell's end
@@ -418,10 +418,11 @@ void launch_one(const GemmArgs& a, const GroupTable& tab, hipStream_t stream) {
 //   288 x 256: twelve waves of 96 x 64 (3 x 2 blocks); a 1152-row cell is
 //              exactly four tiles.                              speed 1.00
 //   256 x 256: eight waves of 64 x 128 (2 x 4 blocks).           speed 0.95
+//   192 x 256: eight waves of 96 x 64 (3 x 2 blocks).            speed 0.85
 //   128 x 256: eight waves of 64 x 64; 32 x 128 for RoPE over
 //              128-wide heads.                                  speed 0.72
 // RoPE needs both halves of a head in one wave's columns, so 128-wide heads
-// exclude the 64-column waves of the 288-row shape.  Every shape uses the
+// exclude the 64-column waves of the 288- and 192-row shapes.  Every shape uses the
 // same K slicing and lane/k assignment, so a cell's result does not depend on
 // the choice.
 int num_cus() {
@@ -446,11 +447,14 @@ void launch_epi(const GemmArgs& a, const GroupTable& tab, hipStream_t stream) {
   const bool wide_heads = EPI == EPI_QKV_ROPE && a.hd == 128;
   const double c288 = wide_heads ? 1e300 : tile_cost(a, tab.G, 288, 1.00);
   const double c256 = tile_cost(a, tab.G, 256, 0.95);
+  const double c192 = wide_heads ? 1e300 : tile_cost(a, tab.G, 192, 0.85);
   const double c128 = tile_cost(a, tab.G, 128, 0.72);
-  if (c288 <= c256 && c288 <= c128) {
+  if (c288 <= c256 && c288 <= c192 && c288 <= c128) {
     launch_one<EPI, 288, 96, 64>(a, tab, stream);
-  } else if (c256 <= c128) {
+  } else if (c256 <= c192 && c256 <= c128) {
     launch_one<EPI, 256, 64, 128>(a, tab, stream);
+  } else if (c192 <= c128) {
+    launch_one<EPI, 192, 96, 64>(a, tab, stream);
   } else if (wide_heads) {
     launch_one<EPI, 128, 32, 128>(a, tab, stream);
   } else {
