@@ -349,15 +349,19 @@ int32_t alloc_workspace(rmt_model* M, int B) {
   size_t total = 0;
   for (auto& p : pieces) total = align_up(total, 256) + p.bytes;
   total = align_up(total, 256);
-  if (M->ws) {
-    HIP_TRY(hipStreamSynchronize(M->stream));
-    HIP_TRY(hipFree(M->ws));
-    M->ws = nullptr;
-    M->ws_bytes = 0;
-  }
+  // The new block is allocated before the old one is released, so a failure
+  // leaves the model as it was (same batch, same buffers).
+  if (M->ws) HIP_TRY(hipStreamSynchronize(M->stream));
   void* ws = nullptr;
   hipError_t e = hipMalloc(&ws, total);
   if (e != hipSuccess) return fail(RMT_ENOMEM, "hipMalloc(%zu) failed: %s", total, hipGetErrorString(e));
+  if (M->ws) {
+    e = hipFree(M->ws);
+    if (e != hipSuccess) {
+      (void)hipFree(ws);
+      return fail(RMT_EHIP, "hipFree: %s", hipGetErrorString(e));
+    }
+  }
   M->ws = ws;
   M->ws_bytes = total;
   size_t off = 0;
