@@ -140,22 +140,44 @@ __global__ __launch_bounds__((BM / WTM) * (BN / WTN) * 64, 1) void gemm_bf16_ker
   // physical chunk L % CPR, which holds logical chunk (L % CPR) ^ swz(row).
   const int lrow = lane / CPR;
   const int lp = lane % CPR;
-  auto issue = [&](int kt, int stage) __attribute__((always_inline)) {
+  // Per-lane byte offsets of this wave's loads at k = 0 (loop invariant); a
+  // K slice adds 2 k0 to them.  The wave index is taken as a uniform value so
+  // that the LDS destination (M0) is computed with scalar instructions.
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  __builtin_assume(wave_u >= 0 && wave_u < NWAVES);
+  int koff[LOADS_PER_WAVE];
+#pragma unroll
+  for (int i = 0; i < LOADS_PER_WAVE; ++i) {
+    const int q = min(wave_u + i * NWAVES, ALL_LOADS - 1);
+    const bool is_a = q < A_LOADS;
+    const int row = (is_a ? q : q - A_LOADS) * RPI + lrow;
+    koff[i] = (row * K + 8 * (lp ^ swz(row))) * 2;
+  }
+  const bool k_whole = K % BK == 0;
+  // CHECKED: the partial last K slice, whose columns past K must read as
+  // zeros (their offsets are moved past the end of the buffer).
+  auto issue_slice = [&](int kt, int stage, auto checked_c) __attribute__((always_inline)) {
+    constexpr bool CHECKED = decltype(checked_c)::value;
     const int k0 = kt * BK;
     uint8_t* sbase = smem + stage * STAGE_BYTES;
 #pragma unroll
     for (int i = 0; i < LOADS_PER_WAVE; ++i) {
-      const int q = wave + i * NWAVES;          // wave-uniform
+      const int q = wave_u + i * NWAVES;        // wave-uniform
       if (ALL_LOADS % NWAVES != 0 && q >= ALL_LOADS) break;
       // i is a constant after unrolling: the operand is known at compile time
       // unless the A/B boundary falls inside this round of loads
       const bool is_a = (i + 1) * NWAVES <= A_LOADS ? true : i * NWAVES >= A_LOADS ? false : q < A_LOADS;
-      const int row = (is_a ? q : q - A_LOADS) * RPI + lrow;
-      const int k = k0 + 8 * (lp ^ swz(row));
-      const int nbytes = is_a ? a_bytes : b_bytes;
-      const int off = k < K ? (row * K + k) * 2 : nbytes;
+      int off = koff[i] + 2 * k0;
+      if constexpr (CHECKED) {
+        const int row = (is_a ? q : q - A_LOADS) * RPI + lrow;
+        if (k0 + 8 * (lp ^ swz(row)) >= K) off = is_a ? a_bytes : b_bytes;
+      }
       __builtin_amdgcn_raw_ptr_buffer_load_lds(is_a ? ra : rb, (lds_ptr_t)(sbase + q * 1024), 16, off, 0, 0, 0);
     }
+  };
+  auto issue = [&](int kt, int stage) __attribute__((always_inline)) {
+    if (!k_whole && kt == (K - 1) / BK) issue_slice(kt, stage, std::true_type{});
+    else issue_slice(kt, stage, std::false_type{});
   };
 
   f32x16 acc[MI][NI];
