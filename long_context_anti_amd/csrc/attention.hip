@@ -16,12 +16,13 @@
 // through the transposing LDS read ds_read_b64_tr_b16.  The softmax is
 // online in fp32 and base 2 (one FMA + one v_exp_f32 per score); the running
 // output is rescaled only when a row maximum grows by more than 2^8, which
-// keeps every probability below 256 and leaves O / l unchanged.  The VALU,
-// not the MFMA, bounds this kernel at head_dim 64 (v_exp_f32 issues at a
-// quarter of the FMA rate), so the row sums l come from one more MFMA per
-// step against a row of ones -- the sum of exactly the bf16 probabilities
-// that multiply V -- and the row maxima cross lane groups with
-// v_permlane16/32_swap instead of LDS permutes.
+// keeps every probability below 256 and leaves O / l unchanged.  At
+// head_dim 64 a key block costs a wave more VALU cycles than MFMA cycles
+// (v_exp_f32 issues at a quarter of the FMA rate), so VALU work is kept
+// off the per-block path where it can be: the row sums l come from one more
+// MFMA per step against a row of ones -- the sum of exactly the bf16
+// probabilities that multiply V -- and the row maxima cross lane groups
+// (v_permlane16/32_swap) only when a rescale is due.
 #include "kernels.h"
 
 namespace rmt {
@@ -53,6 +54,14 @@ __device__ __forceinline__ float max_over_groups(float v) {
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
+// Workgroups are handed to the 8 XCDs round-robin (id mod 8); this
+// renumbering gives each XCD one contiguous run of ids.
+__device__ __forceinline__ int xcd_remap(int bid, int nb) {
+  const int per = nb >> 3, rem = nb & 7;
+  const int xcd = bid & 7, idx = bid >> 3;
+  return xcd * per + (xcd < rem ? xcd : rem) + idx;
+}
+
 template <int HD, int QB>
 __global__ __launch_bounds__(256, 2) void attention_kernel(const uint16_t* __restrict__ qkv,
                                                            uint16_t* __restrict__ out, int R,
@@ -73,13 +82,22 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const uint16_t* __res
   const int c16 = lane & 15;      // column within a 16-wide tile
   const int g4 = lane >> 4;       // lane group 0..3
 
+  // Workgroups go to the 8 XCDs round-robin; renumber them so that each XCD
+  // receives a contiguous run of (cell, KV head) groups and the K/V rows of a
+  // group are fetched into one L2 only.  Within a group the query blocks keep
+  // their order, longest first.
   const int nqb = (R + QB - 1) / QB;
-  const int q0 = (nqb - 1 - (int)blockIdx.x) * QB;   // longest blocks first
+  const int ny = (int)gridDim.y;
+  const int lin = xcd_remap((int)(blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z)),
+                            (int)(gridDim.x * gridDim.y * gridDim.z));
+  const int bx = lin % nqb;
+  const int by = (lin / nqb) % ny;
+  const int q0 = (nqb - 1 - bx) * QB;   // longest blocks first
   const int rep = Hq / Hkv;
   const int quads = rep >> 2;
-  const int kvh = (int)blockIdx.y / quads;
-  const int h = kvh * rep + ((int)blockIdx.y % quads) * 4 + wave;
-  const int g = (int)blockIdx.z;
+  const int kvh = by / quads;
+  const int h = kvh * rep + (by % quads) * 4 + wave;
+  const int g = lin / (nqb * ny);
   const int ld = (Hq + 2 * Hkv) * HD;
   const uint16_t* base = qkv + (size_t)g * R * ld;
   const uint16_t* Kp = base + (size_t)(Hq + kvh) * HD;
@@ -189,8 +207,11 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const uint16_t* __res
       }
     }
 
+    // Lane-local maxima decide whether to rescale: a query's maximum over its
+    // four lane groups crosses the threshold exactly when one lane's does, so
+    // the cross-group maximum is needed only inside the (rare) rescale.
     bool need_rescale = false;
-    float mnew[QT];
+    float mloc[QT];
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
       float mx = -INFINITY;
@@ -199,13 +220,13 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const uint16_t* __res
         mx = fmaxf(fmaxf(mx, s[kt][qt][0]), s[kt][qt][1]);
         mx = fmaxf(fmaxf(mx, s[kt][qt][2]), s[kt][qt][3]);
       }
-      mnew[qt] = max_over_groups(mx) * scale_log2;
-      need_rescale |= mnew[qt] > mref[qt] + RESCALE_LOG2;
+      mloc[qt] = mx;
+      need_rescale |= mx * scale_log2 > mref[qt] + RESCALE_LOG2;
     }
     if (__any(need_rescale)) {
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt) {
-        const float m2 = fmaxf(mref[qt], mnew[qt]);
+        const float m2 = fmaxf(mref[qt], max_over_groups(mloc[qt]) * scale_log2);
         const float corr = __builtin_amdgcn_exp2f(mref[qt] - m2);   // 0 on the first block
         mref[qt] = m2;
         osum[qt] *= corr;
