@@ -362,16 +362,7 @@ __global__ __launch_bounds__((BM / WTM) * (BN / WTN) * 64, 1) void gemm_bf16_ker
         f32x4 x1 = *(const f32x4*)(ep + r * EP_LD + lc);
         f32x4 x2 = *(const f32x4*)(ep + r * EP_LD + 32 + lc);
         if (row >= a.M || col >= a.N) continue;
-        if constexpr (EPI == EPI_SWIGLU) {
-          // 64-column packed blocks: 32 gate columns then the 32 up columns
-          // of the same outputs; output column = block * 32 + offset.
-          const int ocol = (col >> 6) * 32 + (col & 31);
-          float u[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) u[e] = x1[e] / (1.0f + __expf(-x1[e])) * x2[e];
-          *(u32x2*)(C + (size_t)row * a.ld_out + ocol) =
-              u32x2{pack_bf16(u[0], u[1]), pack_bf16(u[2], u[3])};
-        } else {
+        {
           // RoPE, rotate-half: column c < hd/2 of a head pairs with c + hd/2.
           if (col < a.rope_cols) {
             const float2* cs = a.rope + (size_t)row * (a.hd >> 1) + col % a.hd;
@@ -391,13 +382,51 @@ __global__ __launch_bounds__((BM / WTM) * (BN / WTN) * 64, 1) void gemm_bf16_ker
       lds_sync();
     };
     if constexpr (EPI == EPI_SWIGLU) {
+      // The packed weight interleaves 32 gate and 32 up columns per 64-column
+      // block, so the gate and up values of one output are element e of
+      // blocks t and t + 1 in the same lane: SwiGLU runs in registers and only
+      // its bf16 result, one 32 x 32 piece per block pair, goes through LDS.
+      // Staged rows are 64 bytes whose 16-byte chunks are XOR-swizzled by
+      // (row / 4) % 4, so the row-major read-back is bank-conflict free.
+      constexpr int PIECES = MI * (NI / 2);
+      static_assert(PIECES * 32 * 32 * 2 <= 32 * EP_LD * 4, "pieces fit the wave's region");
+      uint16_t* sp = (uint16_t*)ep;
 #pragma unroll
       for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int t = 0; t < NI; t += 2) {
-          stage(acc[i][t], 0);
-          stage(acc[i][t + 1], 1);
-          paired(i, t, t + 1);
+          uint16_t* piece = sp + (i * (NI / 2) + t / 2) * 1024;
+#pragma unroll
+          for (int e4 = 0; e4 < 4; ++e4) {
+            float u[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const float gv = acc[i][t][4 * e4 + q];
+              u[q] = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * acc[i][t + 1][4 * e4 + q];
+            }
+            const int chunk = e4 ^ ((r32 >> 2) & 3);
+            *(u32x2*)(piece + r32 * 32 + chunk * 8 + half_lane) =
+                u32x2{pack_bf16(u[0], u[1]), pack_bf16(u[2], u[3])};
+          }
+        }
+      lds_sync();
+      // Read-back: 4 lanes per 64-byte row, 16 rows per access.
+      const int rc = lane & 3;
+      uint16_t* C = (uint16_t*)tab.out_lo[g];
+      const int out_cols = a.N >> 1;
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int t = 0; t < NI; t += 2) {
+          const uint16_t* piece = sp + (i * (NI / 2) + t / 2) * 1024;
+          const int ocol = ((wcol0 + t * 32) >> 6) * 32 + rc * 8;
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int rr = 16 * h + (lane >> 2);
+            const u32x4 v = *(const u32x4*)(piece + rr * 32 + ((rc ^ ((rr >> 2) & 3)) * 8));
+            const int row = wrow0 + i * 32 + rr;
+            if (row < a.M && ocol < out_cols) *(u32x4*)(C + (size_t)row * a.ld_out + ocol) = v;
+          }
         }
     } else {  // EPI_QKV_ROPE: the wave's columns start on a head boundary
       // (WTN is a multiple of hd), so block t pairs with t + P, P = hd / 64.
