@@ -38,7 +38,16 @@ Readings where the pages are silent (each is listed in the design doc):
     memory rows included;
   - attention is causal over all R rows of the cell, scale 1/sqrt(hd),
     query head h reads KV head h // (Hq / Hkv);
-  - GELU is the exact erf form.
+  - GELU is the exact erf form;
+  - the encoder-layer cell of the *Implementation* sketch (a stack of
+    PyTorch ``nn.TransformerEncoderLayer`` modules whose argument values are
+    stripped from the page) is read as the pre-norm layer with a 4x
+    feed-forward: ``H = A + MHA(LN1(A))``, ``Y = H + FFN(LN2(H))``, where
+    LayerNorm is ``(x - mean) / sqrt(var + eps) * g + b`` (biased variance),
+    MHA projects with biases, attends over all R rows of the cell without a
+    mask (scale 1/sqrt(hd), one KV head per query head) and projects out with
+    a bias, and FFN is ``relu(z W1 + b1) W2 + b2``.  Dropout is the identity
+    at inference.
 
 Arithmetic is in the dtype of the inputs (float32 by default, float64 for
 the pins).  There is no blocking, fusion or reordering beyond the per-cell
@@ -55,6 +64,7 @@ from scipy.special import erf as _erf
 CELL_LINEAR_GELU = 0
 CELL_NORM_SWIGLU = 1
 CELL_LLAMA = 2
+CELL_ENCODER = 3
 
 
 # ---------------------------------------------------------------------------
@@ -115,6 +125,19 @@ def rms_norm(x: np.ndarray, g: np.ndarray, eps: float) -> np.ndarray:
     return x * (x.dtype.type(1.0) / np.sqrt(ms + x.dtype.type(eps))) * g.astype(x.dtype)
 
 
+def layer_norm(x: np.ndarray, g: np.ndarray, b: np.ndarray, eps: float) -> np.ndarray:
+    """Row-wise LayerNorm: (x - mean) / sqrt(var + eps) * g + b, with the
+    biased (population) variance of each row."""
+    mu = np.mean(x, axis=-1, keepdims=True)
+    xc = x - mu
+    var = np.mean(xc * xc, axis=-1, keepdims=True)
+    return xc / np.sqrt(var + x.dtype.type(eps)) * g.astype(x.dtype) + b.astype(x.dtype)
+
+
+def relu(z: np.ndarray) -> np.ndarray:
+    return np.maximum(z, z.dtype.type(0.0))
+
+
 def rope_rotate_half(x: np.ndarray, pos: np.ndarray, theta: float) -> np.ndarray:
     """Rotary position embedding in the rotate-half layout.
 
@@ -151,6 +174,21 @@ def causal_gqa_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray) -> np.ndar
         p = p / p.sum(axis=1, keepdims=True)
         out[:, h, :] = p @ v[:, j, :]
     return out.reshape(R, Hq * hd)
+
+
+def full_mha(q: np.ndarray, k: np.ndarray, v: np.ndarray) -> np.ndarray:
+    """softmax(q_h k_h^T / sqrt(hd)) v_h per head h, every row attending to
+    every row (no mask).  q, k, v: [R, H, hd] -> [R, H*hd]."""
+    R, H, hd = q.shape
+    scale = q.dtype.type(1.0 / math.sqrt(hd))
+    out = np.empty((R, H, hd), dtype=q.dtype)
+    for h in range(H):
+        s = (q[:, h, :] @ k[:, h, :].T) * scale
+        s = s - s.max(axis=1, keepdims=True)
+        p = np.exp(s)
+        p = p / p.sum(axis=1, keepdims=True)
+        out[:, h, :] = p @ v[:, h, :]
+    return out.reshape(R, H * hd)
 
 
 def swiglu(z: np.ndarray, wg: np.ndarray, wu: np.ndarray, wd: np.ndarray) -> np.ndarray:
@@ -191,6 +229,22 @@ def cell_llama(A: np.ndarray, w: Dict[str, np.ndarray], Hq: int, Hkv: int, hd: i
     return H + swiglu(rms_norm(H, w["g2"], eps), w["wg"], w["wu"], w["wd"])
 
 
+def cell_encoder(A: np.ndarray, w: Dict[str, np.ndarray], H: int, hd: int,
+                 eps: float) -> np.ndarray:
+    """Pre-norm encoder layer over the cell's R rows:
+    H = A + MHA(LN1(A));  Y = H + relu(LN2(H) W1 + b1) W2 + b2."""
+    R = A.shape[0]
+    z = layer_norm(A, w["ln1_g"], w["ln1_b"], eps)
+    qkv = z @ w["wqkv"] + w["bqkv"]
+    nq = H * hd
+    q = qkv[:, :nq].reshape(R, H, hd)
+    k = qkv[:, nq:2 * nq].reshape(R, H, hd)
+    v = qkv[:, 2 * nq:3 * nq].reshape(R, H, hd)
+    Hs = A + (full_mha(q, k, v) @ w["wo"] + w["bo"])
+    z2 = layer_norm(Hs, w["ln2_g"], w["ln2_b"], eps)
+    return Hs + (relu(z2 @ w["w1"] + w["b1"]) @ w["w2"] + w["b2"])
+
+
 def cell(cfg, w: Dict[str, np.ndarray], A: np.ndarray) -> np.ndarray:
     if cfg.cell == CELL_LINEAR_GELU:
         return cell_linear_gelu(A, w)
@@ -198,6 +252,8 @@ def cell(cfg, w: Dict[str, np.ndarray], A: np.ndarray) -> np.ndarray:
         return cell_norm_swiglu(A, w, cfg.eps)
     if cfg.cell == CELL_LLAMA:
         return cell_llama(A, w, cfg.Hq, cfg.Hkv, cfg.hd, cfg.eps, cfg.theta)
+    if cfg.cell == CELL_ENCODER:
+        return cell_encoder(A, w, cfg.Hq, cfg.hd, cfg.eps)
     raise ValueError(f"unknown cell kind {cfg.cell}")
 
 

@@ -27,6 +27,7 @@ import numpy as np
 CELL_LINEAR_GELU = 0
 CELL_NORM_SWIGLU = 1
 CELL_LLAMA = 2
+CELL_ENCODER = 3
 
 F32 = "f32"
 BF16 = "bf16"
@@ -35,6 +36,8 @@ BF16 = "bf16"
 _KIND = {
     "w": 1, "b": 2, "x0": 3, "mem0": 4, "wqkv": 5, "wo": 6, "wg": 7, "wu": 8,
     "wd": 9, "embed": 10, "tokens": 11, "gemm_a": 12, "gemm_b": 13,
+    "bqkv": 14, "bo": 15, "w1": 16, "b1": 17, "w2": 18, "b2": 19,
+    "ln1_g": 20, "ln1_b": 21, "ln2_g": 22, "ln2_b": 23,
 }
 
 
@@ -62,8 +65,10 @@ class RMTConfig:
     eps: float = 1e-5
     theta: float = 500000.0
     w_std: float = 0.02       # weight / embedding std (1B/8B-shaped cells)
-    x_std: float = 1.0        # input-embedding std (attention-free cell)
+    x_std: float = 1.0        # input-embedding std (cells that take rows directly)
     mem_std: float = 1.0      # initial memory std
+    b_std: float = 0.02       # encoder cell: bias std
+    ln_std: float = 0.1       # encoder cell: LayerNorm gain spread around 1, and shift std
 
     @property
     def R(self) -> int:
@@ -128,9 +133,26 @@ TINY_LLAMA_HD128 = RMTConfig(
     L=2, S=3, n=136, m=24, d=512, Hq=4, Hkv=1, hd=128, F=448, V=777,
     w_std=0.04, mem_std=0.04)
 
+# The encoder-layer cell of the skill page's Implementation sketch
+# (nn.TransformerEncoderLayer with a 4x feed-forward), at the 1B width and
+# 131,072 tokens, and two small grids (64- and 128-wide heads).
+ENCODER_1B = RMTConfig(
+    name="encoder1b_rmt_L16_S128", wid=5, cell=CELL_ENCODER, dtype=BF16,
+    L=16, S=128, n=1024, m=128, d=2048, Hq=32, Hkv=32, hd=64, F=8192,
+    w_std=0.02, x_std=1.0, mem_std=1.0)
+TINY_ENCODER = RMTConfig(
+    name="tiny_encoder", wid=40, cell=CELL_ENCODER, dtype=BF16,
+    L=3, S=4, n=200, m=40, d=256, Hq=4, Hkv=4, hd=64, F=1024,
+    w_std=0.05, x_std=1.0, mem_std=1.0)
+TINY_ENCODER_HD128 = RMTConfig(
+    name="tiny_encoder_hd128", wid=41, cell=CELL_ENCODER, dtype=BF16,
+    L=2, S=3, n=136, m=24, d=512, Hq=4, Hkv=4, hd=128, F=2048,
+    w_std=0.04, x_std=1.0, mem_std=1.0)
+
 PRESETS: Dict[str, RMTConfig] = {
     c.name: c for c in (TINY_LINEAR_GELU, NORM_SWIGLU_1B, LLAMA_1B, LLAMA_8B,
-                        TINY_SWIGLU, TINY_LLAMA, TINY_LLAMA_HD128)
+                        TINY_SWIGLU, TINY_LLAMA, TINY_LLAMA_HD128, ENCODER_1B,
+                        TINY_ENCODER, TINY_ENCODER_HD128)
 }
 
 
@@ -175,6 +197,24 @@ def layer_weights(cfg: RMTConfig, layer: int, seed: int = 0) -> Dict[str, np.nda
             "w": normal((d, d), 1.0 / math.sqrt(d), seed, cfg.wid, "w", layer, bf),
             "b": normal((d,), 0.1, seed, cfg.wid, "b", layer, bf),
         }
+    if cfg.cell == CELL_ENCODER:
+        # gains 1 + N(0, ln_std), shifts and biases drawn too, so that no term
+        # of the cell is zero
+        F, hd3 = cfg.F, 3 * cfg.Hq * cfg.hd
+        return {
+            "ln1_g": 1.0 + normal((d,), cfg.ln_std, seed, cfg.wid, "ln1_g", layer, bf),
+            "ln1_b": normal((d,), cfg.ln_std, seed, cfg.wid, "ln1_b", layer, bf),
+            "wqkv": normal((d, hd3), cfg.w_std, seed, cfg.wid, "wqkv", layer, bf),
+            "bqkv": normal((hd3,), cfg.b_std, seed, cfg.wid, "bqkv", layer, bf),
+            "wo": normal((cfg.Hq * cfg.hd, d), cfg.w_std, seed, cfg.wid, "wo", layer, bf),
+            "bo": normal((d,), cfg.b_std, seed, cfg.wid, "bo", layer, bf),
+            "ln2_g": 1.0 + normal((d,), cfg.ln_std, seed, cfg.wid, "ln2_g", layer, bf),
+            "ln2_b": normal((d,), cfg.ln_std, seed, cfg.wid, "ln2_b", layer, bf),
+            "w1": normal((d, F), cfg.w_std, seed, cfg.wid, "w1", layer, bf),
+            "b1": normal((F,), cfg.b_std, seed, cfg.wid, "b1", layer, bf),
+            "w2": normal((F, d), cfg.w_std, seed, cfg.wid, "w2", layer, bf),
+            "b2": normal((d,), cfg.b_std, seed, cfg.wid, "b2", layer, bf),
+        }
     out = {
         "g2": np.ones((d,), np.float32),
         "wg": normal((d, cfg.F), cfg.w_std, seed, cfg.wid, "wg", layer, bf),
@@ -216,7 +256,7 @@ def tokens(cfg: RMTConfig, seed: int = 0, S: Optional[int] = None) -> np.ndarray
 def input_embeddings(cfg: RMTConfig, seed: int = 0, S: Optional[int] = None) -> np.ndarray:
     """Segment inputs X(-1, s) as rows [T, d] for the cells that take
     embeddings directly.  A prefix is the first S*n rows of the full draw."""
-    assert cfg.cell in (CELL_LINEAR_GELU, CELL_NORM_SWIGLU)
+    assert cfg.cell in (CELL_LINEAR_GELU, CELL_NORM_SWIGLU, CELL_ENCODER)
     x = normal((cfg.T, cfg.d), cfg.x_std, seed, cfg.wid, "x0", 0, cfg.dtype == BF16)
     return x if S is None else x[: S * cfg.n].copy()
 

@@ -108,9 +108,9 @@ def identity_weights(cfg, seed=0):
     projection of every branch is zero."""
     ws = ri.all_weights(cfg, seed)
     for w in ws:
-        w["wd"] = np.zeros_like(w["wd"])
-        if "wo" in w:
-            w["wo"] = np.zeros_like(w["wo"])
+        for key in ("wd", "wo", "bo", "w2", "b2"):
+            if key in w:
+                w[key] = np.zeros_like(w[key])
     return ws
 
 
@@ -177,6 +177,40 @@ def torch_norm_swiglu_block(A, w, cfg):
     return (A + (F.silu(hn @ t(w["wg"])) * (hn @ t(w["wu"]))) @ t(w["wd"])).numpy()
 
 
+def torch_encoder_block(A, w, cfg):
+    """One torch ``nn.TransformerEncoderLayer`` -- the module the skill page's
+    Implementation sketch stacks -- built pre-norm with a ReLU feed-forward and
+    no dropout, in float64, loaded with the cell's weights (torch keeps Linear
+    weights as [out, in], hence the transposes)."""
+    t = lambda a: torch.from_numpy(np.asarray(a, np.float64))  # noqa: E731
+    layer = torch.nn.TransformerEncoderLayer(
+        d_model=cfg.d, nhead=cfg.Hq, dim_feedforward=cfg.F, dropout=0.0, activation="relu",
+        layer_norm_eps=cfg.eps, batch_first=True, norm_first=True, dtype=torch.float64)
+    layer.eval()
+    with torch.no_grad():
+        layer.self_attn.in_proj_weight.copy_(t(w["wqkv"]).T)
+        layer.self_attn.in_proj_bias.copy_(t(w["bqkv"]))
+        layer.self_attn.out_proj.weight.copy_(t(w["wo"]).T)
+        layer.self_attn.out_proj.bias.copy_(t(w["bo"]))
+        layer.linear1.weight.copy_(t(w["w1"]).T)
+        layer.linear1.bias.copy_(t(w["b1"]))
+        layer.linear2.weight.copy_(t(w["w2"]).T)
+        layer.linear2.bias.copy_(t(w["b2"]))
+        layer.norm1.weight.copy_(t(w["ln1_g"]))
+        layer.norm1.bias.copy_(t(w["ln1_b"]))
+        layer.norm2.weight.copy_(t(w["ln2_g"]))
+        layer.norm2.bias.copy_(t(w["ln2_b"]))
+        return layer(t(A)[None])[0].numpy()
+
+
+def torch_block(A, w, cfg):
+    if cfg.cell == ri.CELL_LLAMA:
+        return torch_llama_block(A, w, cfg)
+    if cfg.cell == ri.CELL_ENCODER:
+        return torch_encoder_block(A, w, cfg)
+    return torch_norm_swiglu_block(A, w, cfg)
+
+
 def pin_single_segment_against_torch(cfg, forward=orc.forward_sequential, seed=0, tol=1e-11):
     """S = 1 and L = 1: the whole sweep is one cell on [M(0,-1); X(-1,0)],
     i.e. one standard pre-norm block over R rows."""
@@ -194,7 +228,7 @@ def pin_single_segment_against_torch(cfg, forward=orc.forward_sequential, seed=0
         x0 = ri.input_embeddings(c1, seed)
         hid, mem = forward(c1, w, x0, mem0, dtype=np.float64)
         A = np.concatenate([mem0[0], x0], axis=0)
-        Y = torch_norm_swiglu_block(A, w[0], c1)
+        Y = torch_block(A, w[0], c1)
     assert normwise(hid, Y[:c1.n]) <= tol, normwise(hid, Y[:c1.n])
     assert normwise(mem[0], Y[c1.n:]) <= tol, normwise(mem[0], Y[c1.n:])
 
@@ -228,6 +262,23 @@ def pin_rms_norm(rms_norm=orc.rms_norm):
     # with g = 1 and eps -> 0 every row has unit root-mean-square
     y = rms_norm(x, np.ones(33), 0.0)
     assert np.allclose(np.sqrt(np.mean(y * y, axis=1)), 1.0, atol=1e-14)
+
+
+def pin_layer_norm(layer_norm=orc.layer_norm):
+    rng = np.random.default_rng(8)
+    x = rng.standard_normal((7, 33)) * 3.0 + 1.5
+    g = rng.standard_normal(33)
+    b = rng.standard_normal(33)
+    ref = F.layer_norm(torch.from_numpy(x), (33,), weight=torch.from_numpy(g),
+                       bias=torch.from_numpy(b), eps=1e-5).numpy()
+    assert np.max(np.abs(layer_norm(x, g, b, 1e-5) - ref)) <= 1e-13
+    # with g = 1, b = 0 and eps -> 0 every row has mean 0 and (population) variance 1
+    y = layer_norm(x, np.ones(33), np.zeros(33), 0.0)
+    assert np.allclose(np.mean(y, axis=1), 0.0, atol=1e-14)
+    assert np.allclose(np.mean(y * y, axis=1), 1.0, atol=1e-13)
+    # a constant added to a row leaves its normalised values unchanged (unlike RMSNorm)
+    shifted = layer_norm(x + rng.standard_normal((7, 1)) * 10.0, g, b, 1e-5)
+    assert np.allclose(shifted, layer_norm(x, g, b, 1e-5), atol=1e-12)
 
 
 def pin_rope(rope=orc.rope_rotate_half, theta=500000.0):
@@ -283,6 +334,40 @@ def pin_attention(attn=orc.causal_gqa_attention):
         assert np.allclose(out[0, h], v[0, h * Hkv // Hq], atol=1e-14)
 
 
+def full_attention_bruteforce(q, k, v):
+    """Per query, per key, with math.exp, every key visible."""
+    R, H, hd = q.shape
+    out = np.zeros((R, H, hd))
+    for h in range(H):
+        for i in range(R):
+            scores = [sum(q[i, h, c] * k[t, h, c] for c in range(hd)) / math.sqrt(hd)
+                      for t in range(R)]
+            mx = max(scores)
+            e = [math.exp(sc - mx) for sc in scores]
+            z = sum(e)
+            for c in range(hd):
+                out[i, h, c] = sum(e[t] * v[t, h, c] for t in range(R)) / z
+    return out.reshape(R, H * hd)
+
+
+def pin_full_attention(attn=orc.full_mha):
+    rng = np.random.default_rng(9)
+    R, H, hd = 6, 3, 4
+    q = rng.standard_normal((R, H, hd))
+    k = rng.standard_normal((R, H, hd))
+    v = rng.standard_normal((R, H, hd))
+    out = attn(q, k, v)
+    assert np.max(np.abs(out - full_attention_bruteforce(q, k, v))) <= 1e-13
+    ref = F.scaled_dot_product_attention(*(torch.from_numpy(a).transpose(0, 1)[None] for a in (q, k, v)),
+                                         is_causal=False)[0].transpose(0, 1).reshape(R, H * hd).numpy()
+    assert np.max(np.abs(out - ref)) <= 1e-13
+    # no mask: permuting the rows of q, k and v together permutes the output rows
+    perm = rng.permutation(R)
+    assert np.allclose(attn(q[perm], k[perm], v[perm]), out[perm], atol=1e-13)
+    # constant values come back unchanged
+    assert np.allclose(attn(q, k, np.full_like(v, -0.625)), -0.625, atol=1e-14)
+
+
 # ---------------------------------------------------------------------------
 # A short last segment (T not a multiple of n)
 # ---------------------------------------------------------------------------
@@ -328,7 +413,7 @@ def pin_short_single_segment_against_torch(cfg, n_short, forward=orc.forward_seq
     hid, mem = forward(c1, w, x, mem0, emb, dtype=np.float64)
     rows = emb[x] if c1.cell == ri.CELL_LLAMA else x
     A = np.concatenate([mem0[0], rows], axis=0)
-    Y = torch_llama_block(A, w[0], c1) if c1.cell == ri.CELL_LLAMA else torch_norm_swiglu_block(A, w[0], c1)
+    Y = torch_block(A, w[0], c1)
     assert hid.shape[0] == n_short
     assert normwise(hid, Y[:n_short]) <= tol, normwise(hid, Y[:n_short])
     assert normwise(mem[0], Y[n_short:]) <= tol, normwise(mem[0], Y[n_short:])

@@ -211,3 +211,75 @@ def test_mutation_short_tail_zero_padded(T):
     bad = _forward_short_tail_mistake(pad_tail=True)
     assert _fails(pins.pin_linear_gelu_bruteforce_ragged, T,
                   forward=lambda *a, **k: bad(*a, **{**k, "dtype": np.float64}))
+
+
+# ---------------------------------------------------------------------------
+# The encoder-layer cell
+# ---------------------------------------------------------------------------
+
+def _post_norm_encoder(A, w, H, hd, eps):
+    """The layer with norm_first=False: the norms follow the residual adds."""
+    R = A.shape[0]
+    qkv = A @ w["wqkv"] + w["bqkv"]
+    nq = H * hd
+    q, k, v = (qkv[:, i * nq:(i + 1) * nq].reshape(R, H, hd) for i in range(3))
+    Hs = orc.layer_norm(A + (orc.full_mha(q, k, v) @ w["wo"] + w["bo"]), w["ln1_g"], w["ln1_b"], eps)
+    return orc.layer_norm(Hs + (orc.relu(Hs @ w["w1"] + w["b1"]) @ w["w2"] + w["b2"]),
+                          w["ln2_g"], w["ln2_b"], eps)
+
+
+def test_mutation_encoder_post_norm(monkeypatch):
+    monkeypatch.setattr(orc, "cell_encoder", _post_norm_encoder)
+    assert _fails(pins.pin_single_segment_against_torch, ri.TINY_ENCODER)
+
+
+def test_mutation_layer_norm_without_shift(monkeypatch):
+    plain = orc.layer_norm
+    monkeypatch.setattr(orc, "layer_norm", lambda x, g, b, eps: plain(x, g, np.zeros_like(b), eps))
+    assert _fails(pins.pin_layer_norm, layer_norm=orc.layer_norm)
+    assert _fails(pins.pin_single_segment_against_torch, ri.TINY_ENCODER)
+
+
+def test_mutation_layer_norm_not_centred(monkeypatch):
+    def rms_like(x, g, b, eps):
+        return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps) * g + b
+    assert _fails(pins.pin_layer_norm, layer_norm=rms_like)
+    monkeypatch.setattr(orc, "layer_norm", rms_like)
+    assert _fails(pins.pin_single_segment_against_torch, ri.TINY_ENCODER)
+
+
+def test_mutation_layer_norm_unbiased_variance():
+    def unbiased(x, g, b, eps):
+        xc = x - np.mean(x, axis=-1, keepdims=True)
+        return xc / np.sqrt(np.var(x, axis=-1, ddof=1, keepdims=True) + eps) * g + b
+    assert _fails(pins.pin_layer_norm, layer_norm=unbiased)
+
+
+def test_mutation_encoder_attention_causal(monkeypatch):
+    causal = lambda q, k, v: orc.causal_gqa_attention(q, k, v)  # noqa: E731
+    assert _fails(pins.pin_full_attention, attn=causal)
+    monkeypatch.setattr(orc, "full_mha", causal)
+    assert _fails(pins.pin_single_segment_against_torch, ri.TINY_ENCODER)
+
+
+@pytest.mark.parametrize("bias", ["bqkv", "bo", "b1", "b2"])
+def test_mutation_encoder_dropped_bias(monkeypatch, bias):
+    plain = orc.cell_encoder
+
+    def dropped(A, w, H, hd, eps):
+        w = dict(w)
+        w[bias] = np.zeros_like(w[bias])
+        return plain(A, w, H, hd, eps)
+    monkeypatch.setattr(orc, "cell_encoder", dropped)
+    assert _fails(pins.pin_single_segment_against_torch, ri.TINY_ENCODER)
+
+
+def test_mutation_encoder_gelu_for_relu(monkeypatch):
+    monkeypatch.setattr(orc, "relu", orc.gelu_erf)
+    assert _fails(pins.pin_single_segment_against_torch, ri.TINY_ENCODER)
+
+
+def test_mutation_encoder_swapped_k_v(monkeypatch):
+    plain = orc.full_mha
+    monkeypatch.setattr(orc, "full_mha", lambda q, k, v: plain(q, v, k))
+    assert _fails(pins.pin_single_segment_against_torch, ri.TINY_ENCODER)

@@ -10,7 +10,8 @@ from oracle import rmt_oracle as orc
 
 import pins
 
-TINY_RESIDUAL = [ri.TINY_SWIGLU, ri.TINY_LLAMA, ri.TINY_LLAMA_HD128]
+TINY_RESIDUAL = [ri.TINY_SWIGLU, ri.TINY_LLAMA, ri.TINY_LLAMA_HD128, ri.TINY_ENCODER,
+                 ri.TINY_ENCODER_HD128]
 
 
 def test_linear_gelu_bruteforce_fp32():
@@ -60,6 +61,14 @@ def test_rope():
 
 def test_attention():
     pins.pin_attention()
+
+
+def test_layer_norm():
+    pins.pin_layer_norm()
+
+
+def test_full_attention():
+    pins.pin_full_attention()
 
 
 # ---------------------------------------------------------------------------
