@@ -49,13 +49,22 @@ extern "C" {
  *   NORM_SWIGLU  Y = A + SwiGLU_l(RMSNorm_l(A))                    (bf16 only)
  *   LLAMA        H = A + Attn_l(RMSNorm1_l(A)) Wo_l;
  *                Y = H + SwiGLU_l(RMSNorm2_l(H))                   (bf16 only)
+ *   ENCODER      H = A + MHA_l(LN1_l(A));
+ *                Y = H + relu(LN2_l(H) W1_l + b1_l) W2_l + b2_l    (bf16 only)
  * with RMSNorm(x) = x * rsqrt(mean(x^2) + eps) * g,
  * SwiGLU(z) = (silu(z Wg) * (z Wu)) Wd, and Attn causal over the cell's R
  * rows with grouped-query heads (query head h reads KV head h / (Hq/Hkv)),
- * rotate-half RoPE at positions 0..R-1 within the cell, scale 1/sqrt(hd). */
+ * rotate-half RoPE at positions 0..R-1 within the cell, scale 1/sqrt(hd).
+ * ENCODER is the layer the skill page's Implementation sketch stacks (torch
+ * nn.TransformerEncoderLayer; its argument values are stripped from the
+ * page, read here as pre-norm with a 4x ReLU feed-forward): LN(x) =
+ * (x - mean) / sqrt(var + eps) * g + beta with the biased variance, and
+ * MHA(z) = concat_h softmax(q_h k_h^T / sqrt(hd)) v_h Wo + bo over all R rows
+ * (no mask, n_kv_heads == n_heads) with [q k v] = z Wqkv + bqkv. */
 #define RMT_CELL_LINEAR_GELU 0
 #define RMT_CELL_NORM_SWIGLU 1
 #define RMT_CELL_LLAMA 2
+#define RMT_CELL_ENCODER 3
 
 /* Storage / arithmetic types. */
 #define RMT_F32 0
@@ -69,12 +78,13 @@ typedef struct rmt_config {
   int32_t n;           /* segment tokens                                      */
   int32_t m;           /* memory rows per layer                               */
   int32_t d;           /* model width                                         */
-  int32_t n_heads;     /* LLAMA: query heads Hq                               */
-  int32_t n_kv_heads;  /* LLAMA: key/value heads Hkv (Hq/Hkv a multiple of 4) */
-  int32_t head_dim;    /* LLAMA: hd, 64 or 128; Hq*hd == d                    */
-  int32_t ffn;         /* NORM_SWIGLU, LLAMA: SwiGLU width F                  */
+  int32_t n_heads;     /* LLAMA, ENCODER: query heads Hq                      */
+  int32_t n_kv_heads;  /* LLAMA: KV heads Hkv (Hq/Hkv 1, 2 or a multiple of 4);
+                          ENCODER: equal to n_heads                           */
+  int32_t head_dim;    /* LLAMA, ENCODER: hd, 64 or 128; Hq*hd == d           */
+  int32_t ffn;         /* NORM_SWIGLU, LLAMA: SwiGLU width F; ENCODER: W1 width */
   int32_t vocab;       /* LLAMA: embedding rows V                             */
-  float eps;           /* RMSNorm epsilon                                     */
+  float eps;           /* RMSNorm / LayerNorm epsilon                         */
   float rope_theta;    /* LLAMA: RoPE base                                    */
 } rmt_config;
 
@@ -83,13 +93,17 @@ typedef struct rmt_config {
  * device layout; the caller may free them afterwards -- except `embed`,
  * which the model keeps borrowing and must outlive it.  Element type of the
  * matrices: fp32 for RMT_F32 models; bf16 (or fp32, rounded to nearest even
- * while packing) for RMT_BF16 models, as given by `weight_dtype`.  Gains
- * g1, g2 and bias b are always fp32.  Unused fields may be NULL.
+ * while packing) for RMT_BF16 models, as given by `weight_dtype`.  Gains,
+ * shifts and biases (g1, g2, b, beta*, b*) are always fp32.  Unused fields
+ * may be NULL.
  *   LINEAR_GELU: w [L][d][d], b [L][d]
  *   NORM_SWIGLU: g2 [L][d], wg [L][d][F], wu [L][d][F], wd [L][F][d]
  *   LLAMA:       g1 [L][d], wqkv [L][d][(Hq+2Hkv)*hd] (columns: Q heads,
  *                then K heads, then V heads, hd each), wo [L][Hq*hd][d],
- *                g2, wg, wu, wd as above, embed [V][d] (bf16). */
+ *                g2, wg, wu, wd as above, embed [V][d] (bf16).
+ *   ENCODER:     g1, beta1 [L][d] (LN1), wqkv [L][d][3d] (Q, K, V heads as
+ *                for LLAMA), bqkv [L][3d], wo [L][d][d], bo [L][d], g2, beta2
+ *                [L][d] (LN2), w1 [L][d][F], b1 [L][F], w2 [L][F][d], b2 [L][d]. */
 typedef struct rmt_weights {
   int32_t weight_dtype;  /* RMT_F32 or RMT_BF16: element type of w/wqkv/wo/wg/wu/wd */
   const void* w;
@@ -102,6 +116,15 @@ typedef struct rmt_weights {
   const void* wu;
   const void* wd;
   const void* embed;
+  /* ENCODER */
+  const float* beta1;
+  const float* bqkv;
+  const float* bo;
+  const float* beta2;
+  const void* w1;
+  const float* b1;
+  const void* w2;
+  const float* b2;
 } rmt_weights;
 
 /* Outputs of a forward call (device pointers, caller-allocated), for each of
@@ -135,8 +158,9 @@ int32_t rmt_diag_schedule(int32_t L, int32_t S, int32_t* diag_ptr, int32_t* cell
  * hipStream_t; NULL = default stream) and waits for the packing to finish.
  * *out receives the handle.
  * Errors: RMT_EINVAL (bad sizes or NULL weights the cell needs),
- * RMT_EUNSUPPORTED (Hq/Hkv not a multiple of 4, hd not 64/128, widths not
- * multiples of 64, ...), RMT_ENOMEM, RMT_EHIP. */
+ * RMT_EUNSUPPORTED (Hq/Hkv not 1, 2 or a multiple of 4, an ENCODER with
+ * n_kv_heads != n_heads, hd not 64/128, widths not multiples of 64, ...),
+ * RMT_ENOMEM, RMT_EHIP. */
 int32_t rmt_model_create(const rmt_config* cfg, const rmt_weights* w, void* stream,
                          rmt_model** out);
 
@@ -204,7 +228,8 @@ int32_t rmt_model_check(rmt_model* model, int32_t* bad_tokens);
  * the model's stream after every launch (and one before the first), so the
  * time between consecutive events is one launch's duration on the stream.
  * rmt_model_stage_times synchronises the stream and returns, for each stage
- * (RMT_STAGE_*), the summed milliseconds, the number of launches, and the
+ * (RMT_STAGE_*; for ENCODER cells NORM1/NORM2 are the LayerNorms and
+ * GATEUP/DOWN the feed-forward's W1 and W2 products), the summed milliseconds, the number of launches, and the
  * algorithmic flops and HBM bytes of those launches (compulsory operand and
  * result traffic, no re-reads), then clears the totals.  Host arrays of
  * RMT_NUM_STAGES entries; any of them may be NULL. */
@@ -262,10 +287,19 @@ int32_t rmt_grouped_gemm(int32_t G, int32_t M, int32_t N, int32_t K, const void*
  *   qkv  device bf16 [G][R][(Hq+2Hkv)*hd]: per row the Q heads, then the K
  *        heads, then the V heads (RoPE, if any, already applied)
  *   out  device bf16 [G][R][Hq*hd]
- * 1 <= G <= 65535, R >= 1, hd in {64, 128}, Hq/Hkv a positive multiple of 4.
+ * 1 <= G <= 65535, R >= 1, hd in {64, 128}, Hq/Hkv 1, 2 or a positive
+ * multiple of 4.
  * Errors: RMT_EINVAL, RMT_EUNSUPPORTED (hd or head ratio), RMT_EHIP. */
 int32_t rmt_causal_attention(int32_t G, int32_t R, int32_t n_heads, int32_t n_kv_heads,
                              int32_t head_dim, const void* qkv, void* out, void* stream);
+
+/* Attention on its own, causal or not (causal != 0: the LLAMA cell's stage,
+ * as rmt_causal_attention; causal == 0: the ENCODER cell's, every row
+ * attending to all R rows of its cell), same layouts and types as
+ * rmt_causal_attention.  Hq/Hkv must be 1, 2 or a positive multiple of 4.
+ * Errors: RMT_EINVAL, RMT_EUNSUPPORTED (hd or head ratio), RMT_EHIP. */
+int32_t rmt_attention(int32_t G, int32_t R, int32_t n_heads, int32_t n_kv_heads,
+                      int32_t head_dim, int32_t causal, const void* qkv, void* out, void* stream);
 
 /* Thread-local description of the last error (empty string if none). */
 const char* rmt_last_error(void);

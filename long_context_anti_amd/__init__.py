@@ -13,13 +13,15 @@ from typing import Dict, Optional
 import numpy as np
 
 from . import _lib
-from ._lib import (RMT_BF16, RMT_CELL_LINEAR_GELU, RMT_CELL_LLAMA, RMT_CELL_NORM_SWIGLU, RMT_F32,
-                   STAGES, RmtConfig, RmtError, RmtOutput, RmtWeights, check, lib)
+from ._lib import (RMT_BF16, RMT_CELL_ENCODER, RMT_CELL_LINEAR_GELU, RMT_CELL_LLAMA,
+                   RMT_CELL_NORM_SWIGLU, RMT_F32, STAGES, RmtConfig, RmtError, RmtOutput, RmtWeights,
+                   check, lib)
 
 __all__ = [
     "RMTModel", "RmtError", "diag_schedule", "grouped_gemm", "pack_weight", "causal_attention",
-    "STAGES",
-    "RMT_CELL_LINEAR_GELU", "RMT_CELL_NORM_SWIGLU", "RMT_CELL_LLAMA", "RMT_F32", "RMT_BF16",
+    "attention", "STAGES",
+    "RMT_CELL_LINEAR_GELU", "RMT_CELL_NORM_SWIGLU", "RMT_CELL_LLAMA", "RMT_CELL_ENCODER", "RMT_F32",
+    "RMT_BF16",
 ]
 
 
@@ -67,9 +69,23 @@ def grouped_gemm(A, B, group_layer, C_out, stream=None) -> None:
     check(lib().rmt_grouped_gemm(G, M, N, K, _ptr(A), _ptr(B), gl, _ptr(C_out), _stream(stream)))
 
 
+def attention(qkv, out, n_heads: int, n_kv_heads: int, head_dim: int, causal: bool = True,
+              stream=None) -> None:
+    """Attention over G cells, causal or unmasked: qkv [G, R, (Hq+2Hkv)*hd] ->
+    out [G, R, Hq*hd], both bf16 device tensors."""
+    import torch
+    G, R, W = qkv.shape
+    assert W == (n_heads + 2 * n_kv_heads) * head_dim
+    assert out.shape == (G, R, n_heads * head_dim)
+    for t in (qkv, out):
+        assert t.dtype == torch.bfloat16 and t.is_contiguous()
+    check(lib().rmt_attention(G, R, n_heads, n_kv_heads, head_dim, int(bool(causal)), _ptr(qkv),
+                              _ptr(out), _stream(stream)))
+
+
 def causal_attention(qkv, out, n_heads: int, n_kv_heads: int, head_dim: int, stream=None) -> None:
-    """Causal GQA attention over G cells: qkv [G, R, (Hq+2Hkv)*hd] -> out
-    [G, R, Hq*hd], both bf16 device tensors."""
+    """Causal GQA attention over G cells (rmt_causal_attention): qkv
+    [G, R, (Hq+2Hkv)*hd] -> out [G, R, Hq*hd], both bf16 device tensors."""
     import torch
     G, R, W = qkv.shape
     assert W == (n_heads + 2 * n_kv_heads) * head_dim
@@ -82,10 +98,12 @@ def causal_attention(qkv, out, n_heads: int, n_kv_heads: int, head_dim: int, str
 
 class RMTModel:
     """A model handle (rmt_model_create).  `weights` maps the rmt_weights field
-    names (w, b, g1, wqkv, wo, g2, wg, wu, wd, embed) to contiguous device
-    tensors in the mathematical layout, stacked over layers."""
+    names (w, b, g1, wqkv, wo, g2, wg, wu, wd, embed, and for the encoder cell
+    beta1, bqkv, bo, beta2, w1, b1, w2, b2) to contiguous device tensors in the
+    mathematical layout, stacked over layers."""
 
-    _FIELDS = ("w", "b", "g1", "wqkv", "wo", "g2", "wg", "wu", "wd", "embed")
+    _FIELDS = ("w", "b", "g1", "wqkv", "wo", "g2", "wg", "wu", "wd", "embed",
+               "beta1", "bqkv", "bo", "beta2", "w1", "b1", "w2", "b2")
 
     def __init__(self, *, cell: int, dtype: int, L: int, S: int, n: int, m: int, d: int,
                  n_heads: int = 0, n_kv_heads: int = 0, head_dim: int = 0, ffn: int = 0,
@@ -94,7 +112,8 @@ class RMTModel:
         import torch
         self.cfg = RmtConfig(cell, dtype, L, S, n, m, d, n_heads, n_kv_heads, head_dim, ffn, vocab,
                              eps, rope_theta)
-        big = [weights[k] for k in ("w", "wqkv", "wo", "wg", "wu", "wd") if weights.get(k) is not None]
+        big = [weights[k] for k in ("w", "wqkv", "wo", "wg", "wu", "wd", "w1", "w2")
+               if weights.get(k) is not None]
         wdt = RMT_BF16 if big and big[0].dtype == torch.bfloat16 else RMT_F32
         for t in weights.values():
             if t is not None:

@@ -20,6 +20,7 @@ RMT_ENOMEM = -4
 RMT_CELL_LINEAR_GELU = 0
 RMT_CELL_NORM_SWIGLU = 1
 RMT_CELL_LLAMA = 2
+RMT_CELL_ENCODER = 3
 RMT_F32 = 0
 RMT_BF16 = 1
 
@@ -41,6 +42,8 @@ class RmtWeights(C.Structure):
         ("weight_dtype", C.c_int32), ("w", C.c_void_p), ("b", C.c_void_p), ("g1", C.c_void_p),
         ("wqkv", C.c_void_p), ("wo", C.c_void_p), ("g2", C.c_void_p), ("wg", C.c_void_p),
         ("wu", C.c_void_p), ("wd", C.c_void_p), ("embed", C.c_void_p),
+        ("beta1", C.c_void_p), ("bqkv", C.c_void_p), ("bo", C.c_void_p), ("beta2", C.c_void_p),
+        ("w1", C.c_void_p), ("b1", C.c_void_p), ("w2", C.c_void_p), ("b2", C.c_void_p),
     ]
 
 
@@ -72,6 +75,8 @@ SIGNATURES = {
                                      C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p]),
     "rmt_causal_attention": (C.c_int32, [C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32,
                                          C.c_void_p, C.c_void_p, C.c_void_p]),
+    "rmt_attention": (C.c_int32, [C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32,
+                                  C.c_void_p, C.c_void_p, C.c_void_p]),
     "rmt_last_error": (C.c_char_p, []),
 }
 

@@ -1,13 +1,15 @@
-// Causal grouped-query attention inside each cell of a diagonal (gfx950).
-//
-// A cell (l, s) attends over its own R = m + n rows [memory; segment] with a
-// lower-triangular mask; query head h reads KV head h / (Hq / Hkv).  All
+// Attention inside each cell of a diagonal (gfx950): a cell (l, s) attends
+// over its own R = m + n rows [memory; segment], either causally (lower-
+// triangular mask: the LLaMA-shaped cell) or with every row seeing every row
+// (the encoder-layer cell); query head h reads KV head h / (Hq / Hkv).  All
 // cells of a diagonal are covered by one launch (grid z = cell).
 //
-// One workgroup = 4 wave64s = 4 query heads that share one KV head, over a
-// block of QB query rows.  K and V blocks of 64 keys go through a two-slot LDS
+// One workgroup = 4 wave64s that share one KV head: 4 of its query heads over
+// one block of QB query rows when Hq / Hkv is a multiple of 4, 2 heads x 2
+// query blocks when it is 2, one head x 4 query blocks when it is 1 (plain
+// multi-head attention).  K and V blocks of 64 keys go through a two-slot LDS
 // ring (the next block is fetched into registers while the current one is
-// used) and are shared by the 4 heads.
+// used) and are shared by the 4 waves.
 //
 // Per 64-key block each wave computes transposed scores S^T = K Q^T with
 // v_mfma_f32_16x16x32_bf16: the S^T accumulator layout is exactly the
@@ -62,7 +64,7 @@ __device__ __forceinline__ int xcd_remap(int bid, int nb) {
   return xcd * per + (xcd < rem ? xcd : rem) + idx;
 }
 
-template <int HD, int QB>
+template <int HD, int QB, bool CAUSAL>
 __global__ __launch_bounds__(256, 2) void attention_kernel(const uint16_t* __restrict__ qkv,
                                                            uint16_t* __restrict__ out, int R,
                                                            int Hq, int Hkv, float scale_log2) {
@@ -82,22 +84,27 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const uint16_t* __res
   const int c16 = lane & 15;      // column within a 16-wide tile
   const int g4 = lane >> 4;       // lane group 0..3
 
+  // The workgroup's waves: hw query heads of one KV head x qw query blocks.
+  const int rep = Hq / Hkv;
+  const int hw = rep >= 4 ? 4 : rep;
+  const int qw = 4 / hw;
+  const int hgroups = rep / hw;                 // workgroups per KV head along y
   // Workgroups go to the 8 XCDs round-robin; renumber them so that each XCD
   // receives a contiguous run of (cell, KV head) groups and the K/V rows of a
   // group are fetched into one L2 only.  Within a group the query blocks keep
   // their order, longest first.
   const int nqb = (R + QB - 1) / QB;
+  const int nqg = (nqb + qw - 1) / qw;          // groups of qw query blocks (grid x)
   const int ny = (int)gridDim.y;
   const int lin = xcd_remap((int)(blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z)),
                             (int)(gridDim.x * gridDim.y * gridDim.z));
-  const int bx = lin % nqb;
-  const int by = (lin / nqb) % ny;
-  const int q0 = (nqb - 1 - bx) * QB;   // longest blocks first
-  const int rep = Hq / Hkv;
-  const int quads = rep >> 2;
-  const int kvh = by / quads;
-  const int h = kvh * rep + (by % quads) * 4 + wave;
-  const int g = lin / (nqb * ny);
+  const int bx = lin % nqg;
+  const int by = (lin / nqg) % ny;
+  const int qg0 = (nqg - 1 - bx) * qw * QB;    // the workgroup's first query row
+  const int q0 = qg0 + (wave / hw) * QB;        // this wave's query block (may start at or past R)
+  const int kvh = by / hgroups;
+  const int h = kvh * rep + (by % hgroups) * hw + wave % hw;
+  const int g = lin / (nqg * ny);
   const int ld = (Hq + 2 * Hkv) * HD;
   const uint16_t* base = qkv + (size_t)g * R * ld;
   const uint16_t* Kp = base + (size_t)(Hq + kvh) * HD;
@@ -163,7 +170,8 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const uint16_t* __res
     }
   };
 
-  const int kend = min(q0 + QB, R);          // keys needed: [0, kend)
+  // keys needed by any of the workgroup's query rows: [0, kend)
+  const int kend = CAUSAL ? min(qg0 + qw * QB, R) : R;
   const int nkb = (kend + KB - 1) / KB;
   fetch(0);
   stash(0);
@@ -193,7 +201,10 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const uint16_t* __res
           s[kt][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[qt][ks], s[kt][qt], 0, 0, 0);
       }
 
-    if ((k0 + KB - 1 > q0) || (k0 + KB > R)) {   // block touches the diagonal or the end
+    // Masked scores: keys past the cell's end and, when causal, keys after
+    // the query.  (A causal block wholly after this wave's rows masks them
+    // all: its probabilities are exactly zero.)
+    if ((CAUSAL && k0 + KB - 1 > q0) || (k0 + KB > R)) {   // wave-uniform
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt) {
         const int q = q0 + 16 * qt + c16;
@@ -202,7 +213,7 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const uint16_t* __res
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const int key = k0 + 16 * kt + 4 * g4 + j;
-            if (key > q || key >= R) s[kt][qt][j] = -INFINITY;
+            if ((CAUSAL && key > q) || key >= R) s[kt][qt][j] = -INFINITY;
           }
       }
     }
@@ -309,20 +320,25 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const uint16_t* __res
 }  // namespace
 
 hipError_t launch_attention(const uint16_t* qkv, uint16_t* out, int G, int R, int Hq, int Hkv,
-                            int hd, hipStream_t stream) {
+                            int hd, bool causal, hipStream_t stream) {
   if (G == 0 || R == 0) return hipSuccess;
+  const int rep = Hq / Hkv;
+  if (Hkv < 1 || Hq % Hkv != 0 || !(rep == 1 || rep == 2 || rep % 4 == 0)) return hipErrorInvalidValue;
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)hd);
-  const int quads = (Hq / Hkv) / 4;
+  constexpr int QB = 32;   // measured faster than 64: lower register use, more waves
+  const int hw = rep >= 4 ? 4 : rep;
+  const int qw = 4 / hw;
+  const int nqb = (R + QB - 1) / QB;
+  const dim3 grid((nqb + qw - 1) / qw, Hkv * (rep / hw), G);
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, grid, dim3(256), 0, stream, qkv, out, R, Hq, Hkv, scale_log2);
+  };
   if (hd == 64) {
-    constexpr int QB = 32;   // measured faster than 64: lower register use, more waves
-    dim3 grid((R + QB - 1) / QB, Hkv * quads, G);
-    hipLaunchKernelGGL((attention_kernel<64, QB>), grid, dim3(256), 0, stream, qkv, out, R, Hq,
-                       Hkv, scale_log2);
+    if (causal) go(attention_kernel<64, QB, true>);
+    else go(attention_kernel<64, QB, false>);
   } else if (hd == 128) {
-    constexpr int QB = 32;
-    dim3 grid((R + QB - 1) / QB, Hkv * quads, G);
-    hipLaunchKernelGGL((attention_kernel<128, QB>), grid, dim3(256), 0, stream, qkv, out, R, Hq,
-                       Hkv, scale_log2);
+    if (causal) go(attention_kernel<128, QB, true>);
+    else go(attention_kernel<128, QB, false>);
   } else {
     return hipErrorInvalidValue;
   }

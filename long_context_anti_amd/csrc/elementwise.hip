@@ -25,12 +25,17 @@ __device__ __forceinline__ float wave_sum(float v) {
 // One wave per row, four rows per workgroup.  Row r of group g comes from
 // in_lo[g] (r < split_in) or in_hi[g]; the normalised row goes to the packed
 // bf16 matrix at row g*R + r.  Rows of up to 64*4*VPL elements stay in
-// registers between the sum of squares and the scaling, so each input byte
-// is read once; wider rows take a second pass.  Requires d % 4 == 0.
-template <int VPL>
-__global__ __launch_bounds__(256) void rmsnorm_kernel(int total_rows, int R, int d, int split_in,
-                                                      GroupTable tab, const float* __restrict__ gamma,
-                                                      float eps, uint16_t* __restrict__ out) {
+// registers between the reductions and the scaling, so each input byte is
+// read once; wider rows take further passes.  Requires d % 4 == 0.
+//   LAYER = false: RMSNorm,   y = x * rsqrt(mean(x^2) + eps) * gamma
+//   LAYER = true:  LayerNorm, y = (x - mu) * rsqrt(mean((x - mu)^2) + eps) * gamma + beta
+// (the centred second pass keeps the variance accurate for rows with a
+// large mean).
+template <int VPL, bool LAYER>
+__global__ __launch_bounds__(256) void norm_kernel(int total_rows, int R, int d, int split_in,
+                                                   GroupTable tab, const float* __restrict__ gamma,
+                                                   const float* __restrict__ beta, float eps,
+                                                   uint16_t* __restrict__ out) {
   const int lane = (int)threadIdx.x & 63;
   const int row = (int)blockIdx.x * 4 + ((int)threadIdx.x >> 6);
   if (row >= total_rows) return;
@@ -39,9 +44,9 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(int total_rows, int R, int
   const float* src = r < split_in ? (const float*)tab.in_lo[g] + (size_t)r * d
                                   : (const float*)tab.in_hi[g] + (size_t)(r - split_in) * d;
   const float* gm = gamma + (size_t)tab.layer[g] * d;
+  const float* bt = LAYER ? beta + (size_t)tab.layer[g] * d : nullptr;
   uint16_t* dst = out + (size_t)row * d;
   f32x4 v[VPL], w[VPL];
-  float ss = 0.f;
   // the row and its gamma are requested together, so the gamma latency
   // overlaps the row's instead of following the reduction
 #pragma unroll
@@ -50,21 +55,42 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(int total_rows, int R, int
     v[j] = c < d ? *(const f32x4*)(src + c) : f32x4{0.f, 0.f, 0.f, 0.f};
     w[j] = c < d ? *(const f32x4*)(gm + c) : f32x4{0.f, 0.f, 0.f, 0.f};
   }
+  float mu = 0.f;
+  if constexpr (LAYER) {
+    float s = 0.f;
 #pragma unroll
-  for (int j = 0; j < VPL; ++j)
-    ss += v[j][0] * v[j][0] + v[j][1] * v[j][1] + v[j][2] * v[j][2] + v[j][3] * v[j][3];
+    for (int j = 0; j < VPL; ++j) s += (v[j][0] + v[j][1]) + (v[j][2] + v[j][3]);
+    for (int c = (lane + 64 * VPL) * 4; c < d; c += 256) {
+      const f32x4 x = *(const f32x4*)(src + c);
+      s += (x[0] + x[1]) + (x[2] + x[3]);
+    }
+    mu = wave_sum(s) / (float)d;
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < VPL; ++j) {
+    const int c = (lane + 64 * j) * 4;
+    if (!LAYER || c < d) {   // padding lanes hold zeros, which LayerNorm would centre
+      const f32x4 x = v[j] - mu;
+      ss += x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3];
+    }
+  }
   for (int c = (lane + 64 * VPL) * 4; c < d; c += 256) {
-    const f32x4 x = *(const f32x4*)(src + c);
+    const f32x4 x = *(const f32x4*)(src + c) - mu;
     ss += x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3];
   }
   ss = wave_sum(ss);
   const float inv = 1.0f / sqrtf(ss / (float)d + eps);
   auto emit = [&](int c, const f32x4& x, const f32x4& gw) __attribute__((always_inline)) {
+    f32x4 y;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) y[e] = (x[e] - mu) * inv * gw[e];
+    if constexpr (LAYER) y += *(const f32x4*)(bt + c);
     u16x4 o;
-    o[0] = to_bf16(x[0] * inv * gw[0]);
-    o[1] = to_bf16(x[1] * inv * gw[1]);
-    o[2] = to_bf16(x[2] * inv * gw[2]);
-    o[3] = to_bf16(x[3] * inv * gw[3]);
+    o[0] = to_bf16(y[0]);
+    o[1] = to_bf16(y[1]);
+    o[2] = to_bf16(y[2]);
+    o[3] = to_bf16(y[3]);
     *(u16x4*)(dst + c) = o;
   };
 #pragma unroll
@@ -182,19 +208,31 @@ __global__ __launch_bounds__(256) void pack_kernel(int K, int N_src, const void*
 
 }  // namespace
 
-hipError_t launch_rmsnorm(int G, int R, int d, int split_in, const GroupTable& tab,
-                          const float* gamma, float eps, uint16_t* out, hipStream_t stream) {
+template <bool LAYER>
+hipError_t launch_norm(int G, int R, int d, int split_in, const GroupTable& tab, const float* gamma,
+                       const float* beta, float eps, uint16_t* out, hipStream_t stream) {
   const int rows = G * R;
   if (rows == 0) return hipSuccess;
   // 8 (16) float4 per lane keep rows of up to 2048 (4096) elements in
   // registers; the smaller variant leaves room for more waves per SIMD
   if (d <= 2048)
-    hipLaunchKernelGGL(rmsnorm_kernel<8>, dim3((rows + 3) / 4), dim3(256), 0, stream, rows, R, d,
-                       split_in, tab, gamma, eps, out);
+    hipLaunchKernelGGL((norm_kernel<8, LAYER>), dim3((rows + 3) / 4), dim3(256), 0, stream, rows, R,
+                       d, split_in, tab, gamma, beta, eps, out);
   else
-    hipLaunchKernelGGL(rmsnorm_kernel<16>, dim3((rows + 3) / 4), dim3(256), 0, stream, rows, R, d,
-                       split_in, tab, gamma, eps, out);
+    hipLaunchKernelGGL((norm_kernel<16, LAYER>), dim3((rows + 3) / 4), dim3(256), 0, stream, rows, R,
+                       d, split_in, tab, gamma, beta, eps, out);
   return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm(int G, int R, int d, int split_in, const GroupTable& tab,
+                          const float* gamma, float eps, uint16_t* out, hipStream_t stream) {
+  return launch_norm<false>(G, R, d, split_in, tab, gamma, nullptr, eps, out, stream);
+}
+
+hipError_t launch_layernorm(int G, int R, int d, int split_in, const GroupTable& tab,
+                            const float* gamma, const float* beta, float eps, uint16_t* out,
+                            hipStream_t stream) {
+  return launch_norm<true>(G, R, d, split_in, tab, gamma, beta, eps, out, stream);
 }
 
 hipError_t launch_gather_tokens(int n, int d, const int32_t* ids, int V, const uint16_t* embed,

@@ -259,7 +259,7 @@ __global__ __launch_bounds__((BM / WTM) * (BN / WTN) * 64, 1) void gemm_bf16_ker
   // through a private LDS region of the wave and read it back row-major, so
   // their stores cover whole row segments.  RoPE and SwiGLU pair their two
   // blocks inside one piece.
-  if constexpr (EPI != EPI_RESID_F32) {
+  if constexpr (EPI != EPI_RESID_F32 && EPI != EPI_RESID_BIAS_F32) {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();      // the ring is free once every wave is past its last slice
     asm volatile("" ::: "memory");
@@ -285,7 +285,30 @@ __global__ __launch_bounds__((BM / WTM) * (BN / WTN) * 64, 1) void gemm_bf16_ker
           f32x4{blk[4 * e4], blk[4 * e4 + 1], blk[4 * e4 + 2], blk[4 * e4 + 3]};
   };
 
-  if constexpr (EPI == EPI_RESID_F32) {
+  if constexpr (EPI == EPI_RESID_F32 || EPI == EPI_RESID_BIAS_F32) {
+    if constexpr (EPI == EPI_RESID_BIAS_F32) {
+      // The bias first (acc + b, then + residual): it depends on the column
+      // only, so one load per column group serves every row block.
+      // One 32-column block at a time (the empty asm keeps the compiler from
+      // hoisting every block's loads at once, which would spill).
+      const float* bl = a.bias + (size_t)tab.layer[g] * a.N;
+#pragma unroll
+      for (int t = 0; t < NI; ++t) {
+        f32x4 bv[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int col = wcol0 + t * 32 + 8 * q + half_lane;
+          bv[q] = col < a.N ? *(const f32x4*)(bl + col) : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[i][t][4 * q + e] += bv[q][e];
+        asm volatile("" ::: "memory");
+      }
+    }
     // Straight from the accumulator layout.  All residual loads of a 32-row
     // block are issued before any of its stores: the compiler cannot prove
     // that `out` does not alias `res`, and would otherwise wait out one full
@@ -322,7 +345,9 @@ __global__ __launch_bounds__((BM / WTM) * (BN / WTN) * 64, 1) void gemm_bf16_ker
           *(f32x4*)(out + col) = r;
         }
     }
-  } else if constexpr (EPI == EPI_STORE_BF16) {
+  } else if constexpr (EPI == EPI_STORE_BF16 || EPI == EPI_BIAS_BF16 || EPI == EPI_BIAS_RELU_BF16) {
+    constexpr bool BIAS = EPI != EPI_STORE_BF16;
+    const float* bl = BIAS ? a.bias + (size_t)tab.layer[g] * a.N : nullptr;
     // Row-major read-back: 16 lanes per 64-column row, 4 rows per access.
     const int lr = lane >> 4;
     const int lc = 4 * (lane & 15);
@@ -339,8 +364,16 @@ __global__ __launch_bounds__((BM / WTM) * (BN / WTN) * 64, 1) void gemm_bf16_ker
         for (int j = 0; j < 8; ++j) {
           const int r = 4 * j + lr;
           const int row = wrow0 + i * 32 + r;
-          const f32x4 v = *(const f32x4*)(ep + r * EP_LD + lc);
+          f32x4 v = *(const f32x4*)(ep + r * EP_LD + lc);
           if (row >= a.M || col >= a.N) continue;
+          if constexpr (BIAS) {
+            const f32x4 bv = *(const f32x4*)(bl + col);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              v[e] += bv[e];
+              if constexpr (EPI == EPI_BIAS_RELU_BF16) v[e] = fmaxf(v[e], 0.f);
+            }
+          }
           *(u32x2*)(C + (size_t)row * a.ld_out + col) = u32x2{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
         }
         lds_sync();
@@ -523,6 +556,9 @@ hipError_t launch_gemm_bf16(int epilogue, const GemmArgs& a, const GroupTable& t
     case EPI_QKV_ROPE: launch_epi<EPI_QKV_ROPE>(a, tab, stream); break;
     case EPI_SWIGLU: launch_epi<EPI_SWIGLU>(a, tab, stream); break;
     case EPI_RESID_F32: launch_epi<EPI_RESID_F32>(a, tab, stream); break;
+    case EPI_BIAS_BF16: launch_epi<EPI_BIAS_BF16>(a, tab, stream); break;
+    case EPI_BIAS_RELU_BF16: launch_epi<EPI_BIAS_RELU_BF16>(a, tab, stream); break;
+    case EPI_RESID_BIAS_F32: launch_epi<EPI_RESID_BIAS_F32>(a, tab, stream); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

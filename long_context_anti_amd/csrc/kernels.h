@@ -31,6 +31,9 @@ enum GemmEpilogue : int {
   EPI_QKV_ROPE = 1,    // C = bf16(rope(acc)) on Q/K columns, bf16(acc) on V
   EPI_SWIGLU = 2,      // gate/up interleaved in 32-column blocks: U = silu(g) * u
   EPI_RESID_F32 = 3,   // C = acc + residual, fp32, split row destinations
+  EPI_BIAS_BF16 = 4,        // C = bf16(acc + bias)
+  EPI_BIAS_RELU_BF16 = 5,   // C = bf16(max(acc + bias, 0))
+  EPI_RESID_BIAS_F32 = 6,   // C = residual + (acc + bias), fp32, split row destinations
 };
 
 struct GemmArgs {
@@ -44,6 +47,7 @@ struct GemmArgs {
   const float2* rope;  // EPI_QKV_ROPE: (cos, sin) table [M][hd/2]
   int rope_cols;       // EPI_QKV_ROPE: columns [0, rope_cols) are rotated
   int hd;              // EPI_QKV_ROPE: head dimension (64 or 128)
+  const float* bias;   // EPI_*BIAS*: fp32 [Lw][N], row layer[g] added to every output row
 };
 
 hipError_t launch_gemm_bf16(int epilogue, const GemmArgs& a, const GroupTable& tab,
@@ -52,6 +56,10 @@ hipError_t launch_gemm_bf16(int epilogue, const GemmArgs& a, const GroupTable& t
 // Row-wise RMSNorm of every group's R rows (fp32 in, bf16 out, packed).
 hipError_t launch_rmsnorm(int G, int R, int d, int split_in, const GroupTable& tab,
                           const float* gamma, float eps, uint16_t* out, hipStream_t stream);
+// Row-wise LayerNorm (gain gamma, shift beta, both [Lw][d]), same layout.
+hipError_t launch_layernorm(int G, int R, int d, int split_in, const GroupTable& tab,
+                            const float* gamma, const float* beta, float eps, uint16_t* out,
+                            hipStream_t stream);
 
 // X(-1, s) rows -> fp32 slot: token-id lookup (bf16 table) or a row copy.
 hipError_t launch_gather_tokens(int n, int d, const int32_t* ids, int V, const uint16_t* embed,
@@ -59,9 +67,10 @@ hipError_t launch_gather_tokens(int n, int d, const int32_t* ids, int V, const u
 hipError_t launch_copy_rows_bf16(int n, int d, const uint16_t* src, float* dst,
                                  hipStream_t stream);
 
-// Causal grouped-query attention over each group's R rows.
+// Attention over each group's R rows, causal or unmasked; Hq / Hkv must be
+// 1, 2 or a multiple of 4.
 hipError_t launch_attention(const uint16_t* qkv, uint16_t* out, int G, int R, int Hq, int Hkv,
-                            int hd, hipStream_t stream);
+                            int hd, bool causal, hipStream_t stream);
 
 // fp32 linear + bias + GELU cell with the split write-back.
 hipError_t launch_linear_gelu_f32(int G, int R, int d, int split_in, int split_out,

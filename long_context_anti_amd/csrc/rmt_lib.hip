@@ -80,6 +80,13 @@ struct rmt_model {
   uint16_t* wd = nullptr;
   float* g1 = nullptr;
   float* g2 = nullptr;
+  // ENCODER: LayerNorm shifts and biases (fp32, [L][width])
+  float* beta1 = nullptr;
+  float* beta2 = nullptr;
+  float* bqkv = nullptr;
+  float* bo = nullptr;
+  float* b1 = nullptr;
+  float* b2 = nullptr;
   float* w32 = nullptr;    // LINEAR_GELU: [L][d][d]
   float* b32 = nullptr;    // LINEAR_GELU: [L][d]
   const uint16_t* embed = nullptr;  // borrowed
@@ -110,6 +117,14 @@ namespace {
 
 int nqkv(const rmt_config& c) { return (c.n_heads + 2 * c.n_kv_heads) * c.head_dim; }
 
+bool has_attention(const rmt_config& c) { return c.cell == RMT_CELL_LLAMA || c.cell == RMT_CELL_ENCODER; }
+
+bool head_ratio_ok(int Hq, int Hkv) {
+  if (Hkv < 1 || Hq < 1 || Hq % Hkv != 0) return false;
+  const int rep = Hq / Hkv;
+  return rep == 1 || rep == 2 || rep % 4 == 0;
+}
+
 int32_t validate_config(const rmt_config* c) {
   if (!c) return fail(RMT_EINVAL, "config is NULL");
   if (c->L < 1 || c->S < 1 || c->n < 1 || c->m < 1 || c->d < 1)
@@ -121,7 +136,7 @@ int32_t validate_config(const rmt_config* c) {
     if ((int64_t)c->L * R * c->d > INT32_MAX) return fail(RMT_EINVAL, "sizes overflow int32");
     return RMT_OK;
   }
-  if (c->cell != RMT_CELL_NORM_SWIGLU && c->cell != RMT_CELL_LLAMA)
+  if (c->cell != RMT_CELL_NORM_SWIGLU && c->cell != RMT_CELL_LLAMA && c->cell != RMT_CELL_ENCODER)
     return fail(RMT_EINVAL, "unknown cell kind %d", c->cell);
   if (c->dtype != RMT_BF16) return fail(RMT_EUNSUPPORTED, "this cell kind runs in bf16 only");
   if (c->d % 64 != 0) return fail(RMT_EUNSUPPORTED, "d must be a multiple of 64 (got %d)", c->d);
@@ -129,18 +144,22 @@ int32_t validate_config(const rmt_config* c) {
     return fail(RMT_EUNSUPPORTED, "ffn must be a positive multiple of 32 (got %d)", c->ffn);
   if (!(c->eps >= 0.f)) return fail(RMT_EINVAL, "eps must be >= 0");
   int64_t widest = std::max<int64_t>(c->d, c->ffn);
-  if (c->cell == RMT_CELL_LLAMA) {
+  if (has_attention(*c)) {
     if (c->n_heads < 1 || c->n_kv_heads < 1 || c->n_heads % c->n_kv_heads != 0)
       return fail(RMT_EINVAL, "n_heads must be a positive multiple of n_kv_heads");
-    if ((c->n_heads / c->n_kv_heads) % 4 != 0)
-      return fail(RMT_EUNSUPPORTED, "n_heads / n_kv_heads must be a multiple of 4");
+    if (c->cell == RMT_CELL_ENCODER && c->n_kv_heads != c->n_heads)
+      return fail(RMT_EUNSUPPORTED, "ENCODER cells have one KV head per query head");
+    if (!head_ratio_ok(c->n_heads, c->n_kv_heads))
+      return fail(RMT_EUNSUPPORTED, "n_heads / n_kv_heads must be 1, 2 or a multiple of 4");
     if (c->head_dim != 64 && c->head_dim != 128)
       return fail(RMT_EUNSUPPORTED, "head_dim must be 64 or 128 (got %d)", c->head_dim);
     if (c->n_heads * c->head_dim != c->d)
       return fail(RMT_EUNSUPPORTED, "n_heads * head_dim must equal d");
+    widest = std::max<int64_t>(widest, nqkv(*c));
+  }
+  if (c->cell == RMT_CELL_LLAMA) {
     if (c->vocab < 1) return fail(RMT_EINVAL, "vocab must be >= 1");
     if (!(c->rope_theta > 0.f)) return fail(RMT_EINVAL, "rope_theta must be > 0");
-    widest = std::max<int64_t>(widest, nqkv(*c));
   }
   if ((int64_t)c->L * R * 2 * widest > INT32_MAX) return fail(RMT_EINVAL, "sizes overflow int32");
   if ((int64_t)c->S * c->n * c->d > ((int64_t)1 << 40)) return fail(RMT_EINVAL, "sequence too long");
@@ -275,7 +294,7 @@ int32_t run_cells(rmt_model* M, const Cell* cells, int G, const void* tokens, co
     LAUNCH(launch_gemm_bf16(EPI_QKV_ROPE, ga, tab, M->stream));
     MARK(RMT_STAGE_QKV, 2.0 * rows * d * NQ, rows * d * 2 + G_ * NQ * d * 2 + rows * NQ * 2);
     // causal GQA attention inside each cell
-    LAUNCH(launch_attention(M->qkv, M->att, G, R, Hq, Hkv, hd, M->stream));
+    LAUNCH(launch_attention(M->qkv, M->att, G, R, Hq, Hkv, hd, true, M->stream));
     MARK(RMT_STAGE_ATTN, 2.0 * G_ * Hq * hd * (double)R * (R + 1), rows * NQ * 2 + rows * Hq * hd * 2);
     // O projection + residual A -> H
     for (int g = 0; g < G; ++g) packed_out[g] = M->hbuf + (size_t)g * R * d;
@@ -290,6 +309,48 @@ int32_t run_cells(rmt_model* M, const Cell* cells, int G, const void* tokens, co
     set_io(packed_lo, packed_lo, nullptr, nullptr);
     LAUNCH(launch_rmsnorm(G, R, d, R, tab, M->g2, c.eps, M->abuf, M->stream));
     MARK(RMT_STAGE_NORM2, 0.0, rows * d * 6);
+  } else if (c.cell == RMT_CELL_ENCODER) {
+    const int hd = c.head_dim, H = c.n_heads, NQ = nqkv(c);
+    // LayerNorm 1 of [M(l, s-1); X(l-1, s)]
+    set_io(in_lo, in_hi, nullptr, nullptr);
+    LAUNCH(launch_layernorm(G, R, d, m, tab, M->g1, M->beta1, c.eps, M->abuf, M->stream));
+    MARK(RMT_STAGE_NORM1, 0.0, rows * d * 6);
+    // Q, K, V projection + bias
+    for (int g = 0; g < G; ++g) packed_out[g] = M->qkv + (size_t)g * R * NQ;
+    set_io(nullptr, nullptr, packed_out, nullptr);
+    ga.A = M->abuf; ga.B = M->wqkv; ga.M = R; ga.N = NQ; ga.K = d;
+    ga.split_in = R; ga.split_out = R; ga.ld_res = 0; ga.ld_out = NQ; ga.bias = M->bqkv;
+    LAUNCH(launch_gemm_bf16(EPI_BIAS_BF16, ga, tab, M->stream));
+    MARK(RMT_STAGE_QKV, 2.0 * rows * d * NQ, rows * d * 2 + G_ * NQ * d * 2 + rows * NQ * 2);
+    // unmasked multi-head attention inside each cell
+    LAUNCH(launch_attention(M->qkv, M->att, G, R, H, H, hd, false, M->stream));
+    MARK(RMT_STAGE_ATTN, 4.0 * G_ * H * hd * (double)R * R, rows * NQ * 2 + rows * H * hd * 2);
+    // O projection + bias + residual A -> H
+    for (int g = 0; g < G; ++g) packed_out[g] = M->hbuf + (size_t)g * R * d;
+    set_io(in_lo, in_hi, packed_out, nullptr);
+    ga.A = M->att; ga.B = M->wo; ga.M = R; ga.N = d; ga.K = H * hd;
+    ga.split_in = m; ga.split_out = R; ga.ld_res = d; ga.ld_out = d; ga.bias = M->bo;
+    LAUNCH(launch_gemm_bf16(EPI_RESID_BIAS_F32, ga, tab, M->stream));
+    MARK(RMT_STAGE_OPROJ, 2.0 * rows * H * hd * d, rows * H * hd * 2 + G_ * d * H * hd * 2 + rows * d * 8);
+    // LayerNorm 2 of H
+    for (int g = 0; g < G; ++g) packed_lo[g] = M->hbuf + (size_t)g * R * d;
+    set_io(packed_lo, packed_lo, nullptr, nullptr);
+    LAUNCH(launch_layernorm(G, R, d, R, tab, M->g2, M->beta2, c.eps, M->abuf, M->stream));
+    MARK(RMT_STAGE_NORM2, 0.0, rows * d * 6);
+    // W1 + bias + ReLU -> U
+    for (int g = 0; g < G; ++g) packed_out[g] = M->ubuf + (size_t)g * R * F;
+    set_io(nullptr, nullptr, packed_out, nullptr);
+    ga.A = M->abuf; ga.B = M->wgu; ga.M = R; ga.N = F; ga.K = d;
+    ga.split_in = R; ga.split_out = R; ga.ld_res = 0; ga.ld_out = F; ga.bias = M->b1;
+    LAUNCH(launch_gemm_bf16(EPI_BIAS_RELU_BF16, ga, tab, M->stream));
+    MARK(RMT_STAGE_GATEUP, 2.0 * rows * d * F, rows * d * 2 + G_ * F * d * 2 + rows * F * 2);
+    // W2 + bias + residual H; rows [0, n) -> X(l, s), rows [n, R) -> M(l, s)
+    set_io(packed_lo, packed_lo, x_out, m_out);
+    ga.A = M->ubuf; ga.B = M->wd; ga.M = R; ga.N = d; ga.K = F;
+    ga.split_in = R; ga.split_out = ns; ga.ld_res = d; ga.ld_out = d; ga.bias = M->b2;
+    LAUNCH(launch_gemm_bf16(EPI_RESID_BIAS_F32, ga, tab, M->stream));
+    MARK(RMT_STAGE_DOWN, 2.0 * rows * F * d, rows * F * 2 + G_ * d * F * 2 + rows * d * 8);
+    return RMT_OK;
   } else {
     // NORM_SWIGLU: RMSNorm of [M(l, s-1); X(l-1, s)]
     set_io(in_lo, in_hi, nullptr, nullptr);
@@ -337,7 +398,7 @@ int32_t alloc_workspace(rmt_model* M, int B) {
   if (c.cell != RMT_CELL_LINEAR_GELU) {
     pieces.push_back({(void**)&M->abuf, rows * d * 2});
     pieces.push_back({(void**)&M->ubuf, rows * F * 2});
-    if (c.cell == RMT_CELL_LLAMA) {
+    if (has_attention(c)) {
       pieces.push_back({(void**)&M->qkv, rows * nqkv(c) * 2});
       pieces.push_back({(void**)&M->att, rows * (size_t)c.n_heads * c.head_dim * 2});
       pieces.push_back({(void**)&M->hbuf, rows * d * 4});
@@ -435,6 +496,12 @@ int32_t rmt_model_create(const rmt_config* cfg, const rmt_weights* w, void* stre
   if (c.cell == RMT_CELL_LINEAR_GELU) {
     if (!w->w || !w->b) return fail(RMT_EINVAL, "LINEAR_GELU needs w and b");
     if (w->weight_dtype != RMT_F32) return fail(RMT_EUNSUPPORTED, "LINEAR_GELU weights must be fp32");
+  } else if (c.cell == RMT_CELL_ENCODER) {
+    if (!w->g1 || !w->beta1 || !w->wqkv || !w->bqkv || !w->wo || !w->bo || !w->g2 || !w->beta2 ||
+        !w->w1 || !w->b1 || !w->w2 || !w->b2)
+      return fail(RMT_EINVAL, "ENCODER needs g1, beta1, wqkv, bqkv, wo, bo, g2, beta2, w1, b1, w2, b2");
+    if (w->weight_dtype != RMT_F32 && w->weight_dtype != RMT_BF16)
+      return fail(RMT_EINVAL, "weight_dtype must be RMT_F32 or RMT_BF16");
   } else {
     if (!w->g2 || !w->wg || !w->wu || !w->wd) return fail(RMT_EINVAL, "g2, wg, wu and wd are required");
     if (c.cell == RMT_CELL_LLAMA && (!w->g1 || !w->wqkv || !w->wo || !w->embed))
@@ -450,12 +517,26 @@ int32_t rmt_model_create(const rmt_config* cfg, const rmt_weights* w, void* stre
 
   // Carve one allocation.
   const size_t F = (size_t)c.ffn;
-  const size_t NQ = c.cell == RMT_CELL_LLAMA ? (size_t)nqkv(c) : 0;
-  const size_t HQD = c.cell == RMT_CELL_LLAMA ? (size_t)c.n_heads * c.head_dim : 0;
+  const size_t NQ = has_attention(c) ? (size_t)nqkv(c) : 0;
+  const size_t HQD = has_attention(c) ? (size_t)c.n_heads * c.head_dim : 0;
   std::vector<Piece> pieces;
   if (c.cell == RMT_CELL_LINEAR_GELU) {
     pieces.push_back({(void**)&M->w32, (size_t)L * d * d * 4});
     pieces.push_back({(void**)&M->b32, (size_t)L * d * 4});
+  } else if (c.cell == RMT_CELL_ENCODER) {
+    // W1 packed [L][F][d] in the `wgu` slot, W2 packed [L][d][F] in `wd`
+    pieces.push_back({(void**)&M->wgu, (size_t)L * F * d * 2});
+    pieces.push_back({(void**)&M->wd, (size_t)L * d * F * 2});
+    pieces.push_back({(void**)&M->wqkv, (size_t)L * NQ * d * 2});
+    pieces.push_back({(void**)&M->wo, (size_t)L * d * HQD * 2});
+    pieces.push_back({(void**)&M->g1, (size_t)L * d * 4});
+    pieces.push_back({(void**)&M->beta1, (size_t)L * d * 4});
+    pieces.push_back({(void**)&M->g2, (size_t)L * d * 4});
+    pieces.push_back({(void**)&M->beta2, (size_t)L * d * 4});
+    pieces.push_back({(void**)&M->bqkv, (size_t)L * NQ * 4});
+    pieces.push_back({(void**)&M->bo, (size_t)L * d * 4});
+    pieces.push_back({(void**)&M->b1, (size_t)L * F * 4});
+    pieces.push_back({(void**)&M->b2, (size_t)L * d * 4});
   } else {
     pieces.push_back({(void**)&M->wgu, (size_t)L * 2 * F * d * 2});
     pieces.push_back({(void**)&M->wd, (size_t)L * d * F * 2});
@@ -502,6 +583,21 @@ int32_t rmt_model_create(const rmt_config* cfg, const rmt_weights* w, void* stre
   if (c.cell == RMT_CELL_LINEAR_GELU) {
     CREATE_TRY(hipMemcpyAsync(M->w32, w->w, (size_t)L * d * d * 4, hipMemcpyDeviceToDevice, st));
     CREATE_TRY(hipMemcpyAsync(M->b32, w->b, (size_t)L * d * 4, hipMemcpyDeviceToDevice, st));
+  } else if (c.cell == RMT_CELL_ENCODER) {
+    const int bf = w->weight_dtype == RMT_BF16;
+    CREATE_TRY(launch_pack(L, d, (int)F, w->w1, nullptr, bf, 0, M->wgu, st));
+    CREATE_TRY(launch_pack(L, (int)F, d, w->w2, nullptr, bf, 0, M->wd, st));
+    CREATE_TRY(launch_pack(L, d, (int)NQ, w->wqkv, nullptr, bf, 0, M->wqkv, st));
+    CREATE_TRY(launch_pack(L, (int)HQD, d, w->wo, nullptr, bf, 0, M->wo, st));
+    const size_t Ld4 = (size_t)L * d * 4;
+    CREATE_TRY(hipMemcpyAsync(M->g1, w->g1, Ld4, hipMemcpyDeviceToDevice, st));
+    CREATE_TRY(hipMemcpyAsync(M->beta1, w->beta1, Ld4, hipMemcpyDeviceToDevice, st));
+    CREATE_TRY(hipMemcpyAsync(M->g2, w->g2, Ld4, hipMemcpyDeviceToDevice, st));
+    CREATE_TRY(hipMemcpyAsync(M->beta2, w->beta2, Ld4, hipMemcpyDeviceToDevice, st));
+    CREATE_TRY(hipMemcpyAsync(M->bqkv, w->bqkv, (size_t)L * NQ * 4, hipMemcpyDeviceToDevice, st));
+    CREATE_TRY(hipMemcpyAsync(M->bo, w->bo, Ld4, hipMemcpyDeviceToDevice, st));
+    CREATE_TRY(hipMemcpyAsync(M->b1, w->b1, (size_t)L * F * 4, hipMemcpyDeviceToDevice, st));
+    CREATE_TRY(hipMemcpyAsync(M->b2, w->b2, Ld4, hipMemcpyDeviceToDevice, st));
   } else {
     const int bf = w->weight_dtype == RMT_BF16;
     CREATE_TRY(launch_pack(L, d, (int)F, w->wg, w->wu, bf, 1, M->wgu, st));
@@ -743,16 +839,23 @@ int32_t rmt_grouped_gemm(int32_t G, int32_t Mr, int32_t N, int32_t K, const void
   return RMT_OK;
 }
 
-int32_t rmt_causal_attention(int32_t G, int32_t R, int32_t Hq, int32_t Hkv, int32_t hd,
-                             const void* qkv, void* out, void* stream) {
+int32_t rmt_attention(int32_t G, int32_t R, int32_t Hq, int32_t Hkv, int32_t hd, int32_t causal,
+                      const void* qkv, void* out, void* stream) {
   if (G < 1 || G > 65535 || R < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0)
     return fail(RMT_EINVAL, "need 1 <= G <= 65535, R >= 1 and n_heads a multiple of n_kv_heads");
   if (!qkv || !out) return fail(RMT_EINVAL, "qkv and out must be non-NULL");
   if (hd != 64 && hd != 128) return fail(RMT_EUNSUPPORTED, "head_dim must be 64 or 128");
-  if ((Hq / Hkv) % 4 != 0) return fail(RMT_EUNSUPPORTED, "n_heads / n_kv_heads must be a multiple of 4");
+  if (!head_ratio_ok(Hq, Hkv))
+    return fail(RMT_EUNSUPPORTED, "n_heads / n_kv_heads must be 1, 2 or a multiple of 4");
   if ((int64_t)G * R * (Hq + 2 * Hkv) * hd > ((int64_t)1 << 40)) return fail(RMT_EINVAL, "sizes too large");
-  HIP_TRY(launch_attention((const uint16_t*)qkv, (uint16_t*)out, G, R, Hq, Hkv, hd, (hipStream_t)stream));
+  HIP_TRY(launch_attention((const uint16_t*)qkv, (uint16_t*)out, G, R, Hq, Hkv, hd, causal != 0,
+                           (hipStream_t)stream));
   return RMT_OK;
+}
+
+int32_t rmt_causal_attention(int32_t G, int32_t R, int32_t Hq, int32_t Hkv, int32_t hd,
+                             const void* qkv, void* out, void* stream) {
+  return rmt_attention(G, R, Hq, Hkv, hd, 1, qkv, out, stream);
 }
 
 }  // extern "C"

@@ -22,6 +22,12 @@ def f32_tensor(arr: np.ndarray, device="cuda"):
     return torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32)).to(device)
 
 
+# generator key -> rmt_weights field (the encoder's LayerNorm parameters)
+_ABI_NAME = {"ln1_g": "g1", "ln1_b": "beta1", "ln2_g": "g2", "ln2_b": "beta2"}
+# fields the C ABI takes in fp32 whatever the model's dtype: gains, shifts, biases
+_FP32_FIELDS = {"g1", "g2", "b", "beta1", "beta2", "bqkv", "bo", "b1", "b2"}
+
+
 def device_weights(cfg: RMTConfig, layers: List[Dict[str, np.ndarray]],
                    embed: Optional[np.ndarray] = None, device="cuda") -> Dict[str, object]:
     """Stack per-layer weights and upload them.  Matrices go up as bf16 for
@@ -30,10 +36,11 @@ def device_weights(cfg: RMTConfig, layers: List[Dict[str, np.ndarray]],
     bf = cfg.dtype == BF16
     for key in layers[0]:
         stacked = np.stack([w[key] for w in layers])
-        if key in ("g1", "g2", "b") or not bf:
-            out[key] = f32_tensor(stacked, device)
+        name = _ABI_NAME.get(key, key)
+        if name in _FP32_FIELDS or not bf:
+            out[name] = f32_tensor(stacked, device)
         else:
-            out[key] = bf16_tensor(stacked, device)
+            out[name] = bf16_tensor(stacked, device)
         del stacked
     if cfg.cell == CELL_LLAMA:
         assert embed is not None

@@ -38,7 +38,11 @@ def test_linear_gelu_fp32():
     run.close()
 
 
-@pytest.mark.parametrize("cfg", [ri.TINY_SWIGLU, ri.TINY_LLAMA, ri.TINY_LLAMA_HD128],
+TINY_GQA2 = dataclasses.replace(ri.TINY_LLAMA, name="tiny_llama_gqa2", wid=32, Hq=4, Hkv=2)
+
+
+@pytest.mark.parametrize("cfg", [ri.TINY_SWIGLU, ri.TINY_LLAMA, ri.TINY_LLAMA_HD128, TINY_GQA2,
+                                 ri.TINY_ENCODER, ri.TINY_ENCODER_HD128],
                          ids=lambda c: c.name)
 def test_tiny_bf16(cfg):
     gu.say(f"[parity] {cfg.name} bf16 L={cfg.L} S={cfg.S} R={cfg.R} d={cfg.d}")
@@ -108,8 +112,8 @@ def test_bad_token_ids_are_flagged():
 
 
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("cfg,S", [(ri.NORM_SWIGLU_1B, 2), (ri.LLAMA_1B, 2)],
-                         ids=["norm_swiglu_1b_S2", "llama1b_S2"])
+@pytest.mark.parametrize("cfg,S", [(ri.NORM_SWIGLU_1B, 2), (ri.LLAMA_1B, 2), (ri.ENCODER_1B, 2)],
+                         ids=["norm_swiglu_1b_S2", "llama1b_S2", "encoder1b_S2"])
 def test_full_width_prefix(cfg, S):
     """The full-width workloads on a prefix of S segments (a prefix is exactly
     the first S segments of the full run: segment s never reads later ones)."""
@@ -160,6 +164,29 @@ def test_llama1b_full_length_teacher_forced():
     assert np.array_equal(hd, hs) and np.array_equal(md, ms)
     n = cfg.n
     for s in (0, 1, 64, cfg.S - 1):
+        m_in = _gpu_state_after(run, s)
+        m_out = md if s == cfg.S - 1 else _gpu_state_after(run, s + 1)
+        h_o, m_o = orc.forward_sequential(cfg, run.layers, run.x[s * n:(s + 1) * n], m_in, run.embed)
+        e_h = gu.rel_l2(hd[s * n:(s + 1) * n], h_o)
+        e_m = gu.rel_l2(m_out, m_o)
+        gu.say(f"  segment {s}: rel L2 hidden {e_h:.3e} mem {e_m:.3e}")
+        assert e_h <= BF16_TOL and e_m <= BF16_TOL
+    run.close()
+
+
+@pytest.mark.timeout(900)
+def test_encoder1b_full_length_teacher_forced():
+    """The encoder-layer workload over the full 131,072 tokens: diagonal ==
+    sequential bitwise, and segments across the run checked one step at a
+    time from the GPU's own state, as for the LLaMA-shaped sweep."""
+    cfg = ri.ENCODER_1B
+    gu.say(f"[parity] {cfg.name} full length S={cfg.S}: diagonal vs sequential, teacher-forced segments")
+    run = gu.GpuRun(cfg)
+    hd, md = run.run("diagonal")
+    hs, ms = run.run("sequential")
+    assert np.array_equal(hd, hs) and np.array_equal(md, ms)
+    n = cfg.n
+    for s in (0, 63, cfg.S - 1):
         m_in = _gpu_state_after(run, s)
         m_out = md if s == cfg.S - 1 else _gpu_state_after(run, s + 1)
         h_o, m_o = orc.forward_sequential(cfg, run.layers, run.x[s * n:(s + 1) * n], m_in, run.embed)

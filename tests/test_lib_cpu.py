@@ -86,7 +86,7 @@ def _cfg(**kw):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(L=0), -1), (dict(n=0), -1), (dict(head_dim=96, n_heads=2, d=192), -2),
-    (dict(n_kv_heads=2), -2), (dict(d=200), -2), (dict(ffn=100), -2), (dict(dtype=0), -2),
+    (dict(n_heads=6, n_kv_heads=2, d=384), -2), (dict(d=200), -2), (dict(ffn=100), -2), (dict(dtype=0), -2),
     (dict(cell=7), -1), (dict(vocab=0), -1), (dict(n_heads=3, n_kv_heads=2), -1),
 ])
 def test_model_create_rejects_bad_configs(kw, code):
@@ -106,6 +106,45 @@ def test_model_create_rejects_missing_weights():
     handle = C.c_void_p()
     assert L.lib().rmt_model_create(C.byref(cfg), C.byref(w), None, C.byref(handle)) == L.RMT_EINVAL
     assert b"LLAMA needs" in L.lib().rmt_last_error() or b"required" in L.lib().rmt_last_error()
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n_kv_heads=2), -2),                       # one KV head per query head
+    (dict(n_heads=4, n_kv_heads=4, head_dim=96, d=384), -2),
+    (dict(ffn=100), -2), (dict(dtype=0), -2), (dict(n_heads=3, n_kv_heads=3, d=256), -2),
+])
+def test_encoder_create_rejects_bad_configs(kw, code):
+    L = _lib()
+    base = dict(cell=L.RMT_CELL_ENCODER, n_heads=4, n_kv_heads=4, ffn=1024)
+    base.update(kw)
+    cfg = _cfg(**base)
+    w = L.RmtWeights()
+    handle = C.c_void_p()
+    rc = L.lib().rmt_model_create(C.byref(cfg), C.byref(w), None, C.byref(handle))
+    assert rc == code, L.lib().rmt_last_error()
+    assert not handle.value
+
+
+def test_encoder_create_rejects_missing_weights():
+    L = _lib()
+    cfg = _cfg(cell=L.RMT_CELL_ENCODER, n_heads=4, n_kv_heads=4, ffn=1024)
+    w = L.RmtWeights()
+    handle = C.c_void_p()
+    assert L.lib().rmt_model_create(C.byref(cfg), C.byref(w), None, C.byref(handle)) == L.RMT_EINVAL
+    assert b"ENCODER needs" in L.lib().rmt_last_error()
+
+
+def test_attention_rejects_bad_arguments():
+    L = _lib()
+    h = L.lib()
+    p = C.c_void_p(16)
+    assert h.rmt_attention(0, 64, 4, 4, 64, 0, p, p, None) == L.RMT_EINVAL
+    assert h.rmt_attention(1, 0, 4, 4, 64, 0, p, p, None) == L.RMT_EINVAL
+    assert h.rmt_attention(1, 64, 4, 3, 64, 0, p, p, None) == L.RMT_EINVAL      # 4 % 3 != 0
+    assert h.rmt_attention(1, 64, 6, 2, 64, 0, p, p, None) == L.RMT_EUNSUPPORTED  # ratio 3
+    assert h.rmt_attention(1, 64, 4, 4, 96, 0, p, p, None) == L.RMT_EUNSUPPORTED
+    assert h.rmt_attention(1, 64, 4, 4, 64, 0, None, p, None) == L.RMT_EINVAL
+    assert h.rmt_causal_attention(1, 64, 6, 2, 64, p, p, None) == L.RMT_EUNSUPPORTED
 
 
 def test_grouped_gemm_rejects_bad_shapes():
