@@ -46,14 +46,15 @@ __global__ __launch_bounds__(256) void norm_kernel(int total_rows, int R, int d,
   const float* gm = gamma + (size_t)tab.layer[g] * d;
   const float* bt = LAYER ? beta + (size_t)tab.layer[g] * d : nullptr;
   uint16_t* dst = out + (size_t)row * d;
-  f32x4 v[VPL], w[VPL];
-  // the row and its gamma are requested together, so the gamma latency
-  // overlaps the row's instead of following the reduction
+  f32x4 v[VPL], w[VPL], bb[LAYER ? VPL : 1];
+  // the row, its gamma (and beta) are requested together, so their latency
+  // overlaps the row's instead of following the reductions
 #pragma unroll
   for (int j = 0; j < VPL; ++j) {
     const int c = (lane + 64 * j) * 4;
     v[j] = c < d ? *(const f32x4*)(src + c) : f32x4{0.f, 0.f, 0.f, 0.f};
     w[j] = c < d ? *(const f32x4*)(gm + c) : f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (LAYER) bb[j] = c < d ? *(const f32x4*)(bt + c) : f32x4{0.f, 0.f, 0.f, 0.f};
   }
   float mu = 0.f;
   if constexpr (LAYER) {
@@ -81,11 +82,11 @@ __global__ __launch_bounds__(256) void norm_kernel(int total_rows, int R, int d,
   }
   ss = wave_sum(ss);
   const float inv = 1.0f / sqrtf(ss / (float)d + eps);
-  auto emit = [&](int c, const f32x4& x, const f32x4& gw) __attribute__((always_inline)) {
+  auto emit = [&](int c, const f32x4& x, const f32x4& gw, const f32x4& sh) __attribute__((always_inline)) {
     f32x4 y;
 #pragma unroll
     for (int e = 0; e < 4; ++e) y[e] = (x[e] - mu) * inv * gw[e];
-    if constexpr (LAYER) y += *(const f32x4*)(bt + c);
+    if constexpr (LAYER) y += sh;
     u16x4 o;
     o[0] = to_bf16(y[0]);
     o[1] = to_bf16(y[1]);
@@ -96,10 +97,11 @@ __global__ __launch_bounds__(256) void norm_kernel(int total_rows, int R, int d,
 #pragma unroll
   for (int j = 0; j < VPL; ++j) {
     const int c = (lane + 64 * j) * 4;
-    if (c < d) emit(c, v[j], w[j]);
+    if (c < d) emit(c, v[j], w[j], bb[LAYER ? j : 0]);
   }
   for (int c = (lane + 64 * VPL) * 4; c < d; c += 256)
-    emit(c, *(const f32x4*)(src + c), *(const f32x4*)(gm + c));
+    emit(c, *(const f32x4*)(src + c), *(const f32x4*)(gm + c),
+         LAYER ? *(const f32x4*)(bt + c) : f32x4{0.f, 0.f, 0.f, 0.f});
 }
 
 // Embedding lookup of one segment's n token ids into an fp32 slot.  An id

@@ -346,38 +346,60 @@ __global__ __launch_bounds__((BM / WTM) * (BN / WTN) * 64, 1) void gemm_bf16_ker
         }
     }
   } else if constexpr (EPI == EPI_STORE_BF16 || EPI == EPI_BIAS_BF16 || EPI == EPI_BIAS_RELU_BF16) {
+    // Bias and ReLU run on the accumulators (a lane's four consecutive
+    // columns share one 16-byte bias load, the same for every row block);
+    // each 32-row block of the wave's outputs is then staged as bf16 -- rows
+    // of WTN values whose 16-byte chunks are XOR-swizzled, so the staging
+    // writes of 32 rows spread over the banks -- and read back row-major for
+    // 16-byte stores.  Output columns come in whole 8-column chunks (the host
+    // requires N % 8 == 0).
     constexpr bool BIAS = EPI != EPI_STORE_BF16;
-    const float* bl = BIAS ? a.bias + (size_t)tab.layer[g] * a.N : nullptr;
-    // Row-major read-back: 16 lanes per 64-column row, 4 rows per access.
-    const int lr = lane >> 4;
-    const int lc = 4 * (lane & 15);
+    constexpr int OCH = WTN / 8;                  // 16-byte chunks per staged row
+    static_assert(32 * WTN * 2 <= 32 * EP_LD * 4, "a staged row block fits the wave's region");
+    auto swz_o = [](int r) { return OCH == 8 ? ((r >> 1) & 7) : (r & (OCH - 1)); };
+    uint16_t* sp = (uint16_t*)ep;
+    uint16_t* C = (uint16_t*)tab.out_lo[g];
+    f32x4 bv[BIAS ? NI : 1][4];
+    if constexpr (BIAS) {
+      const float* bl = a.bias + (size_t)tab.layer[g] * a.N;
 #pragma unroll
-    for (int i = 0; i < MI; ++i)
+      for (int t = 0; t < NI; ++t)
 #pragma unroll
-      for (int t = 0; t < NI; t += 2) {
-        stage(acc[i][t], 0);
-        stage(acc[i][t + 1], 1);
-        lds_sync();
-        const int col = wcol0 + t * 32 + lc;
-        uint16_t* C = (uint16_t*)tab.out_lo[g];
+        for (int e4 = 0; e4 < 4; ++e4) {
+          const int col = wcol0 + t * 32 + 8 * e4 + half_lane;
+          bv[t][e4] = col < a.N ? *(const f32x4*)(bl + col) : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    }
+    const int rc = lane % OCH;
+    const int col = wcol0 + rc * 8;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int r = 4 * j + lr;
-          const int row = wrow0 + i * 32 + r;
-          f32x4 v = *(const f32x4*)(ep + r * EP_LD + lc);
-          if (row >= a.M || col >= a.N) continue;
+    for (int i = 0; i < MI; ++i) {
+#pragma unroll
+      for (int t = 0; t < NI; ++t)
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) {
+          f32x4 x = {acc[i][t][4 * e4], acc[i][t][4 * e4 + 1], acc[i][t][4 * e4 + 2], acc[i][t][4 * e4 + 3]};
           if constexpr (BIAS) {
-            const f32x4 bv = *(const f32x4*)(bl + col);
+            x += bv[t][e4];
+            if constexpr (EPI == EPI_BIAS_RELU_BF16) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              v[e] += bv[e];
-              if constexpr (EPI == EPI_BIAS_RELU_BF16) v[e] = fmaxf(v[e], 0.f);
+              for (int e = 0; e < 4; ++e) x[e] = fmaxf(x[e], 0.f);
             }
           }
-          *(u32x2*)(C + (size_t)row * a.ld_out + col) = u32x2{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
+          const int c = (t * 4 + e4) ^ swz_o(r32);
+          *(u32x2*)(sp + r32 * WTN + c * 8 + half_lane) = u32x2{pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3])};
         }
-        lds_sync();
+      lds_sync();
+      // OCH lanes per staged row, 64 / OCH rows per access.
+#pragma unroll
+      for (int k = 0; k < 32 * OCH / 64; ++k) {
+        const int rr = k * (64 / OCH) + lane / OCH;
+        const u32x4 v = *(const u32x4*)(sp + rr * WTN + (rc ^ swz_o(rr)) * 8);
+        const int row = wrow0 + i * 32 + rr;
+        if (row < a.M && col < a.N) *(u32x4*)(C + (size_t)row * a.ld_out + col) = v;
       }
+      lds_sync();
+    }
   } else {
     // Paired read-back: 8 lanes per row, each with 4 columns of the first
     // block and the same 4 columns of the second; 8 rows per access.
@@ -551,6 +573,9 @@ void launch_epi(const GemmArgs& a, const GroupTable& tab, hipStream_t stream) {
 hipError_t launch_gemm_bf16(int epilogue, const GemmArgs& a, const GroupTable& tab,
                             hipStream_t stream) {
   if (tab.G == 0 || a.M == 0 || a.N == 0) return hipSuccess;
+  const bool plain_store = epilogue == EPI_STORE_BF16 || epilogue == EPI_BIAS_BF16 ||
+                           epilogue == EPI_BIAS_RELU_BF16;
+  if (plain_store && a.N % 8 != 0) return hipErrorInvalidValue;   // whole 16-byte output chunks
   switch (epilogue) {
     case EPI_STORE_BF16: launch_epi<EPI_STORE_BF16>(a, tab, stream); break;
     case EPI_QKV_ROPE: launch_epi<EPI_QKV_ROPE>(a, tab, stream); break;
