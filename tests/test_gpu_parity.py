@@ -279,3 +279,26 @@ def test_llama8b_first_segment_gate():
     gu.say(f"  rel L2 hidden {e_h:.3e} mem {e_m:.3e}")
     run.close()
     assert e_h <= BF16_TOL and e_m <= BF16_TOL
+
+
+def test_encoder_rows_with_a_large_mean():
+    """Every input row and memory row offset by c = 1000 (mean 1000, spread
+    ~1).  LayerNorm ignores a uniform shift and the residual carries it, so
+    the recurrence is the unshifted one plus c.  The GPU's LayerNorm takes the
+    variance from centred values: on fp32 rows like these (the memory rows
+    and every deeper layer's input) a plain one-pass E[x^2] - mean^2 in fp32
+    is off by more than the variance itself, measured on the CPU.  Compared
+    after removing c, within the bf16 gate."""
+    cfg = ri.TINY_ENCODER
+    c = 1000.0
+    gu.say(f"[parity] {cfg.name} with rows shifted by {c}")
+    layers, x, mem0, _ = gu.inputs(cfg)
+    x = ri.round_bf16((x + c).astype(np.float32))     # input rows travel as bf16
+    mem0 = (mem0 + c).astype(np.float32)              # memory rows are fp32
+    run = gu.GpuRun(cfg, layers=layers, x=x, mem0=mem0, embed=None)
+    hd, md = run.run("diagonal")
+    ho, mo = _oracle(cfg, run)
+    e_h, e_m = gu.rel_l2(hd - c, ho - c), gu.rel_l2(md - c, mo - c)
+    gu.say(f"  rel L2 (offset removed) hidden {e_h:.3e} mem {e_m:.3e}")
+    assert e_h <= BF16_TOL and e_m <= BF16_TOL
+    run.close()
