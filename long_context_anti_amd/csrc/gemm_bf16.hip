@@ -255,10 +255,12 @@ __global__ __launch_bounds__((BM / WTM) * (BN / WTN) * 64, 1) void gemm_bf16_ker
   // Accumulator layout (C^T blocks): element e of lane l of block (i, t) is
   // row i*32 + l%32, column t*32 + 8*(e/4) + 4*(l/32) + e%4.  A wave-wide
   // access straight from that layout touches 32 rows at 16-32 bytes each, so
-  // the bf16 epilogues send every 32 x 64 piece (two 32-column blocks)
-  // through a private LDS region of the wave and read it back row-major, so
-  // their stores cover whole row segments.  RoPE and SwiGLU pair their two
-  // blocks inside one piece.
+  // the bf16 epilogues go through a private LDS region of the wave and read
+  // it back row-major, so that their stores cover whole row segments: the
+  // plain-store, bias and SwiGLU epilogues finish their arithmetic on the
+  // accumulators and stage bf16 results; RoPE stages the two fp32 blocks of
+  // a rotation pair and rotates after the read-back.  The fp32 residual
+  // epilogues work straight from the accumulator layout.
   if constexpr (EPI != EPI_RESID_F32 && EPI != EPI_RESID_BIAS_F32) {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();      // the ring is free once every wave is past its last slice
