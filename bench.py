@@ -66,17 +66,28 @@ def gen_layers(cfg, seed=0):
     return ri.all_weights(cfg, seed, workers=8)
 
 
+def code_hash(path):
+    """sha256 prefix of a C++ source with its comments and blank space removed,
+    so that the figure certifies the code, not its commentary."""
+    import hashlib
+    import re
+    src = open(path).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", "", src)
+    src = re.sub(r"\s+", " ", src).strip()
+    return hashlib.sha256(src.encode()).hexdigest()[:16]
+
+
 def measured_traffic():
     """HBM bytes per gate/up launch from the committed counter summary, used
-    only while the GEMM source is the one the counters were taken on."""
-    import hashlib
+    only while the GEMM code is the one the counters were taken on."""
     import re
     src = os.path.join(ROOT, "long_context_anti_amd", "csrc", "gemm_bf16.hip")
     summ = os.path.join(ROOT, "profiles", "llama1b_rmt_L16_S128_gateup_hbm_traffic.md")
     try:
         text = open(summ).read()
-        h = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
-        if f"sha256 prefix: {h}" not in text:
+        h = code_hash(src)
+        if f"code sha256 prefix: {h}" not in text:
             return None
         m = re.search(r"traffic \(bench roofline field\) = ([0-9.]+) GB \+ ([0-9.]+) GB", text)
         return round((float(m.group(1)) + float(m.group(2))) * 1e9) if m else None
