@@ -311,6 +311,10 @@ def main():
     if encoder:
         config["cell"] = "pre-norm encoder layer (LayerNorm, unmasked MHA, ReLU FFN, biases)"
     config.update({"ffn": cfg.F, "tokens": T, "path": "rmt_forward_diagonal"})
+    props = torch.cuda.get_device_properties(0)
+    device = {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
+              "compute_units": props.multi_processor_count,
+              "hbm_gib": round(props.total_memory / 2**30, 1)}
     if B > 1:
         config["sequences"] = B
     if llama:
@@ -324,6 +328,7 @@ def main():
         "data": data,
         "config": config,
         "roofline": roofline,
+        "device": device,
         "grouped_gemm_stages": gemm_out,
         "ms_per_step_with_stage_events": round(wall_ev / args.steps * 1e3, 2),
         "stages": ({ENCODER_STAGE_NAMES.get(k, k): v for k, v in st_out.items()} if encoder else st_out),
