@@ -40,7 +40,8 @@ PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 METRIC = "tokens/s for one 131K-token sequence; grouped-GEMM % of bf16 MFMA peak"
 WORKLOADS = {"llama1b": "LLAMA_1B", "llama8b": "LLAMA_8B", "norm_swiglu_1b": "NORM_SWIGLU_1B",
-             "encoder1b": "ENCODER_1B"}
+             "encoder1b": "ENCODER_1B", "tiny_linear_gelu": "TINY_LINEAR_GELU"}
+PEAK_FP32_VALU_TFLOPS = 157.3  # MI355X fp32 vector (FMA) peak
 # the encoder cell's stages, named by what they compute there
 ENCODER_STAGE_NAMES = {"norm1": "layernorm1", "norm2": "layernorm2", "gateup": "ffn_w1", "down": "ffn_w2"}
 GEMM_KERNELS = {
@@ -54,6 +55,7 @@ GEMM_KERNELS = {
                 "down": "W2 stage + bias + residual epilogue (gemm_bf16_kernel<6>)"},
     "norm_swiglu": {"gateup": "gate/up stage + SwiGLU epilogue (gemm_bf16_kernel<2>)",
                     "down": "down stage + residual epilogue (gemm_bf16_kernel<3>)"},
+    "linear_gelu": {"linear": "fp32 linear + bias + GELU cell (linear_gelu_f32_kernel, VALU FMAs)"},
 }
 
 
@@ -260,8 +262,12 @@ def main():
     def rates(v):
         e = {"ms_per_step": round(v["ms"] / args.steps, 3), "launches_per_step": v["launches"] // args.steps}
         if v["ms"] > 0 and v["flops"] > 0:
-            e["tflops"] = round(v["flops"] / (v["ms"] / 1e3) / 1e12, 1)
-            e["frac_bf16_peak"] = round(e["tflops"] / PEAK_BF16_TFLOPS, 4)
+            tf = v["flops"] / (v["ms"] / 1e3) / 1e12
+            e["tflops"] = round(tf, 1 if tf >= 1 else 6)
+            if cfg.cell == ri.CELL_LINEAR_GELU:     # fp32 on the vector ALUs
+                e["frac_fp32_valu_peak"] = round(tf / PEAK_FP32_VALU_TFLOPS, 6)
+            else:
+                e["frac_bf16_peak"] = round(tf / PEAK_BF16_TFLOPS, 4)
         if v["ms"] > 0 and v["bytes"] > 0:
             e["gbs"] = round(v["bytes"] / (v["ms"] / 1e3) / 1e9, 1)
             e["frac_hbm_peak"] = round(e["gbs"] / PEAK_HBM_GBS, 4)
@@ -292,15 +298,18 @@ def main():
     gemm_out["ramp_diagonals"] = gemm_out.pop("ramp", None)
 
     # the dominant kernel: the GEMM stage that takes the most time
-    kind = "llama" if llama else "encoder" if encoder else "norm_swiglu"
+    kind = ("llama" if llama else "encoder" if encoder else
+            "linear_gelu" if cfg.cell == ri.CELL_LINEAR_GELU else "norm_swiglu")
     dom = max((s for s in GEMM_KERNELS[kind] if stages[s]["launches"]), key=lambda s: stages[s]["ms"])
     # the committed counter summary covers the 1B-shaped workload's gate/up kernel only
     traffic = measured_traffic() if args.workload == "llama1b" and dom == "gateup" else None
     gu = stages[dom]
     achieved = gu["flops"] / gu["launches"] / (gu["ms"] / 1e3 / gu["launches"]) / 1e12
-    roofline = {"kernel": "grouped GEMM, " + GEMM_KERNELS[kind][dom],
-                "bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+    alu = kind == "linear_gelu"      # fp32 arithmetic on the vector ALUs, no matrix cores
+    peak = PEAK_FP32_VALU_TFLOPS if alu else PEAK_BF16_TFLOPS
+    roofline = {"kernel": ("" if alu else "grouped GEMM, ") + GEMM_KERNELS[kind][dom],
+                "bound": "alu" if alu else "mfma", "achieved": round(achieved, 3), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 5), "traffic": traffic,
                 "avg_launch_us": round(gu["ms"] / gu["launches"] * 1e3, 2),
                 "flops_per_launch": gu["flops"] / gu["launches"]}
 
@@ -321,10 +330,11 @@ def main():
         config["vocab"] = cfg.V
     data = ("synthetic (seeded random weights, token ids uniform over the vocabulary)" if llama
             else "synthetic (seeded random weights and input embeddings)")
+    dtype = "f32" if cfg.dtype != ri.BF16 else "bf16"
     result = {
         "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 2),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dtype,
         "data": data,
         "config": config,
         "roofline": roofline,
