@@ -47,7 +47,8 @@ Readings where the pages are silent (each is listed in the design doc):
     MHA projects with biases, attends over all R rows of the cell without a
     mask (scale 1/sqrt(hd), one KV head per query head) and projects out with
     a bias, and FFN is ``relu(z W1 + b1) W2 + b2``.  Dropout is the identity
-    at inference.
+    at inference.  The post-norm order (torch's default, ``norm_first=False``)
+    is also provided: ``H = LN1(A + MHA(A))``, ``Y = LN2(H + FFN(H))``.
 
 Arithmetic is in the dtype of the inputs (float32 by default, float64 for
 the pins).  There is no blocking, fusion or reordering beyond the per-cell
@@ -229,20 +230,33 @@ def cell_llama(A: np.ndarray, w: Dict[str, np.ndarray], Hq: int, Hkv: int, hd: i
     return H + swiglu(rms_norm(H, w["g2"], eps), w["wg"], w["wu"], w["wd"])
 
 
-def cell_encoder(A: np.ndarray, w: Dict[str, np.ndarray], H: int, hd: int,
-                 eps: float) -> np.ndarray:
-    """Pre-norm encoder layer over the cell's R rows:
-    H = A + MHA(LN1(A));  Y = H + relu(LN2(H) W1 + b1) W2 + b2."""
-    R = A.shape[0]
-    z = layer_norm(A, w["ln1_g"], w["ln1_b"], eps)
+def _encoder_mha(z: np.ndarray, w: Dict[str, np.ndarray], H: int, hd: int) -> np.ndarray:
+    """Biased Q/K/V projection, unmasked multi-head attention, biased output
+    projection, on rows z [R, d]."""
+    R = z.shape[0]
     qkv = z @ w["wqkv"] + w["bqkv"]
     nq = H * hd
     q = qkv[:, :nq].reshape(R, H, hd)
     k = qkv[:, nq:2 * nq].reshape(R, H, hd)
     v = qkv[:, 2 * nq:3 * nq].reshape(R, H, hd)
-    Hs = A + (full_mha(q, k, v) @ w["wo"] + w["bo"])
-    z2 = layer_norm(Hs, w["ln2_g"], w["ln2_b"], eps)
-    return Hs + (relu(z2 @ w["w1"] + w["b1"]) @ w["w2"] + w["b2"])
+    return full_mha(q, k, v) @ w["wo"] + w["bo"]
+
+
+def _encoder_ffn(z: np.ndarray, w: Dict[str, np.ndarray]) -> np.ndarray:
+    return relu(z @ w["w1"] + w["b1"]) @ w["w2"] + w["b2"]
+
+
+def cell_encoder(A: np.ndarray, w: Dict[str, np.ndarray], H: int, hd: int,
+                 eps: float, post_norm: bool = False) -> np.ndarray:
+    """Encoder layer over the cell's R rows.
+    Pre-norm:  H = A + MHA(LN1(A));    Y = H + FFN(LN2(H)).
+    Post-norm: H = LN1(A + MHA(A));    Y = LN2(H + FFN(H)).
+    FFN(z) = relu(z W1 + b1) W2 + b2."""
+    if post_norm:
+        Hs = layer_norm(A + _encoder_mha(A, w, H, hd), w["ln1_g"], w["ln1_b"], eps)
+        return layer_norm(Hs + _encoder_ffn(Hs, w), w["ln2_g"], w["ln2_b"], eps)
+    Hs = A + _encoder_mha(layer_norm(A, w["ln1_g"], w["ln1_b"], eps), w, H, hd)
+    return Hs + _encoder_ffn(layer_norm(Hs, w["ln2_g"], w["ln2_b"], eps), w)
 
 
 def cell(cfg, w: Dict[str, np.ndarray], A: np.ndarray) -> np.ndarray:
@@ -253,7 +267,7 @@ def cell(cfg, w: Dict[str, np.ndarray], A: np.ndarray) -> np.ndarray:
     if cfg.cell == CELL_LLAMA:
         return cell_llama(A, w, cfg.Hq, cfg.Hkv, cfg.hd, cfg.eps, cfg.theta)
     if cfg.cell == CELL_ENCODER:
-        return cell_encoder(A, w, cfg.Hq, cfg.hd, cfg.eps)
+        return cell_encoder(A, w, cfg.Hq, cfg.hd, cfg.eps, getattr(cfg, "post_norm", False))
     raise ValueError(f"unknown cell kind {cfg.cell}")
 
 

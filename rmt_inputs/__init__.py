@@ -69,6 +69,7 @@ class RMTConfig:
     mem_std: float = 1.0      # initial memory std
     b_std: float = 0.02       # encoder cell: bias std
     ln_std: float = 0.1       # encoder cell: LayerNorm gain spread around 1, and shift std
+    post_norm: bool = False   # encoder cell: LayerNorm after each residual add (torch's default)
 
     @property
     def R(self) -> int:
@@ -149,10 +150,19 @@ TINY_ENCODER_HD128 = RMTConfig(
     L=2, S=3, n=136, m=24, d=512, Hq=4, Hkv=4, hd=128, F=2048,
     w_std=0.04, x_std=1.0, mem_std=1.0)
 
+# The same encoder layer in the post-norm order (norm_first=False, torch's default).
+ENCODER_1B_POSTNORM = dataclasses.replace(ENCODER_1B, name="encoder1b_postnorm_rmt_L16_S128", wid=6,
+                                          post_norm=True)
+TINY_ENCODER_POSTNORM = dataclasses.replace(TINY_ENCODER, name="tiny_encoder_postnorm", wid=42,
+                                            post_norm=True)
+TINY_ENCODER_POSTNORM_HD128 = dataclasses.replace(TINY_ENCODER_HD128, name="tiny_encoder_postnorm_hd128",
+                                                  wid=43, post_norm=True)
+
 PRESETS: Dict[str, RMTConfig] = {
     c.name: c for c in (TINY_LINEAR_GELU, NORM_SWIGLU_1B, LLAMA_1B, LLAMA_8B,
                         TINY_SWIGLU, TINY_LLAMA, TINY_LLAMA_HD128, ENCODER_1B,
-                        TINY_ENCODER, TINY_ENCODER_HD128)
+                        TINY_ENCODER, TINY_ENCODER_HD128, ENCODER_1B_POSTNORM,
+                        TINY_ENCODER_POSTNORM, TINY_ENCODER_POSTNORM_HD128)
 }
 
 

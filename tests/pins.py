@@ -179,13 +179,14 @@ def torch_norm_swiglu_block(A, w, cfg):
 
 def torch_encoder_block(A, w, cfg):
     """One torch ``nn.TransformerEncoderLayer`` -- the module the skill page's
-    Implementation sketch stacks -- built pre-norm with a ReLU feed-forward and
-    no dropout, in float64, loaded with the cell's weights (torch keeps Linear
-    weights as [out, in], hence the transposes)."""
+    Implementation sketch stacks -- with a ReLU feed-forward and no dropout,
+    pre-norm or post-norm as the workload says, in float64, loaded with the
+    cell's weights (torch keeps Linear weights as [out, in], hence the
+    transposes)."""
     t = lambda a: torch.from_numpy(np.asarray(a, np.float64))  # noqa: E731
     layer = torch.nn.TransformerEncoderLayer(
         d_model=cfg.d, nhead=cfg.Hq, dim_feedforward=cfg.F, dropout=0.0, activation="relu",
-        layer_norm_eps=cfg.eps, batch_first=True, norm_first=True, dtype=torch.float64)
+        layer_norm_eps=cfg.eps, batch_first=True, norm_first=not cfg.post_norm, dtype=torch.float64)
     layer.eval()
     with torch.no_grad():
         layer.self_attn.in_proj_weight.copy_(t(w["wqkv"]).T)

@@ -217,8 +217,9 @@ def test_mutation_short_tail_zero_padded(T):
 # The encoder-layer cell
 # ---------------------------------------------------------------------------
 
-def _post_norm_encoder(A, w, H, hd, eps):
-    """The layer with norm_first=False: the norms follow the residual adds."""
+def _post_norm_encoder(A, w, H, hd, eps, post_norm=False):
+    """The layer with norm_first=False (whatever the workload asks): the norms
+    follow the residual adds."""
     R = A.shape[0]
     qkv = A @ w["wqkv"] + w["bqkv"]
     nq = H * hd
@@ -266,10 +267,10 @@ def test_mutation_encoder_attention_causal(monkeypatch):
 def test_mutation_encoder_dropped_bias(monkeypatch, bias):
     plain = orc.cell_encoder
 
-    def dropped(A, w, H, hd, eps):
+    def dropped(A, w, H, hd, eps, post_norm=False):
         w = dict(w)
         w[bias] = np.zeros_like(w[bias])
-        return plain(A, w, H, hd, eps)
+        return plain(A, w, H, hd, eps, post_norm)
     monkeypatch.setattr(orc, "cell_encoder", dropped)
     assert _fails(pins.pin_single_segment_against_torch, ri.TINY_ENCODER)
 
@@ -283,3 +284,11 @@ def test_mutation_encoder_swapped_k_v(monkeypatch):
     plain = orc.full_mha
     monkeypatch.setattr(orc, "full_mha", lambda q, k, v: plain(q, v, k))
     assert _fails(pins.pin_single_segment_against_torch, ri.TINY_ENCODER)
+
+
+def test_mutation_encoder_pre_norm_for_post_norm(monkeypatch):
+    """The post-norm workload computed in the pre-norm order fails its torch pin."""
+    plain = orc.cell_encoder
+    monkeypatch.setattr(orc, "cell_encoder",
+                        lambda A, w, H, hd, eps, post_norm=False: plain(A, w, H, hd, eps, False))
+    assert _fails(pins.pin_single_segment_against_torch, ri.TINY_ENCODER_POSTNORM)

@@ -11,7 +11,10 @@ from oracle import rmt_oracle as orc
 import pins
 
 TINY_RESIDUAL = [ri.TINY_SWIGLU, ri.TINY_LLAMA, ri.TINY_LLAMA_HD128, ri.TINY_ENCODER,
-                 ri.TINY_ENCODER_HD128]
+                 ri.TINY_ENCODER_HD128, ri.TINY_ENCODER_POSTNORM, ri.TINY_ENCODER_POSTNORM_HD128]
+# cells that compute Y = A exactly when the last projection of every branch is zero (a post-norm
+# layer still normalises, so it has no such weights)
+TINY_IDENTITY = [c for c in TINY_RESIDUAL if not c.post_norm]
 
 
 def test_linear_gelu_bruteforce_fp32():
@@ -27,7 +30,7 @@ def test_linear_gelu_bruteforce_diagonal():
     pins.pin_linear_gelu_bruteforce(forward=orc.forward_diagonal, tol=1e-5)
 
 
-@pytest.mark.parametrize("cfg", TINY_RESIDUAL, ids=lambda c: c.name)
+@pytest.mark.parametrize("cfg", TINY_IDENTITY, ids=lambda c: c.name)
 def test_shift_register(cfg):
     pins.pin_shift_register(cfg)
     pins.pin_shift_register(cfg, forward=orc.forward_diagonal)
@@ -167,7 +170,7 @@ def test_linear_gelu_bruteforce_ragged(T):
     pins.pin_linear_gelu_bruteforce_ragged(T, forward=fwd)
 
 
-@pytest.mark.parametrize("cfg", TINY_RESIDUAL, ids=lambda c: c.name)
+@pytest.mark.parametrize("cfg", TINY_IDENTITY, ids=lambda c: c.name)
 def test_shift_register_ragged(cfg):
     T = (cfg.S - 1) * cfg.n + cfg.n // 3
     pins.pin_shift_register_ragged(cfg, T)
