@@ -40,10 +40,13 @@ PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 METRIC = "tokens/s for one 131K-token sequence; grouped-GEMM % of bf16 MFMA peak"
 WORKLOADS = {"llama1b": "LLAMA_1B", "llama8b": "LLAMA_8B", "norm_swiglu_1b": "NORM_SWIGLU_1B",
-             "encoder1b": "ENCODER_1B", "tiny_linear_gelu": "TINY_LINEAR_GELU"}
+             "encoder1b": "ENCODER_1B", "encoder1b_postnorm": "ENCODER_1B_POSTNORM",
+             "tiny_linear_gelu": "TINY_LINEAR_GELU"}
 PEAK_FP32_VALU_TFLOPS = 157.3  # MI355X fp32 vector (FMA) peak
 # the encoder cell's stages, named by what they compute there
 ENCODER_STAGE_NAMES = {"norm1": "layernorm1", "norm2": "layernorm2", "gateup": "ffn_w1", "down": "ffn_w2"}
+# post-norm: the first norm-stage launch is the bf16 copy of A, the second stage holds both LayerNorms
+POSTNORM_STAGE_NAMES = {"norm1": "cast_a_bf16", "norm2": "layernorms", "gateup": "ffn_w1", "down": "ffn_w2"}
 GEMM_KERNELS = {
     "llama": {"qkv": "QKV stage + RoPE epilogue (gemm_bf16_kernel<1>)",
               "oproj": "O stage + residual epilogue (gemm_bf16_kernel<3>)",
@@ -318,7 +321,8 @@ def main():
     if llama or encoder:
         config.update({"heads": cfg.Hq, "kv_heads": cfg.Hkv, "head_dim": cfg.hd})
     if encoder:
-        config["cell"] = "pre-norm encoder layer (LayerNorm, unmasked MHA, ReLU FFN, biases)"
+        config["cell"] = (("post" if cfg.post_norm else "pre") +
+                          "-norm encoder layer (LayerNorm, unmasked MHA, ReLU FFN, biases)")
     config.update({"ffn": cfg.F, "tokens": T, "path": "rmt_forward_diagonal"})
     props = torch.cuda.get_device_properties(0)
     device = {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
@@ -341,7 +345,8 @@ def main():
         "device": device,
         "grouped_gemm_stages": gemm_out,
         "ms_per_step_with_stage_events": round(wall_ev / args.steps * 1e3, 2),
-        "stages": ({ENCODER_STAGE_NAMES.get(k, k): v for k, v in st_out.items()} if encoder else st_out),
+        "stages": ({(POSTNORM_STAGE_NAMES if cfg.post_norm else ENCODER_STAGE_NAMES).get(k, k): v
+                    for k, v in st_out.items()} if encoder else st_out),
     }
 
     if not args.no_seq:

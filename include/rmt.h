@@ -86,6 +86,9 @@ typedef struct rmt_config {
   int32_t vocab;       /* LLAMA: embedding rows V                             */
   float eps;           /* RMSNorm / LayerNorm epsilon                         */
   float rope_theta;    /* LLAMA: RoPE base                                    */
+  int32_t post_norm;   /* ENCODER: 0 = pre-norm (the default reading), 1 =
+                          post-norm (torch's norm_first=False): H = LN1(A +
+                          MHA(A)), Y = LN2(H + FFN(H)); must be 0 otherwise   */
 } rmt_config;
 
 /* Mathematical-layout weights, stacked over layers (device pointers).  They
@@ -228,7 +231,8 @@ int32_t rmt_model_check(rmt_model* model, int32_t* bad_tokens);
  * the model's stream after every launch (and one before the first), so the
  * time between consecutive events is one launch's duration on the stream.
  * rmt_model_stage_times synchronises the stream and returns, for each stage
- * (RMT_STAGE_*; for ENCODER cells NORM1/NORM2 are the LayerNorms and
+ * (RMT_STAGE_*; for ENCODER cells NORM1/NORM2 are the LayerNorms -- with
+ * post_norm, NORM1 is the bf16 copy of A and NORM2 both LayerNorms -- and
  * GATEUP/DOWN the feed-forward's W1 and W2 products), the summed milliseconds, the number of launches, and the
  * algorithmic flops and HBM bytes of those launches (compulsory operand and
  * result traffic, no re-reads), then clears the totals.  Host arrays of

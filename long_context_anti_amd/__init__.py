@@ -108,10 +108,10 @@ class RMTModel:
     def __init__(self, *, cell: int, dtype: int, L: int, S: int, n: int, m: int, d: int,
                  n_heads: int = 0, n_kv_heads: int = 0, head_dim: int = 0, ffn: int = 0,
                  vocab: int = 0, eps: float = 1e-5, rope_theta: float = 500000.0,
-                 weights: Dict[str, object], stream=None):
+                 post_norm: bool = False, weights: Dict[str, object], stream=None):
         import torch
         self.cfg = RmtConfig(cell, dtype, L, S, n, m, d, n_heads, n_kv_heads, head_dim, ffn, vocab,
-                             eps, rope_theta)
+                             eps, rope_theta, int(bool(post_norm)))
         big = [weights[k] for k in ("w", "wqkv", "wo", "wg", "wu", "wd", "w1", "w2")
                if weights.get(k) is not None]
         wdt = RMT_BF16 if big and big[0].dtype == torch.bfloat16 else RMT_F32

@@ -34,6 +34,7 @@ class RmtConfig(C.Structure):
         ("n", C.c_int32), ("m", C.c_int32), ("d", C.c_int32), ("n_heads", C.c_int32),
         ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32), ("ffn", C.c_int32),
         ("vocab", C.c_int32), ("eps", C.c_float), ("rope_theta", C.c_float),
+        ("post_norm", C.c_int32),
     ]
 
 

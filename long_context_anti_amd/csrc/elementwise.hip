@@ -22,20 +22,27 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+enum NormMode : int { NORM_RMS = 0, NORM_LAYER = 1, NORM_CAST = 2 };
+
 // One wave per row, four rows per workgroup.  Row r of group g comes from
-// in_lo[g] (r < split_in) or in_hi[g]; the normalised row goes to the packed
-// bf16 matrix at row g*R + r.  Rows of up to 64*4*VPL elements stay in
-// registers between the reductions and the scaling, so each input byte is
-// read once; wider rows take further passes.  Requires d % 4 == 0.
-//   LAYER = false: RMSNorm,   y = x * rsqrt(mean(x^2) + eps) * gamma
-//   LAYER = true:  LayerNorm, y = (x - mu) * rsqrt(mean((x - mu)^2) + eps) * gamma + beta
-// (the centred second pass keeps the variance accurate for rows with a
-// large mean).
-template <int VPL, bool LAYER>
+// in_lo[g] (r < split_in) or in_hi[g].  The result goes to the packed bf16
+// matrix at row g*R + r (unless `out` is null) and, with F32OUT, in fp32 to
+// out_lo[g] (r < split_out) or out_hi[g].  Rows of up to 64*4*VPL elements
+// stay in registers between the reductions and the scaling, so each input
+// byte is read once; wider rows take further passes.  Requires d % 4 == 0.
+//   NORM_RMS:   y = x * rsqrt(mean(x^2) + eps) * gamma
+//   NORM_LAYER: y = (x - mu) * rsqrt(mean((x - mu)^2) + eps) * gamma + beta
+//               (the centred second pass keeps the variance accurate for
+//               rows with a large mean)
+//   NORM_CAST:  y = x (a bf16 copy of the rows)
+template <int VPL, int MODE, bool F32OUT>
 __global__ __launch_bounds__(256) void norm_kernel(int total_rows, int R, int d, int split_in,
-                                                   GroupTable tab, const float* __restrict__ gamma,
+                                                   int split_out, GroupTable tab,
+                                                   const float* __restrict__ gamma,
                                                    const float* __restrict__ beta, float eps,
                                                    uint16_t* __restrict__ out) {
+  constexpr bool LAYER = MODE == NORM_LAYER;
+  constexpr bool SCALE = MODE != NORM_CAST;
   const int lane = (int)threadIdx.x & 63;
   const int row = (int)blockIdx.x * 4 + ((int)threadIdx.x >> 6);
   if (row >= total_rows) return;
@@ -43,20 +50,24 @@ __global__ __launch_bounds__(256) void norm_kernel(int total_rows, int R, int d,
   const int r = row - g * R;
   const float* src = r < split_in ? (const float*)tab.in_lo[g] + (size_t)r * d
                                   : (const float*)tab.in_hi[g] + (size_t)(r - split_in) * d;
-  const float* gm = gamma + (size_t)tab.layer[g] * d;
+  const float* gm = SCALE ? gamma + (size_t)tab.layer[g] * d : nullptr;
   const float* bt = LAYER ? beta + (size_t)tab.layer[g] * d : nullptr;
-  uint16_t* dst = out + (size_t)row * d;
-  f32x4 v[VPL], w[VPL], bb[LAYER ? VPL : 1];
+  uint16_t* dst = out ? out + (size_t)row * d : nullptr;
+  float* dst32 = nullptr;
+  if constexpr (F32OUT)
+    dst32 = r < split_out ? (float*)tab.out_lo[g] + (size_t)r * d
+                          : (float*)tab.out_hi[g] + (size_t)(r - split_out) * d;
+  f32x4 v[VPL], w[SCALE ? VPL : 1], bb[LAYER ? VPL : 1];
   // the row, its gamma (and beta) are requested together, so their latency
   // overlaps the row's instead of following the reductions
 #pragma unroll
   for (int j = 0; j < VPL; ++j) {
     const int c = (lane + 64 * j) * 4;
     v[j] = c < d ? *(const f32x4*)(src + c) : f32x4{0.f, 0.f, 0.f, 0.f};
-    w[j] = c < d ? *(const f32x4*)(gm + c) : f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (SCALE) w[j] = c < d ? *(const f32x4*)(gm + c) : f32x4{0.f, 0.f, 0.f, 0.f};
     if constexpr (LAYER) bb[j] = c < d ? *(const f32x4*)(bt + c) : f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  float mu = 0.f;
+  float mu = 0.f, inv = 1.f;
   if constexpr (LAYER) {
     float s = 0.f;
 #pragma unroll
@@ -67,41 +78,51 @@ __global__ __launch_bounds__(256) void norm_kernel(int total_rows, int R, int d,
     }
     mu = wave_sum(s) / (float)d;
   }
-  float ss = 0.f;
+  if constexpr (SCALE) {
+    float ss = 0.f;
 #pragma unroll
-  for (int j = 0; j < VPL; ++j) {
-    const int c = (lane + 64 * j) * 4;
-    if (!LAYER || c < d) {   // padding lanes hold zeros, which LayerNorm would centre
-      const f32x4 x = v[j] - mu;
+    for (int j = 0; j < VPL; ++j) {
+      const int c = (lane + 64 * j) * 4;
+      if (!LAYER || c < d) {   // padding lanes hold zeros, which LayerNorm would centre
+        const f32x4 x = v[j] - mu;
+        ss += x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3];
+      }
+    }
+    for (int c = (lane + 64 * VPL) * 4; c < d; c += 256) {
+      const f32x4 x = *(const f32x4*)(src + c) - mu;
       ss += x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3];
     }
+    ss = wave_sum(ss);
+    inv = 1.0f / sqrtf(ss / (float)d + eps);
   }
-  for (int c = (lane + 64 * VPL) * 4; c < d; c += 256) {
-    const f32x4 x = *(const f32x4*)(src + c) - mu;
-    ss += x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3];
-  }
-  ss = wave_sum(ss);
-  const float inv = 1.0f / sqrtf(ss / (float)d + eps);
   auto emit = [&](int c, const f32x4& x, const f32x4& gw, const f32x4& sh) __attribute__((always_inline)) {
     f32x4 y;
+    if constexpr (SCALE) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) y[e] = (x[e] - mu) * inv * gw[e];
+      for (int e = 0; e < 4; ++e) y[e] = (x[e] - mu) * inv * gw[e];
+    } else {
+      y = x;
+    }
     if constexpr (LAYER) y += sh;
-    u16x4 o;
-    o[0] = to_bf16(y[0]);
-    o[1] = to_bf16(y[1]);
-    o[2] = to_bf16(y[2]);
-    o[3] = to_bf16(y[3]);
-    *(u16x4*)(dst + c) = o;
+    if (dst) {
+      u16x4 o;
+      o[0] = to_bf16(y[0]);
+      o[1] = to_bf16(y[1]);
+      o[2] = to_bf16(y[2]);
+      o[3] = to_bf16(y[3]);
+      *(u16x4*)(dst + c) = o;
+    }
+    if constexpr (F32OUT) *(f32x4*)(dst32 + c) = y;
   };
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int j = 0; j < VPL; ++j) {
     const int c = (lane + 64 * j) * 4;
-    if (c < d) emit(c, v[j], w[j], bb[LAYER ? j : 0]);
+    if (c < d) emit(c, v[j], w[SCALE ? j : 0], bb[LAYER ? j : 0]);
   }
   for (int c = (lane + 64 * VPL) * 4; c < d; c += 256)
-    emit(c, *(const f32x4*)(src + c), *(const f32x4*)(gm + c),
-         LAYER ? *(const f32x4*)(bt + c) : f32x4{0.f, 0.f, 0.f, 0.f});
+    emit(c, *(const f32x4*)(src + c), SCALE ? *(const f32x4*)(gm + c) : zero,
+         LAYER ? *(const f32x4*)(bt + c) : zero);
 }
 
 // Embedding lookup of one segment's n token ids into an fp32 slot.  An id
@@ -210,31 +231,44 @@ __global__ __launch_bounds__(256) void pack_kernel(int K, int N_src, const void*
 
 }  // namespace
 
-template <bool LAYER>
-hipError_t launch_norm(int G, int R, int d, int split_in, const GroupTable& tab, const float* gamma,
-                       const float* beta, float eps, uint16_t* out, hipStream_t stream) {
+template <int MODE, bool F32OUT>
+hipError_t launch_norm(int G, int R, int d, int split_in, int split_out, const GroupTable& tab,
+                       const float* gamma, const float* beta, float eps, uint16_t* out,
+                       hipStream_t stream) {
   const int rows = G * R;
   if (rows == 0) return hipSuccess;
   // 8 (16) float4 per lane keep rows of up to 2048 (4096) elements in
   // registers; the smaller variant leaves room for more waves per SIMD
   if (d <= 2048)
-    hipLaunchKernelGGL((norm_kernel<8, LAYER>), dim3((rows + 3) / 4), dim3(256), 0, stream, rows, R,
-                       d, split_in, tab, gamma, beta, eps, out);
+    hipLaunchKernelGGL((norm_kernel<8, MODE, F32OUT>), dim3((rows + 3) / 4), dim3(256), 0, stream,
+                       rows, R, d, split_in, split_out, tab, gamma, beta, eps, out);
   else
-    hipLaunchKernelGGL((norm_kernel<16, LAYER>), dim3((rows + 3) / 4), dim3(256), 0, stream, rows, R,
-                       d, split_in, tab, gamma, beta, eps, out);
+    hipLaunchKernelGGL((norm_kernel<16, MODE, F32OUT>), dim3((rows + 3) / 4), dim3(256), 0, stream,
+                       rows, R, d, split_in, split_out, tab, gamma, beta, eps, out);
   return hipGetLastError();
 }
 
 hipError_t launch_rmsnorm(int G, int R, int d, int split_in, const GroupTable& tab,
                           const float* gamma, float eps, uint16_t* out, hipStream_t stream) {
-  return launch_norm<false>(G, R, d, split_in, tab, gamma, nullptr, eps, out, stream);
+  return launch_norm<NORM_RMS, false>(G, R, d, split_in, R, tab, gamma, nullptr, eps, out, stream);
 }
 
 hipError_t launch_layernorm(int G, int R, int d, int split_in, const GroupTable& tab,
                             const float* gamma, const float* beta, float eps, uint16_t* out,
                             hipStream_t stream) {
-  return launch_norm<true>(G, R, d, split_in, tab, gamma, beta, eps, out, stream);
+  return launch_norm<NORM_LAYER, false>(G, R, d, split_in, R, tab, gamma, beta, eps, out, stream);
+}
+
+hipError_t launch_layernorm_f32(int G, int R, int d, int split_in, int split_out,
+                                const GroupTable& tab, const float* gamma, const float* beta,
+                                float eps, uint16_t* out_bf16, hipStream_t stream) {
+  return launch_norm<NORM_LAYER, true>(G, R, d, split_in, split_out, tab, gamma, beta, eps, out_bf16,
+                                       stream);
+}
+
+hipError_t launch_cast_rows(int G, int R, int d, int split_in, const GroupTable& tab, uint16_t* out,
+                            hipStream_t stream) {
+  return launch_norm<NORM_CAST, false>(G, R, d, split_in, R, tab, nullptr, nullptr, 0.f, out, stream);
 }
 
 hipError_t launch_gather_tokens(int n, int d, const int32_t* ids, int V, const uint16_t* embed,

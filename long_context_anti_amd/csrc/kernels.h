@@ -60,6 +60,14 @@ hipError_t launch_rmsnorm(int G, int R, int d, int split_in, const GroupTable& t
 hipError_t launch_layernorm(int G, int R, int d, int split_in, const GroupTable& tab,
                             const float* gamma, const float* beta, float eps, uint16_t* out,
                             hipStream_t stream);
+// LayerNorm with an fp32 result written to out_lo[g] (rows < split_out) or
+// out_hi[g], and also the packed bf16 copy when out_bf16 is not null.
+hipError_t launch_layernorm_f32(int G, int R, int d, int split_in, int split_out,
+                                const GroupTable& tab, const float* gamma, const float* beta,
+                                float eps, uint16_t* out_bf16, hipStream_t stream);
+// Rows of every group as bf16, packed (no normalisation).
+hipError_t launch_cast_rows(int G, int R, int d, int split_in, const GroupTable& tab, uint16_t* out,
+                            hipStream_t stream);
 
 // X(-1, s) rows -> fp32 slot: token-id lookup (bf16 table) or a row copy.
 hipError_t launch_gather_tokens(int n, int d, const int32_t* ids, int V, const uint16_t* embed,

@@ -98,6 +98,7 @@ struct rmt_model {
   uint16_t* qkv = nullptr;   // [C*R][Nqkv]
   uint16_t* att = nullptr;   // [C*R][Hq*hd]
   float* hbuf = nullptr;     // [C*R][d]
+  float* h2buf = nullptr;    // [C*R][d] (post-norm ENCODER: H after LayerNorm 1)
   uint16_t* ubuf = nullptr;  // [C*R][F]
   float* xbuf[2] = {nullptr, nullptr};  // [B][L][n][d] each
   float* memw = nullptr;     // [B][L][m][d]
@@ -157,6 +158,8 @@ int32_t validate_config(const rmt_config* c) {
       return fail(RMT_EUNSUPPORTED, "n_heads * head_dim must equal d");
     widest = std::max<int64_t>(widest, nqkv(*c));
   }
+  if (c->post_norm != 0 && (c->cell != RMT_CELL_ENCODER || c->post_norm != 1))
+    return fail(RMT_EINVAL, "post_norm is 0 or 1, and 1 only for ENCODER cells");
   if (c->cell == RMT_CELL_LLAMA) {
     if (c->vocab < 1) return fail(RMT_EINVAL, "vocab must be >= 1");
     if (!(c->rope_theta > 0.f)) return fail(RMT_EINVAL, "rope_theta must be > 0");
@@ -309,6 +312,62 @@ int32_t run_cells(rmt_model* M, const Cell* cells, int G, const void* tokens, co
     set_io(packed_lo, packed_lo, nullptr, nullptr);
     LAUNCH(launch_rmsnorm(G, R, d, R, tab, M->g2, c.eps, M->abuf, M->stream));
     MARK(RMT_STAGE_NORM2, 0.0, rows * d * 6);
+  } else if (c.cell == RMT_CELL_ENCODER && c.post_norm) {
+    const int hd = c.head_dim, H = c.n_heads, NQ = nqkv(c);
+    // A = [M(l, s-1); X(l-1, s)] as bf16 (the attention sees A itself)
+    set_io(in_lo, in_hi, nullptr, nullptr);
+    LAUNCH(launch_cast_rows(G, R, d, m, tab, M->abuf, M->stream));
+    MARK(RMT_STAGE_NORM1, 0.0, rows * d * 6);
+    // Q, K, V projection + bias
+    for (int g = 0; g < G; ++g) packed_out[g] = M->qkv + (size_t)g * R * NQ;
+    set_io(nullptr, nullptr, packed_out, nullptr);
+    ga.A = M->abuf; ga.B = M->wqkv; ga.M = R; ga.N = NQ; ga.K = d;
+    ga.split_in = R; ga.split_out = R; ga.ld_res = 0; ga.ld_out = NQ; ga.bias = M->bqkv;
+    LAUNCH(launch_gemm_bf16(EPI_BIAS_BF16, ga, tab, M->stream));
+    MARK(RMT_STAGE_QKV, 2.0 * rows * d * NQ, rows * d * 2 + G_ * NQ * d * 2 + rows * NQ * 2);
+    LAUNCH(launch_attention(M->qkv, M->att, G, R, H, H, hd, false, M->stream));
+    MARK(RMT_STAGE_ATTN, 4.0 * G_ * H * hd * (double)R * R, rows * NQ * 2 + rows * H * hd * 2);
+    // O projection + bias + residual A -> hbuf (before LayerNorm 1)
+    for (int g = 0; g < G; ++g) packed_out[g] = M->hbuf + (size_t)g * R * d;
+    set_io(in_lo, in_hi, packed_out, nullptr);
+    ga.A = M->att; ga.B = M->wo; ga.M = R; ga.N = d; ga.K = H * hd;
+    ga.split_in = m; ga.split_out = R; ga.ld_res = d; ga.ld_out = d; ga.bias = M->bo;
+    LAUNCH(launch_gemm_bf16(EPI_RESID_BIAS_F32, ga, tab, M->stream));
+    MARK(RMT_STAGE_OPROJ, 2.0 * rows * H * hd * d, rows * H * hd * 2 + G_ * d * H * hd * 2 + rows * d * 8);
+    // H = LayerNorm 1 -> h2buf (fp32, the residual stream) and abuf (bf16, the W1 operand)
+    const void* hb_lo[kMaxGroups];
+    void* h2_out[kMaxGroups];
+    for (int g = 0; g < G; ++g) {
+      hb_lo[g] = M->hbuf + (size_t)g * R * d;
+      h2_out[g] = M->h2buf + (size_t)g * R * d;
+    }
+    set_io(hb_lo, hb_lo, h2_out, h2_out);
+    LAUNCH(launch_layernorm_f32(G, R, d, R, R, tab, M->g1, M->beta1, c.eps, M->abuf, M->stream));
+    MARK(RMT_STAGE_NORM2, 0.0, rows * d * 10);
+    // W1 + bias + ReLU -> U
+    for (int g = 0; g < G; ++g) packed_out[g] = M->ubuf + (size_t)g * R * F;
+    set_io(nullptr, nullptr, packed_out, nullptr);
+    ga.A = M->abuf; ga.B = M->wgu; ga.M = R; ga.N = F; ga.K = d;
+    ga.split_in = R; ga.split_out = R; ga.ld_res = 0; ga.ld_out = F; ga.bias = M->b1;
+    LAUNCH(launch_gemm_bf16(EPI_BIAS_RELU_BF16, ga, tab, M->stream));
+    MARK(RMT_STAGE_GATEUP, 2.0 * rows * d * F, rows * d * 2 + G_ * F * d * 2 + rows * F * 2);
+    // W2 + bias + residual H -> hbuf (before LayerNorm 2)
+    const void* h2_lo[kMaxGroups];
+    void* hb_out[kMaxGroups];
+    for (int g = 0; g < G; ++g) {
+      h2_lo[g] = M->h2buf + (size_t)g * R * d;
+      hb_out[g] = M->hbuf + (size_t)g * R * d;
+    }
+    set_io(h2_lo, h2_lo, hb_out, hb_out);
+    ga.A = M->ubuf; ga.B = M->wd; ga.M = R; ga.N = d; ga.K = F;
+    ga.split_in = R; ga.split_out = R; ga.ld_res = d; ga.ld_out = d; ga.bias = M->b2;
+    LAUNCH(launch_gemm_bf16(EPI_RESID_BIAS_F32, ga, tab, M->stream));
+    MARK(RMT_STAGE_DOWN, 2.0 * rows * F * d, rows * F * 2 + G_ * d * F * 2 + rows * d * 8);
+    // Y = LayerNorm 2; rows [0, n) -> X(l, s), rows [n, R) -> M(l, s)
+    set_io(hb_lo, hb_lo, x_out, m_out);
+    LAUNCH(launch_layernorm_f32(G, R, d, R, ns, tab, M->g2, M->beta2, c.eps, nullptr, M->stream));
+    MARK(RMT_STAGE_NORM2, 0.0, rows * d * 8);
+    return RMT_OK;
   } else if (c.cell == RMT_CELL_ENCODER) {
     const int hd = c.head_dim, H = c.n_heads, NQ = nqkv(c);
     // LayerNorm 1 of [M(l, s-1); X(l-1, s)]
@@ -402,6 +461,7 @@ int32_t alloc_workspace(rmt_model* M, int B) {
       pieces.push_back({(void**)&M->qkv, rows * nqkv(c) * 2});
       pieces.push_back({(void**)&M->att, rows * (size_t)c.n_heads * c.head_dim * 2});
       pieces.push_back({(void**)&M->hbuf, rows * d * 4});
+      if (c.post_norm) pieces.push_back({(void**)&M->h2buf, rows * d * 4});
     }
   }
   pieces.push_back({(void**)&M->xbuf[0], (size_t)B * L * n * d * 4});

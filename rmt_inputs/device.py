@@ -53,7 +53,7 @@ def model_kwargs(cfg: RMTConfig, S: Optional[int] = None) -> Dict[str, object]:
     return dict(cell=cfg.cell, dtype=0 if cfg.dtype != BF16 else 1, L=cfg.L,
                 S=cfg.S if S is None else S, n=cfg.n, m=cfg.m, d=cfg.d, n_heads=cfg.Hq,
                 n_kv_heads=cfg.Hkv, head_dim=cfg.hd, ffn=cfg.F, vocab=cfg.V, eps=cfg.eps,
-                rope_theta=cfg.theta)
+                rope_theta=cfg.theta, post_norm=cfg.post_norm)
 
 
 def segment_inputs(cfg: RMTConfig, inputs: np.ndarray, device="cuda"):

@@ -27,7 +27,7 @@ def _run(model, tok_d, mem0_d, B, cfg, path="diagonal"):
 
 
 @pytest.mark.parametrize("cfg,B", [(ri.TINY_LINEAR_GELU, 2), (ri.TINY_SWIGLU, 2), (ri.TINY_LLAMA, 3),
-                                   (ri.TINY_LLAMA, 12), (ri.TINY_ENCODER, 3)],
+                                   (ri.TINY_LLAMA, 12), (ri.TINY_ENCODER, 3), (ri.TINY_ENCODER_POSTNORM, 2)],
                          ids=lambda v: getattr(v, "name", str(v)))
 def test_batch_matches_single_sequences(cfg, B):
     import torch

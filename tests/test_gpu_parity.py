@@ -42,7 +42,8 @@ TINY_GQA2 = dataclasses.replace(ri.TINY_LLAMA, name="tiny_llama_gqa2", wid=32, H
 
 
 @pytest.mark.parametrize("cfg", [ri.TINY_SWIGLU, ri.TINY_LLAMA, ri.TINY_LLAMA_HD128, TINY_GQA2,
-                                 ri.TINY_ENCODER, ri.TINY_ENCODER_HD128],
+                                 ri.TINY_ENCODER, ri.TINY_ENCODER_HD128, ri.TINY_ENCODER_POSTNORM,
+                                 ri.TINY_ENCODER_POSTNORM_HD128],
                          ids=lambda c: c.name)
 def test_tiny_bf16(cfg):
     gu.say(f"[parity] {cfg.name} bf16 L={cfg.L} S={cfg.S} R={cfg.R} d={cfg.d}")
@@ -112,8 +113,9 @@ def test_bad_token_ids_are_flagged():
 
 
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("cfg,S", [(ri.NORM_SWIGLU_1B, 2), (ri.LLAMA_1B, 2), (ri.ENCODER_1B, 2)],
-                         ids=["norm_swiglu_1b_S2", "llama1b_S2", "encoder1b_S2"])
+@pytest.mark.parametrize("cfg,S", [(ri.NORM_SWIGLU_1B, 2), (ri.LLAMA_1B, 2), (ri.ENCODER_1B, 2),
+                                   (ri.ENCODER_1B_POSTNORM, 2)],
+                         ids=["norm_swiglu_1b_S2", "llama1b_S2", "encoder1b_S2", "encoder1b_postnorm_S2"])
 def test_full_width_prefix(cfg, S):
     """The full-width workloads on a prefix of S segments (a prefix is exactly
     the first S segments of the full run: segment s never reads later ones)."""

@@ -38,7 +38,7 @@ def _run(model, x_d, mem0_d, T, cfg, path="diagonal", B=None):
 CASES = [(ri.TINY_LINEAR_GELU, 5 * 16 + 7), (ri.TINY_LINEAR_GELU, 5 * 16 + 2), (ri.TINY_LINEAR_GELU, 9),
          (ri.TINY_SWIGLU, 4 * 200 + 67), (ri.TINY_LLAMA, 3 * 200 + 66), (ri.TINY_LLAMA, 3 * 200 + 1),
          (ri.TINY_LLAMA_HD128, 2 * 136 + 45), (ri.TINY_ENCODER, 3 * 200 + 33),
-         (ri.TINY_ENCODER_HD128, 2 * 136 + 1)]
+         (ri.TINY_ENCODER_HD128, 2 * 136 + 1), (ri.TINY_ENCODER_POSTNORM, 3 * 200 + 77)]
 
 
 @pytest.mark.parametrize("cfg,T", CASES, ids=lambda v: getattr(v, "name", str(v)))

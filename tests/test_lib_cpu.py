@@ -112,6 +112,7 @@ def test_model_create_rejects_missing_weights():
     (dict(n_kv_heads=2), -2),                       # one KV head per query head
     (dict(n_heads=4, n_kv_heads=4, head_dim=96, d=384), -2),
     (dict(ffn=100), -2), (dict(dtype=0), -2), (dict(n_heads=3, n_kv_heads=3, d=256), -2),
+    (dict(post_norm=2), -1),
 ])
 def test_encoder_create_rejects_bad_configs(kw, code):
     L = _lib()
@@ -123,6 +124,15 @@ def test_encoder_create_rejects_bad_configs(kw, code):
     rc = L.lib().rmt_model_create(C.byref(cfg), C.byref(w), None, C.byref(handle))
     assert rc == code, L.lib().rmt_last_error()
     assert not handle.value
+
+
+def test_post_norm_only_for_encoder_cells():
+    L = _lib()
+    w = L.RmtWeights()
+    handle = C.c_void_p()
+    cfg = _cfg(post_norm=1)       # a LLaMA cell
+    assert L.lib().rmt_model_create(C.byref(cfg), C.byref(w), None, C.byref(handle)) == L.RMT_EINVAL
+    assert b"post_norm" in L.lib().rmt_last_error()
 
 
 def test_encoder_create_rejects_missing_weights():
