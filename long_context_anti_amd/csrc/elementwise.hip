@@ -57,7 +57,10 @@ __global__ __launch_bounds__(256) void norm_kernel(int total_rows, int R, int d,
   if constexpr (F32OUT)
     dst32 = r < split_out ? (float*)tab.out_lo[g] + (size_t)r * d
                           : (float*)tab.out_hi[g] + (size_t)(r - split_out) * d;
-  f32x4 v[VPL], w[SCALE ? VPL : 1], bb[LAYER ? VPL : 1];
+  // LayerNorm's shift is requested with the row too, unless that would take
+  // the register count past what keeps several waves per SIMD (wide rows)
+  constexpr bool HOIST_BETA = LAYER && VPL <= 8;
+  f32x4 v[VPL], w[SCALE ? VPL : 1], bb[HOIST_BETA ? VPL : 1];
   // the row, its gamma (and beta) are requested together, so their latency
   // overlaps the row's instead of following the reductions
 #pragma unroll
@@ -65,7 +68,7 @@ __global__ __launch_bounds__(256) void norm_kernel(int total_rows, int R, int d,
     const int c = (lane + 64 * j) * 4;
     v[j] = c < d ? *(const f32x4*)(src + c) : f32x4{0.f, 0.f, 0.f, 0.f};
     if constexpr (SCALE) w[j] = c < d ? *(const f32x4*)(gm + c) : f32x4{0.f, 0.f, 0.f, 0.f};
-    if constexpr (LAYER) bb[j] = c < d ? *(const f32x4*)(bt + c) : f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (HOIST_BETA) bb[j] = c < d ? *(const f32x4*)(bt + c) : f32x4{0.f, 0.f, 0.f, 0.f};
   }
   float mu = 0.f, inv = 1.f;
   if constexpr (LAYER) {
@@ -118,7 +121,9 @@ __global__ __launch_bounds__(256) void norm_kernel(int total_rows, int R, int d,
 #pragma unroll
   for (int j = 0; j < VPL; ++j) {
     const int c = (lane + 64 * j) * 4;
-    if (c < d) emit(c, v[j], w[SCALE ? j : 0], bb[LAYER ? j : 0]);
+    if (c < d)
+      emit(c, v[j], w[SCALE ? j : 0],
+           HOIST_BETA ? bb[j] : LAYER ? *(const f32x4*)(bt + c) : zero);
   }
   for (int c = (lane + 64 * VPL) * 4; c < d; c += 256)
     emit(c, *(const f32x4*)(src + c), SCALE ? *(const f32x4*)(gm + c) : zero,

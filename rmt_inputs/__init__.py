@@ -158,11 +158,20 @@ TINY_ENCODER_POSTNORM = dataclasses.replace(TINY_ENCODER, name="tiny_encoder_pos
 TINY_ENCODER_POSTNORM_HD128 = dataclasses.replace(TINY_ENCODER_HD128, name="tiny_encoder_postnorm_hd128",
                                                   wid=43, post_norm=True)
 
+# Rows wider than 2048 (the norm kernels' wide-row variant), in both norm orders.
+TINY_ENCODER_WIDE = RMTConfig(
+    name="tiny_encoder_wide", wid=44, cell=CELL_ENCODER, dtype=BF16,
+    L=2, S=2, n=100, m=20, d=2560, Hq=20, Hkv=20, hd=128, F=10240,
+    w_std=0.02, x_std=1.0, mem_std=1.0)
+TINY_ENCODER_WIDE_POSTNORM = dataclasses.replace(TINY_ENCODER_WIDE, name="tiny_encoder_wide_postnorm",
+                                                 wid=45, post_norm=True)
+
 PRESETS: Dict[str, RMTConfig] = {
     c.name: c for c in (TINY_LINEAR_GELU, NORM_SWIGLU_1B, LLAMA_1B, LLAMA_8B,
                         TINY_SWIGLU, TINY_LLAMA, TINY_LLAMA_HD128, ENCODER_1B,
                         TINY_ENCODER, TINY_ENCODER_HD128, ENCODER_1B_POSTNORM,
-                        TINY_ENCODER_POSTNORM, TINY_ENCODER_POSTNORM_HD128)
+                        TINY_ENCODER_POSTNORM, TINY_ENCODER_POSTNORM_HD128, TINY_ENCODER_WIDE,
+                        TINY_ENCODER_WIDE_POSTNORM)
 }
 
 

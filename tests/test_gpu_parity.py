@@ -43,7 +43,8 @@ TINY_GQA2 = dataclasses.replace(ri.TINY_LLAMA, name="tiny_llama_gqa2", wid=32, H
 
 @pytest.mark.parametrize("cfg", [ri.TINY_SWIGLU, ri.TINY_LLAMA, ri.TINY_LLAMA_HD128, TINY_GQA2,
                                  ri.TINY_ENCODER, ri.TINY_ENCODER_HD128, ri.TINY_ENCODER_POSTNORM,
-                                 ri.TINY_ENCODER_POSTNORM_HD128],
+                                 ri.TINY_ENCODER_POSTNORM_HD128, ri.TINY_ENCODER_WIDE,
+                                 ri.TINY_ENCODER_WIDE_POSTNORM],
                          ids=lambda c: c.name)
 def test_tiny_bf16(cfg):
     gu.say(f"[parity] {cfg.name} bf16 L={cfg.L} S={cfg.S} R={cfg.R} d={cfg.d}")
