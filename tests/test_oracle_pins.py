@@ -11,7 +11,8 @@ from oracle import rmt_oracle as orc
 import pins
 
 TINY_RESIDUAL = [ri.TINY_SWIGLU, ri.TINY_LLAMA, ri.TINY_LLAMA_HD128, ri.TINY_ENCODER,
-                 ri.TINY_ENCODER_HD128, ri.TINY_ENCODER_POSTNORM, ri.TINY_ENCODER_POSTNORM_HD128]
+                 ri.TINY_ENCODER_HD128, ri.TINY_ENCODER_POSTNORM, ri.TINY_ENCODER_POSTNORM_HD128,
+                 ri.TINY_ENCODER_WIDE, ri.TINY_ENCODER_WIDE_POSTNORM]
 # cells that compute Y = A exactly when the last projection of every branch is zero (a post-norm
 # layer still normalises, so it has no such weights)
 TINY_IDENTITY = [c for c in TINY_RESIDUAL if not c.post_norm]
