@@ -76,3 +76,33 @@ def test_set_batch_rejects_bad_sizes():
     assert _lib.lib().rmt_model_set_batch(run.model._handle, 0) == _lib.RMT_EINVAL
     assert _lib.lib().rmt_model_set_batch(run.model._handle, -3) == _lib.RMT_EINVAL
     run.close()
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("B", [2, 3])
+def test_full_width_batch_fills_the_largest_launch(B):
+    """The LLaMA-1B width over 16 segments: with B = 2 every full diagonal
+    holds 2 x 16 = 32 cells, the most one launch's group table carries; with
+    B = 3 its 48 cells take a launch of 32 and one of 16.  Each sequence
+    equals its own single-sequence run bit for bit (the oracle's agreement
+    at this width is covered by the prefix and teacher-forced tests)."""
+    import torch
+    import long_context_anti_amd as rmt
+    cfg = ri.LLAMA_1B.with_segments(16)
+    gu.say(f"[batch] {cfg.name} S=16 B={B} at full width")
+    layers = ri.all_weights(cfg, 0, workers=8)
+    embed = ri.embedding(cfg, 0)
+    xs = [ri.tokens(cfg, 200 + b) for b in range(B)]
+    mems = [ri.initial_memory(cfg, 200 + b) for b in range(B)]
+    dw = rdev.device_weights(cfg, layers, embed)
+    model = rmt.RMTModel(**rdev.model_kwargs(cfg), weights=dw)
+    singles = [_run(model, rdev.segment_inputs(cfg, xs[b]), rdev.f32_tensor(mems[b]), 1, cfg)
+               for b in range(B)]
+    model.set_batch(B)
+    tok_d = torch.stack([rdev.segment_inputs(cfg, x) for x in xs]).contiguous()
+    hb, mb = _run(model, tok_d, rdev.f32_tensor(np.stack(mems)), B, cfg)
+    for b in range(B):
+        assert np.array_equal(hb[b], singles[b][0][0]), f"hidden of sequence {b}"
+        assert np.array_equal(mb[b], singles[b][1][0]), f"memory of sequence {b}"
+        assert np.isfinite(hb[b]).all()
+    model.close()
