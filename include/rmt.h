@@ -292,7 +292,8 @@ int32_t rmt_grouped_gemm(int32_t G, int32_t M, int32_t N, int32_t K, const void*
  *        heads, then the V heads (RoPE, if any, already applied)
  *   out  device bf16 [G][R][Hq*hd]
  * 1 <= G <= 65535, R >= 1, hd in {64, 128}, Hq/Hkv 1, 2 or a positive
- * multiple of 4.
+ * multiple of 4; one cell's qkv rows, R * (Hq+2Hkv) * hd * 2 bytes, below
+ * 2 GiB (RMT_EINVAL otherwise).
  * Errors: RMT_EINVAL, RMT_EUNSUPPORTED (hd or head ratio), RMT_EHIP. */
 int32_t rmt_causal_attention(int32_t G, int32_t R, int32_t n_heads, int32_t n_kv_heads,
                              int32_t head_dim, const void* qkv, void* out, void* stream);

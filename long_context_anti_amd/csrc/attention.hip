@@ -8,8 +8,10 @@
 // one block of QB query rows when Hq / Hkv is a multiple of 4, 2 heads x 2
 // query blocks when it is 2, one head x 4 query blocks when it is 1 (plain
 // multi-head attention).  K and V blocks of 64 keys go through a two-slot LDS
-// ring (the next block is fetched into registers while the current one is
-// used) and are shared by the 4 waves.
+// ring shared by the 4 waves: buffer loads write the next block straight into
+// LDS (no staging registers) while the current one is used.  LDS rows are
+// unpadded; their 16-byte chunks are XOR-swizzled per row so that both the
+// K reads and the transposing V reads are free of bank conflicts.
 //
 // Per 64-key block each wave computes transposed scores S^T = K Q^T with
 // v_mfma_f32_16x16x32_bf16: the S^T accumulator layout is exactly the
@@ -39,6 +41,9 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int KB = 64;            // keys per block
 constexpr float RESCALE_LOG2 = 8.0f;
+constexpr int BUF_FLAGS = 0x00020000;        // raw buffer, 32-bit data format
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   bf16x2 v;
@@ -64,19 +69,39 @@ __device__ __forceinline__ int xcd_remap(int bid, int nb) {
   return xcd * per + (xcd < rem ? xcd : rem) + idx;
 }
 
+// Chunk permutation of LDS row r, the same for K and V: logical 16-byte chunk
+// c sits at physical chunk c ^ swz(r), which depends on r mod 16 only.  K is
+// read 16 bytes per lane from 16 consecutive rows at one logical chunk; V
+// through 8-byte transposing reads that take 32 bytes (a chunk pair) from
+// each of 4 consecutive rows per 16 lanes.  The permutation maps pairs to
+// pairs and keeps both patterns free of bank conflicts for 32 and for 64
+// four-byte banks (checked exhaustively on the host).
+template <int HD>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (HD == 64) return (2 * (r & 3)) ^ (3 * ((r >> 2) & 1)) ^ ((r >> 3) & 1);
+  else return (2 * (r & 7)) | (((r >> 2) ^ (r >> 3)) & 1);
+}
+
+// One wave-wide 16-byte-per-lane buffer load into LDS: lane L's bytes land
+// at dst + 16 L.
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rs, uint8_t* dst, int voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)dst, 16, voff, soff, 0, 0);
+}
+
 template <int HD, int QB, bool CAUSAL>
-__global__ __launch_bounds__(256, 2) void attention_kernel(const uint16_t* __restrict__ qkv,
+__global__ __launch_bounds__(256, HD == 64 ? 4 : 2) void attention_kernel(const uint16_t* __restrict__ qkv,
                                                            uint16_t* __restrict__ out, int R,
                                                            int Hq, int Hkv, float scale_log2) {
   constexpr int QT = QB / 16;     // query tiles of 16 per wave
   constexpr int KS = HD / 32;     // k-steps of 32 over the head dimension
   constexpr int HT = HD / 16;     // head-dimension tiles of 16 in O^T
-  constexpr int LDK = HD + 8;     // K row stride: 16-byte reads of 16 rows hit distinct banks
-  constexpr int LDV = HD + 16;    // V row stride: 8-byte transposing reads of 8 rows tile the banks
-  constexpr int CH = HD / 8;      // 16-byte chunks per key row
-  constexpr int LOADS = KB * CH / 256;   // chunks per thread per block, for K and for V
-  __shared__ __attribute__((aligned(16))) uint16_t sK[2][KB * LDK];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[2][KB * LDV];
+  constexpr int ROWB = HD * 2;    // bytes per K / V row in LDS (unpadded)
+  constexpr int CPR = HD / 8;     // 16-byte chunks per row
+  constexpr int RPL = 64 / CPR;   // rows per wave-wide 1 KiB load
+  constexpr int PPW = KB / RPL / 4;   // such loads per wave per block, for K and for V
+  static_assert(KB * ROWB == 4 * PPW * 1024, "a block is whole 1 KiB loads, dealt evenly");
+  __shared__ __attribute__((aligned(1024))) uint8_t sK[2][KB * ROWB];
+  __shared__ __attribute__((aligned(1024))) uint8_t sV[2][KB * ROWB];
 
   const int tid = (int)threadIdx.x;
   const int lane = tid & 63;
@@ -107,8 +132,6 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const uint16_t* __res
   const int g = lin / (nqg * ny);
   const int ld = (Hq + 2 * Hkv) * HD;
   const uint16_t* base = qkv + (size_t)g * R * ld;
-  const uint16_t* Kp = base + (size_t)(Hq + kvh) * HD;
-  const uint16_t* Vp = base + (size_t)(Hq + Hkv + kvh) * HD;
 
   // Q^T as the B operand: lane holds Q[q0 + 16 qt + c16][32 ks + 8 g4 + 0..7].
   bf16x8 qf[QT][KS];
@@ -142,46 +165,59 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const uint16_t* __res
   const uint32_t one2 = c16 == 0 ? 0x3F803F80u : 0u;   // two bf16 ones, or zeros
   const bf16x8 ones_row = __builtin_bit_cast(bf16x8, u32x4{one2, one2, one2, one2});
 
-  // K/V block loads: thread chunk c -> key c / CH, columns (c % CH) * 8.
-  u32x4 rk[LOADS], rv[LOADS];
-  auto fetch = [&](int k0) __attribute__((always_inline)) {
+  // K/V block loads straight into LDS: wave-wide load q of a block moves
+  // 1 KiB, rows RPL q .. RPL q + RPL - 1, lane L landing at byte 16 L, i.e.
+  // row RPL q + L / CPR at physical chunk L % CPR, which holds that row's
+  // logical chunk (L % CPR) ^ swz(row).  The buffer resource starts at the
+  // block's first row and ends with the cell, so keys past R read as zeros
+  // (their scores are masked, and zero V rows keep P V finite).  Per-lane
+  // offsets are the same for every block.
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  __builtin_assume(wave_u >= 0 && wave_u < 4);
+  // K and V share the row permutation, so a V load is its K load moved by the
+  // uniform Hkv * HD columns (the buffer's scalar offset).
+  int koff[PPW];
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int c = tid + 256 * i;
-      const int r = c / CH;
-      const int cc = (c % CH) * 8;
-      rk[i] = u32x4{0u, 0u, 0u, 0u};
-      rv[i] = u32x4{0u, 0u, 0u, 0u};
-      if (k0 + r < R) {
-        rk[i] = *(const u32x4*)(Kp + (size_t)(k0 + r) * ld + cc);
-        rv[i] = *(const u32x4*)(Vp + (size_t)(k0 + r) * ld + cc);
-      }
+  for (int i = 0; i < PPW; ++i) {
+    const int row = RPL * (wave_u + 4 * i) + lane / CPR;
+    koff[i] = (row * ld + (Hq + kvh) * HD + 8 * ((lane % CPR) ^ swz<HD>(row))) * 2;
+  }
+  const int vdelta = Hkv * HD * 2;
+  auto fetch = [&](int kb, int slot) __attribute__((always_inline)) {
+    const int k0 = kb * KB;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(base + (size_t)k0 * ld), (short)0, (R - k0) * ld * 2, BUF_FLAGS);
+#pragma unroll
+    for (int i = 0; i < PPW; ++i) {
+      const int q = wave_u + 4 * i;
+      load_lds16(rs, &sK[slot][q * 1024], koff[i], 0);
+      load_lds16(rs, &sV[slot][q * 1024], koff[i], vdelta);
     }
   };
-  auto stash = [&](int slot) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int c = tid + 256 * i;
-      const int r = c / CH;
-      const int cc = (c % CH) * 8;
-      *(u32x4*)(&sK[slot][r * LDK + cc]) = rk[i];
-      *(u32x2*)(&sV[slot][r * LDV + cc]) = u32x2{rv[i][0], rv[i][1]};
-      *(u32x2*)(&sV[slot][r * LDV + cc + 4]) = u32x2{rv[i][2], rv[i][3]};
-    }
+  // Every wave waits for its own loads into LDS, then a bare barrier makes
+  // the block visible to the workgroup (and certifies that the other slot's
+  // readers are done).  The empty asm statements keep LDS accesses on their
+  // side of it.
+  auto block_sync = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt((7 << 4) | (0 << 8));   // vmcnt(0) lgkmcnt(0)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
   };
 
   // keys needed by any of the workgroup's query rows: [0, kend)
   const int kend = CAUSAL ? min(qg0 + qw * QB, R) : R;
   const int nkb = (kend + KB - 1) / KB;
-  fetch(0);
-  stash(0);
-  __syncthreads();
+  // The K rows a lane reads are 16 kt + c16, whose permutation is that of c16.
+  const int kswz = swz<HD>(c16);
+  fetch(0, 0);
+  block_sync();
   for (int kb = 0; kb < nkb; ++kb) {
     const int slot = kb & 1;
     const int k0 = kb * KB;
-    if (kb + 1 < nkb) fetch(k0 + KB);
-    const uint16_t* K_ = sK[slot];
-    const uint16_t* V_ = sV[slot];
+    if (kb + 1 < nkb) fetch(kb + 1, slot ^ 1);
+    const uint8_t* K_ = sK[slot];
+    const uint8_t* V_ = sV[slot];
 
     // S^T block: 64 keys x QB queries.  Lane holds keys 16 kt + 4 g4 + j of
     // query column 16 qt + c16 (raw, unscaled scores).
@@ -195,7 +231,7 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const uint16_t* __res
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) {
         const bf16x8 kf = __builtin_bit_cast(
-            bf16x8, *(const u32x4*)(K_ + (16 * kt + c16) * LDK + 32 * ks + 8 * g4));
+            bf16x8, *(const u32x4*)(K_ + (16 * kt + c16) * ROWB + 16 * ((4 * ks + g4) ^ kswz)));
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt)
           s[kt][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[qt][ks], s[kt][qt], 0, 0, 0);
@@ -260,7 +296,9 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const uint16_t* __res
     // key0 + j / 4, columns 4 (j % 4) .. +3; lane i receives column i of the
     // four rows.
     const int tr_row = 4 * g4 + (c16 >> 2);
-    const int tr_col = 4 * (c16 & 3);
+    const int tr_chunk = (c16 & 3) >> 1;     // columns 4 (c16 & 3) .. +3: chunk and byte in it
+    const int tr_byte = 8 * (c16 & 1);
+    const int vswz = swz<HD>(tr_row);        // rows 32 ks2 + tr_row (+ 16): same permutation
 #pragma unroll
     for (int ks2 = 0; ks2 < 2; ++ks2) {
       bf16x8 pf[QT];
@@ -276,11 +314,11 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const uint16_t* __res
       }
 #pragma unroll
       for (int ht = 0; ht < HT; ++ht) {
-        const uint16_t* v0 = V_ + (32 * ks2 + tr_row) * LDV + 16 * ht + tr_col;
+        const uint8_t* v0 = V_ + (32 * ks2 + tr_row) * ROWB + 16 * ((2 * ht + tr_chunk) ^ vswz) + tr_byte;
         const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (__attribute__((address_space(3))) s16x4*)(v0));
         const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) s16x4*)(v0 + 16 * LDV));
+            (__attribute__((address_space(3))) s16x4*)(v0 + 16 * ROWB));
         u32x4 w;
         const u32x2 wl = __builtin_bit_cast(u32x2, lo);
         const u32x2 wh = __builtin_bit_cast(u32x2, hi);
@@ -295,8 +333,7 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const uint16_t* __res
       }
     }
 
-    if (kb + 1 < nkb) stash(slot ^ 1);
-    __syncthreads();
+    block_sync();
   }
 
   // O^T accumulator: lane holds head dims 16 ht + 4 g4 + j of query 16 qt + c16.
@@ -322,8 +359,11 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const uint16_t* __res
 hipError_t launch_attention(const uint16_t* qkv, uint16_t* out, int G, int R, int Hq, int Hkv,
                             int hd, bool causal, hipStream_t stream) {
   if (G == 0 || R == 0) return hipSuccess;
+  if (Hkv < 1 || Hq < 1 || R < 0 || Hq % Hkv != 0) return hipErrorInvalidValue;
   const int rep = Hq / Hkv;
-  if (Hkv < 1 || Hq % Hkv != 0 || !(rep == 1 || rep == 2 || rep % 4 == 0)) return hipErrorInvalidValue;
+  if (!(rep == 1 || rep == 2 || rep % 4 == 0)) return hipErrorInvalidValue;
+  // K/V loads address one cell's rows with 32-bit buffer offsets
+  if ((size_t)R * (size_t)(Hq + 2 * Hkv) * (size_t)hd * 2 > (size_t)INT32_MAX) return hipErrorInvalidValue;
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)hd);
   constexpr int QB = 32;   // measured faster than 64: lower register use, more waves
   const int hw = rep >= 4 ? 4 : rep;

@@ -908,6 +908,8 @@ int32_t rmt_attention(int32_t G, int32_t R, int32_t Hq, int32_t Hkv, int32_t hd,
   if (!head_ratio_ok(Hq, Hkv))
     return fail(RMT_EUNSUPPORTED, "n_heads / n_kv_heads must be 1, 2 or a multiple of 4");
   if ((int64_t)G * R * (Hq + 2 * Hkv) * hd > ((int64_t)1 << 40)) return fail(RMT_EINVAL, "sizes too large");
+  if ((int64_t)R * (Hq + 2 * Hkv) * hd * 2 > INT32_MAX)
+    return fail(RMT_EINVAL, "one cell's qkv rows must stay below 2 GiB (32-bit buffer offsets)");
   HIP_TRY(launch_attention((const uint16_t*)qkv, (uint16_t*)out, G, R, Hq, Hkv, hd, causal != 0,
                            (hipStream_t)stream));
   return RMT_OK;

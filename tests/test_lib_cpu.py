@@ -155,6 +155,8 @@ def test_attention_rejects_bad_arguments():
     assert h.rmt_attention(1, 64, 4, 4, 96, 0, p, p, None) == L.RMT_EUNSUPPORTED
     assert h.rmt_attention(1, 64, 4, 4, 64, 0, None, p, None) == L.RMT_EINVAL
     assert h.rmt_causal_attention(1, 64, 6, 2, 64, p, p, None) == L.RMT_EUNSUPPORTED
+    # one cell's qkv rows above 2 GiB: 65,536 rows x (64 + 2 * 64) heads x 128 x 2 bytes = 3 GiB
+    assert h.rmt_attention(1, 65536, 64, 64, 128, 0, p, p, None) == L.RMT_EINVAL
 
 
 def test_grouped_gemm_rejects_bad_shapes():
