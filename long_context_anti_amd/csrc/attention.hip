@@ -88,7 +88,7 @@ __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rs, uint8_t* d
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)dst, 16, voff, soff, 0, 0);
 }
 
-template <int HD, int QB, bool CAUSAL>
+template <int HD, int QB, bool CAUSAL, bool QPRE>
 __global__ __launch_bounds__(256, HD == 64 ? 4 : 2) void attention_kernel(const uint16_t* __restrict__ qkv,
                                                            uint16_t* __restrict__ out, int R,
                                                            int Hq, int Hkv, float scale_log2) {
@@ -155,12 +155,16 @@ __global__ __launch_bounds__(256, HD == 64 ? 4 : 2) void attention_kernel(const 
   // the bf16 probabilities, from one more MFMA per step whose A operand has a
   // row of ones (row 0, i.e. lanes c16 == 0): element 0 of lane c16 < 16
   // holds the sum for query 16 qt + c16, and the rescaling treats it like O.
+  // QPRE (Q already scaled): the score MFMAs start from c0 = -mref, so they
+  // yield the exponent itself, and mref starts at block 0's row maxima;
+  // otherwise mref starts at -inf and every score takes one FMA.
   float mref[QT];
-  f32x4 osum[QT];
+  f32x4 osum[QT], c0[QT];
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
-    mref[qt] = -INFINITY;
+    mref[qt] = QPRE ? 0.f : -INFINITY;
     osum[qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    c0[qt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   const uint32_t one2 = c16 == 0 ? 0x3F803F80u : 0u;   // two bf16 ones, or zeros
   const bf16x8 ones_row = __builtin_bit_cast(bf16x8, u32x4{one2, one2, one2, one2});
@@ -210,22 +214,13 @@ __global__ __launch_bounds__(256, HD == 64 ? 4 : 2) void attention_kernel(const 
   const int nkb = (kend + KB - 1) / KB;
   // The K rows a lane reads are 16 kt + c16, whose permutation is that of c16.
   const int kswz = swz<HD>(c16);
-  fetch(0, 0);
-  block_sync();
-  for (int kb = 0; kb < nkb; ++kb) {
-    const int slot = kb & 1;
-    const int k0 = kb * KB;
-    if (kb + 1 < nkb) fetch(kb + 1, slot ^ 1);
-    const uint8_t* K_ = sK[slot];
-    const uint8_t* V_ = sV[slot];
-
-    // S^T block: 64 keys x QB queries.  Lane holds keys 16 kt + 4 g4 + j of
-    // query column 16 qt + c16 (raw, unscaled scores).
-    f32x4 s[4][QT];
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-      for (int qt = 0; qt < QT; ++qt) s[kt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // S^T block: 64 keys x QB queries.  Lane holds keys 16 kt + 4 g4 + j of
+  // query column 16 qt + c16: raw scores, or with QPRE scaled scores minus
+  // mref (the accumulation starts from c0).  Then the masked scores: keys
+  // past the cell's end and, when causal, keys after the query.  (A causal
+  // block wholly after this wave's rows masks them all: its probabilities
+  // are exactly zero.)
+  auto scores = [&](const uint8_t* K_, int k0, f32x4 (&s)[4][QT]) __attribute__((always_inline)) {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
@@ -234,25 +229,53 @@ __global__ __launch_bounds__(256, HD == 64 ? 4 : 2) void attention_kernel(const 
             bf16x8, *(const u32x4*)(K_ + (16 * kt + c16) * ROWB + 16 * ((4 * ks + g4) ^ kswz)));
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt)
-          s[kt][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[qt][ks], s[kt][qt], 0, 0, 0);
+          s[kt][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[qt][ks], ks == 0 ? c0[qt] : s[kt][qt],
+                                                              0, 0, 0);
       }
-
-    // Masked scores: keys past the cell's end and, when causal, keys after
-    // the query.  (A causal block wholly after this wave's rows masks them
-    // all: its probabilities are exactly zero.)
     if ((CAUSAL && k0 + KB - 1 > q0) || (k0 + KB > R)) {   // wave-uniform
+      // element (kt, j) holds key k0 + 16 kt + 4 g4 + j: it is masked when
+      // 16 kt + j exceeds a limit that depends on the lane and the query tile
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt) {
-        const int q = q0 + 16 * qt + c16;
+        const int last = CAUSAL ? min(q0 + 16 * qt + c16, R - 1) : R - 1;   // last visible key
+        const int lim = last - k0 - 4 * g4;
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int key = k0 + 16 * kt + 4 * g4 + j;
-            if ((CAUSAL && key > q) || key >= R) s[kt][qt][j] = -INFINITY;
-          }
+          for (int j = 0; j < 4; ++j)
+            if (16 * kt + j > lim) s[kt][qt][j] = -INFINITY;
       }
     }
+  };
+  fetch(0, 0);
+  block_sync();
+  if constexpr (QPRE) {
+    // The reference maxima come from block 0, which every row sees (key 0 is
+    // visible to all): its scores are formed once more inside the loop, then
+    // relative to this reference.
+    f32x4 s[4][QT];
+    scores(sK[0], 0, s);
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        mx = fmaxf(fmaxf(mx, s[kt][qt][0]), s[kt][qt][1]);
+        mx = fmaxf(fmaxf(mx, s[kt][qt][2]), s[kt][qt][3]);
+      }
+      mref[qt] = max_over_groups(mx);
+      c0[qt] = f32x4{-mref[qt], -mref[qt], -mref[qt], -mref[qt]};
+    }
+  }
+  for (int kb = 0; kb < nkb; ++kb) {
+    const int slot = kb & 1;
+    const int k0 = kb * KB;
+    if (kb + 1 < nkb) fetch(kb + 1, slot ^ 1);
+    const uint8_t* K_ = sK[slot];
+    const uint8_t* V_ = sV[slot];
+
+    f32x4 s[4][QT];
+    scores(K_, k0, s);
 
     // Lane-local maxima decide whether to rescale: a query's maximum over its
     // four lane groups crosses the threshold exactly when one lane's does, so
@@ -268,26 +291,52 @@ __global__ __launch_bounds__(256, HD == 64 ? 4 : 2) void attention_kernel(const 
         mx = fmaxf(fmaxf(mx, s[kt][qt][2]), s[kt][qt][3]);
       }
       mloc[qt] = mx;
-      need_rescale |= mx * scale_log2 > mref[qt] + RESCALE_LOG2;
+      if constexpr (QPRE) need_rescale |= mx > RESCALE_LOG2;
+      else need_rescale |= mx * scale_log2 > mref[qt] + RESCALE_LOG2;
     }
-    if (__any(need_rescale)) {
+    if constexpr (QPRE) {
+      // A rescale moves the reference up by what the row maximum exceeds it
+      // and the block's exponents down by the same amount.
+      if (__any(need_rescale)) {
 #pragma unroll
-      for (int qt = 0; qt < QT; ++qt) {
-        const float m2 = fmaxf(mref[qt], max_over_groups(mloc[qt]) * scale_log2);
-        const float corr = __builtin_amdgcn_exp2f(mref[qt] - m2);   // 0 on the first block
-        mref[qt] = m2;
-        osum[qt] *= corr;
+        for (int qt = 0; qt < QT; ++qt) {
+          const float shift = fmaxf(max_over_groups(mloc[qt]), 0.f);
+          const float corr = __builtin_amdgcn_exp2f(-shift);
+          osum[qt] *= corr;
 #pragma unroll
-        for (int ht = 0; ht < HT; ++ht) o[ht][qt] *= corr;
+          for (int ht = 0; ht < HT; ++ht) o[ht][qt] *= corr;
+          mref[qt] += shift;
+          c0[qt] = f32x4{-mref[qt], -mref[qt], -mref[qt], -mref[qt]};
+#pragma unroll
+          for (int kt = 0; kt < 4; ++kt) s[kt][qt] -= shift;
+        }
       }
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) s[kt][qt][j] = __builtin_amdgcn_exp2f(s[kt][qt][j]);
+    } else {
+      if (__any(need_rescale)) {
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) {
+          const float m2 = fmaxf(mref[qt], max_over_groups(mloc[qt]) * scale_log2);
+          const float corr = __builtin_amdgcn_exp2f(mref[qt] - m2);   // 0 on the first block
+          mref[qt] = m2;
+          osum[qt] *= corr;
+#pragma unroll
+          for (int ht = 0; ht < HT; ++ht) o[ht][qt] *= corr;
+        }
+      }
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            s[kt][qt][j] = __builtin_amdgcn_exp2f(fmaf(s[kt][qt][j], scale_log2, -mref[qt]));
     }
-#pragma unroll
-    for (int qt = 0; qt < QT; ++qt)
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          s[kt][qt][j] = __builtin_amdgcn_exp2f(fmaf(s[kt][qt][j], scale_log2, -mref[qt]));
 
     // O^T += V^T P^T over two 32-key steps.  In step ks2, operand slot e < 4
     // is key 32 ks2 + 4 g4 + e and slot e >= 4 is key 32 ks2 + 16 + 4 g4 +
@@ -357,14 +406,14 @@ __global__ __launch_bounds__(256, HD == 64 ? 4 : 2) void attention_kernel(const 
 }  // namespace
 
 hipError_t launch_attention(const uint16_t* qkv, uint16_t* out, int G, int R, int Hq, int Hkv,
-                            int hd, bool causal, hipStream_t stream) {
+                            int hd, bool causal, bool q_prescaled, hipStream_t stream) {
   if (G == 0 || R == 0) return hipSuccess;
   if (Hkv < 1 || Hq < 1 || R < 0 || Hq % Hkv != 0) return hipErrorInvalidValue;
   const int rep = Hq / Hkv;
   if (!(rep == 1 || rep == 2 || rep % 4 == 0)) return hipErrorInvalidValue;
   // K/V loads address one cell's rows with 32-bit buffer offsets
   if ((size_t)R * (size_t)(Hq + 2 * Hkv) * (size_t)hd * 2 > (size_t)INT32_MAX) return hipErrorInvalidValue;
-  const float scale_log2 = 1.4426950408889634f / sqrtf((float)hd);
+  const float scale_log2 = attention_scale_log2(hd);
   constexpr int QB = 32;   // measured faster than 64: lower register use, more waves
   const int hw = rep >= 4 ? 4 : rep;
   const int qw = 4 / hw;
@@ -374,11 +423,21 @@ hipError_t launch_attention(const uint16_t* qkv, uint16_t* out, int G, int R, in
     hipLaunchKernelGGL(kern, grid, dim3(256), 0, stream, qkv, out, R, Hq, Hkv, scale_log2);
   };
   if (hd == 64) {
-    if (causal) go(attention_kernel<64, QB, true>);
-    else go(attention_kernel<64, QB, false>);
+    if (q_prescaled) {
+      if (causal) go(attention_kernel<64, QB, true, true>);
+      else go(attention_kernel<64, QB, false, true>);
+    } else {
+      if (causal) go(attention_kernel<64, QB, true, false>);
+      else go(attention_kernel<64, QB, false, false>);
+    }
   } else if (hd == 128) {
-    if (causal) go(attention_kernel<128, QB, true>);
-    else go(attention_kernel<128, QB, false>);
+    if (q_prescaled) {
+      if (causal) go(attention_kernel<128, QB, true, true>);
+      else go(attention_kernel<128, QB, false, true>);
+    } else {
+      if (causal) go(attention_kernel<128, QB, true, false>);
+      else go(attention_kernel<128, QB, false, false>);
+    }
   } else {
     return hipErrorInvalidValue;
   }

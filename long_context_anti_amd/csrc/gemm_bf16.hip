@@ -372,6 +372,11 @@ __global__ __launch_bounds__((BM / WTM) * (BN / WTN) * 64, 1) void gemm_bf16_ker
           bv[t][e4] = col < a.N ? *(const f32x4*)(bl + col) : f32x4{0.f, 0.f, 0.f, 0.f};
         }
     }
+    // Q columns of the QKV projection take the attention scale (a 32-column
+    // block is wholly Q or not; 1.0 elsewhere leaves the values unchanged).
+    float qs[NI];
+#pragma unroll
+    for (int t = 0; t < NI; ++t) qs[t] = wcol0 + t * 32 < a.q_cols ? a.q_scale : 1.0f;
     const int rc = lane % OCH;
     const int col = wcol0 + rc * 8;
 #pragma unroll
@@ -388,6 +393,7 @@ __global__ __launch_bounds__((BM / WTM) * (BN / WTN) * 64, 1) void gemm_bf16_ker
               for (int e = 0; e < 4; ++e) x[e] = fmaxf(x[e], 0.f);
             }
           }
+          if constexpr (EPI == EPI_BIAS_BF16) x *= qs[t];
           const int c = (t * 4 + e4) ^ swz_o(r32);
           *(u32x2*)(sp + r32 * WTN + c * 8 + half_lane) = u32x2{pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3])};
         }
@@ -431,6 +437,10 @@ __global__ __launch_bounds__((BM / WTM) * (BN / WTN) * 64, 1) void gemm_bf16_ker
               x1[e] = y1;
               x2[e] = y2;
             }
+          }
+          if (col < a.q_cols) {   // Q: the attention scale (a rotation pair is wholly Q or not)
+            x1 *= a.q_scale;
+            x2 *= a.q_scale;
           }
           *(u32x2*)(C + (size_t)row * a.ld_out + col) = u32x2{pack_bf16(x1[0], x1[1]), pack_bf16(x1[2], x1[3])};
           *(u32x2*)(C + (size_t)row * a.ld_out + col2) = u32x2{pack_bf16(x2[0], x2[1]), pack_bf16(x2[2], x2[3])};
@@ -578,6 +588,7 @@ hipError_t launch_gemm_bf16(int epilogue, const GemmArgs& a, const GroupTable& t
   const bool plain_store = epilogue == EPI_STORE_BF16 || epilogue == EPI_BIAS_BF16 ||
                            epilogue == EPI_BIAS_RELU_BF16;
   if (plain_store && a.N % 8 != 0) return hipErrorInvalidValue;   // whole 16-byte output chunks
+  if (a.q_cols < 0 || a.q_cols % 32 != 0) return hipErrorInvalidValue;   // whole 32-column blocks
   switch (epilogue) {
     case EPI_STORE_BF16: launch_epi<EPI_STORE_BF16>(a, tab, stream); break;
     case EPI_QKV_ROPE: launch_epi<EPI_QKV_ROPE>(a, tab, stream); break;

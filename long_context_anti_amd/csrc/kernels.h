@@ -3,6 +3,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <math.h>
 #include <stdint.h>
 
 namespace rmt {
@@ -48,7 +49,14 @@ struct GemmArgs {
   int rope_cols;       // EPI_QKV_ROPE: columns [0, rope_cols) are rotated
   int hd;              // EPI_QKV_ROPE: head dimension (64 or 128)
   const float* bias;   // EPI_*BIAS*: fp32 [Lw][N], row layer[g] added to every output row
+  int q_cols;          // EPI_QKV_ROPE, EPI_BIAS_BF16: columns [0, q_cols) (a multiple of 32)
+  float q_scale;       //   are multiplied by q_scale before the bf16 rounding (0 cols: none)
 };
+
+// Softmax scale of attention in the base-2 domain, log2(e) / sqrt(hd).  The
+// QKV projection folds it into Q for the attention stage of the model, so
+// both sides must use this one value.
+inline float attention_scale_log2(int hd) { return 1.4426950408889634f / sqrtf((float)hd); }
 
 hipError_t launch_gemm_bf16(int epilogue, const GemmArgs& a, const GroupTable& tab,
                             hipStream_t stream);
@@ -76,9 +84,10 @@ hipError_t launch_copy_rows_bf16(int n, int d, const uint16_t* src, float* dst,
                                  hipStream_t stream);
 
 // Attention over each group's R rows, causal or unmasked; Hq / Hkv must be
-// 1, 2 or a multiple of 4.
+// 1, 2 or a multiple of 4.  q_prescaled: Q already carries the softmax scale
+// attention_scale_log2(hd) (the QKV epilogue applied it).
 hipError_t launch_attention(const uint16_t* qkv, uint16_t* out, int G, int R, int Hq, int Hkv,
-                            int hd, bool causal, hipStream_t stream);
+                            int hd, bool causal, bool q_prescaled, hipStream_t stream);
 
 // fp32 linear + bias + GELU cell with the split write-back.
 hipError_t launch_linear_gelu_f32(int G, int R, int d, int split_in, int split_out,

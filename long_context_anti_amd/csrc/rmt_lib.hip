@@ -294,10 +294,12 @@ int32_t run_cells(rmt_model* M, const Cell* cells, int G, const void* tokens, co
     ga.A = M->abuf; ga.B = M->wqkv; ga.M = R; ga.N = NQ; ga.K = d;
     ga.split_in = R; ga.split_out = R; ga.ld_res = 0; ga.ld_out = NQ;
     ga.rope = M->rope; ga.rope_cols = (Hq + Hkv) * hd; ga.hd = hd;
+    ga.q_cols = Hq * hd; ga.q_scale = attention_scale_log2(hd);   // Q leaves with the softmax scale
     LAUNCH(launch_gemm_bf16(EPI_QKV_ROPE, ga, tab, M->stream));
+    ga.q_cols = 0;
     MARK(RMT_STAGE_QKV, 2.0 * rows * d * NQ, rows * d * 2 + G_ * NQ * d * 2 + rows * NQ * 2);
     // causal GQA attention inside each cell
-    LAUNCH(launch_attention(M->qkv, M->att, G, R, Hq, Hkv, hd, true, M->stream));
+    LAUNCH(launch_attention(M->qkv, M->att, G, R, Hq, Hkv, hd, true, true, M->stream));
     MARK(RMT_STAGE_ATTN, 2.0 * G_ * Hq * hd * (double)R * (R + 1), rows * NQ * 2 + rows * Hq * hd * 2);
     // O projection + residual A -> H
     for (int g = 0; g < G; ++g) packed_out[g] = M->hbuf + (size_t)g * R * d;
@@ -323,9 +325,11 @@ int32_t run_cells(rmt_model* M, const Cell* cells, int G, const void* tokens, co
     set_io(nullptr, nullptr, packed_out, nullptr);
     ga.A = M->abuf; ga.B = M->wqkv; ga.M = R; ga.N = NQ; ga.K = d;
     ga.split_in = R; ga.split_out = R; ga.ld_res = 0; ga.ld_out = NQ; ga.bias = M->bqkv;
+    ga.q_cols = H * hd; ga.q_scale = attention_scale_log2(hd);    // Q leaves with the softmax scale
     LAUNCH(launch_gemm_bf16(EPI_BIAS_BF16, ga, tab, M->stream));
+    ga.q_cols = 0;
     MARK(RMT_STAGE_QKV, 2.0 * rows * d * NQ, rows * d * 2 + G_ * NQ * d * 2 + rows * NQ * 2);
-    LAUNCH(launch_attention(M->qkv, M->att, G, R, H, H, hd, false, M->stream));
+    LAUNCH(launch_attention(M->qkv, M->att, G, R, H, H, hd, false, true, M->stream));
     MARK(RMT_STAGE_ATTN, 4.0 * G_ * H * hd * (double)R * R, rows * NQ * 2 + rows * H * hd * 2);
     // O projection + bias + residual A -> hbuf (before LayerNorm 1)
     for (int g = 0; g < G; ++g) packed_out[g] = M->hbuf + (size_t)g * R * d;
@@ -379,10 +383,12 @@ int32_t run_cells(rmt_model* M, const Cell* cells, int G, const void* tokens, co
     set_io(nullptr, nullptr, packed_out, nullptr);
     ga.A = M->abuf; ga.B = M->wqkv; ga.M = R; ga.N = NQ; ga.K = d;
     ga.split_in = R; ga.split_out = R; ga.ld_res = 0; ga.ld_out = NQ; ga.bias = M->bqkv;
+    ga.q_cols = H * hd; ga.q_scale = attention_scale_log2(hd);    // Q leaves with the softmax scale
     LAUNCH(launch_gemm_bf16(EPI_BIAS_BF16, ga, tab, M->stream));
+    ga.q_cols = 0;
     MARK(RMT_STAGE_QKV, 2.0 * rows * d * NQ, rows * d * 2 + G_ * NQ * d * 2 + rows * NQ * 2);
     // unmasked multi-head attention inside each cell
-    LAUNCH(launch_attention(M->qkv, M->att, G, R, H, H, hd, false, M->stream));
+    LAUNCH(launch_attention(M->qkv, M->att, G, R, H, H, hd, false, true, M->stream));
     MARK(RMT_STAGE_ATTN, 4.0 * G_ * H * hd * (double)R * R, rows * NQ * 2 + rows * H * hd * 2);
     // O projection + bias + residual A -> H
     for (int g = 0; g < G; ++g) packed_out[g] = M->hbuf + (size_t)g * R * d;
@@ -910,7 +916,7 @@ int32_t rmt_attention(int32_t G, int32_t R, int32_t Hq, int32_t Hkv, int32_t hd,
   if ((int64_t)G * R * (Hq + 2 * Hkv) * hd > ((int64_t)1 << 40)) return fail(RMT_EINVAL, "sizes too large");
   if ((int64_t)R * (Hq + 2 * Hkv) * hd * 2 > INT32_MAX)
     return fail(RMT_EINVAL, "one cell's qkv rows must stay below 2 GiB (32-bit buffer offsets)");
-  HIP_TRY(launch_attention((const uint16_t*)qkv, (uint16_t*)out, G, R, Hq, Hkv, hd, causal != 0,
+  HIP_TRY(launch_attention((const uint16_t*)qkv, (uint16_t*)out, G, R, Hq, Hkv, hd, causal != 0, false,
                            (hipStream_t)stream));
   return RMT_OK;
 }
