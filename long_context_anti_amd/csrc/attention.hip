@@ -18,11 +18,18 @@
 // B-operand layout that O^T += V^T P^T needs, so probabilities go from the
 // softmax straight into the second MFMA.  V^T operands come from row-major V
 // through the transposing LDS read ds_read_b64_tr_b16.  The softmax is
-// online in fp32 and base 2 (one FMA + one v_exp_f32 per score); the running
-// output is rescaled only when a row maximum grows by more than 2^8, which
-// keeps every probability below 256 and leaves O / l unchanged.  At
+// online in fp32 and base 2.  In the model, Q arrives multiplied by
+// log2(e) / sqrt(hd) (the QKV epilogue applies it before the bf16 rounding)
+// and each score MFMA starts from minus the row's reference maximum, so its
+// result is the exponent itself: one v_exp_f32 per score and nothing else.
+// (That sum of -m and the products is rounded at the scale of max(|m|, the
+// products), which stays far below the bf16 rounding of the probabilities
+// for any realistic score range.)  Called on its own, with unscaled Q, the
+// kernel spends one FMA per score instead.  The running output is rescaled
+// only when a row maximum grows by more than 2^8, which keeps every
+// probability below 256 and leaves O / l unchanged.  At
 // head_dim 64 a key block costs a wave more VALU cycles than MFMA cycles
-// (v_exp_f32 issues at a quarter of the FMA rate), so VALU work is kept
+// (v_exp_f32 issues at about a third of the FMA rate, measured), so VALU work is kept
 // off the per-block path where it can be: the row sums l come from one more
 // MFMA per step against a row of ones -- the sum of exactly the bf16
 // probabilities that multiply V -- and the row maxima cross lane groups
