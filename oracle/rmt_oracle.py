@@ -29,7 +29,7 @@ Recurrent Memory Transformers for Long Contexts" (catalogue record, abstract).
   segment count up): its cells have m + n' rows, the first n' become X and
   the last m become M, the same split rule as every other cell.
 
-Readings where the pages are silent (each is listed in the design doc):
+Readings where the pages are silent (the design notes list each one):
   - the cell function is the one each workload defines: linear+GELU (tiny
     grid), RMSNorm+SwiGLU with residual (attention-free), or a pre-norm
     LLaMA block (RMSNorm, QKV, RoPE, causal GQA, O, RMSNorm, SwiGLU);
