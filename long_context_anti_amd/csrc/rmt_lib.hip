@@ -211,7 +211,8 @@ int32_t run_cells(rmt_model* M, const Cell* cells, int G, const void* tokens, co
   const rmt_config& c = M->cfg;
   const int L = c.L, S = c.S, n = c.n, m = c.m, d = c.d;
   // Every cell of one launch has the same number of segment rows: n, or
-  // n_last for the cells of a short last segment (the driver keeps them apart).
+  // n_last for the cells of a short last segment (rmt_forward_diagonal
+  // launches those on their own).
   const int ns = cells[0].s == S - 1 ? M->n_last : n;
   const int R = ns + m;
   const int k = cells[0].l + cells[0].s;
