@@ -305,3 +305,31 @@ def test_encoder_rows_with_a_large_mean():
     gu.say(f"  rel L2 (offset removed) hidden {e_h:.3e} mem {e_m:.3e}")
     assert e_h <= BF16_TOL and e_m <= BF16_TOL
     run.close()
+
+
+DEGENERATE_GRIDS = [(1, 5), (5, 1), (7, 2), (2, 7)]
+
+
+@pytest.mark.parametrize("base", [ri.TINY_LINEAR_GELU, ri.TINY_LLAMA, ri.TINY_ENCODER], ids=lambda c: c.name)
+@pytest.mark.parametrize("L,S", DEGENERATE_GRIDS, ids=lambda v: str(v))
+def test_degenerate_grids(base, L, S):
+    """Grid shapes at the edges of the schedule: one layer (every diagonal a
+    single cell, the diagonal order equal to the sequential one), one segment
+    (likewise, layer by layer), and grids much deeper than long or the
+    reverse, which are all ramp (no diagonal holds min(L, S) cells for long).
+    Against the oracle within the dtype's gate; diagonal == sequential
+    bitwise."""
+    cfg = dataclasses.replace(base, name=f"{base.name}_L{L}_S{S}", L=L, S=S)
+    gu.say(f"[parity] {cfg.name} L={L} S={S}")
+    run = gu.GpuRun(cfg)
+    hd, md = run.run("diagonal")
+    hs, ms = run.run("sequential")
+    ho, mo = _oracle(cfg, run)
+    if cfg.dtype == ri.F32:
+        e_h, e_m, tol = gu.normwise(hd, ho), gu.normwise(md, mo), F32_TOL
+    else:
+        e_h, e_m, tol = gu.rel_l2(hd, ho), gu.rel_l2(md, mo), BF16_TOL
+    gu.say(f"  hidden {e_h:.3e} mem {e_m:.3e} (tol {tol})")
+    assert e_h <= tol and e_m <= tol
+    assert np.array_equal(hd, hs) and np.array_equal(md, ms)
+    run.close()
