@@ -87,7 +87,8 @@ __device__ __forceinline__ int xcd_remap(int bid, int nb) {
 
 // BM x BN output tile per workgroup; WTM x WTN is one wave's sub-tile and the
 // workgroup has one wave per sub-tile.
-template <int EPI, int BM, int WTM, int WTN>
+// BNT: weight slices are loaded with the non-temporal policy (see launch_one).
+template <int EPI, int BM, int WTM, int WTN, bool BNT>
 __global__ __launch_bounds__((BM / WTM) * (BN / WTN) * 64, 1) void gemm_bf16_kernel(
     GemmArgs a, GroupTable tab) {
   constexpr int STAGE_BYTES = (BM + BN) * ROWB;
@@ -172,7 +173,12 @@ __global__ __launch_bounds__((BM / WTM) * (BN / WTN) * 64, 1) void gemm_bf16_ker
         const int row = (is_a ? q : q - A_LOADS) * RPI + lrow;
         if (k0 + 8 * (lp ^ swz(row)) >= K) off = is_a ? a_bytes : b_bytes;
       }
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(is_a ? ra : rb, (lds_ptr_t)(sbase + q * 1024), 16, off, 0, 0, 0);
+      if constexpr (BNT) {
+        if (is_a) __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(sbase + q * 1024), 16, off, 0, 0, 0);
+        else __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(sbase + q * 1024), 16, off, 0, 0, 2);
+      } else {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(is_a ? ra : rb, (lds_ptr_t)(sbase + q * 1024), 16, off, 0, 0, 0);
+      }
     }
   };
   auto issue = [&](int kt, int stage) __attribute__((always_inline)) {
@@ -520,11 +526,20 @@ __global__ __launch_bounds__((BM / WTM) * (BN / WTN) * 64, 1) void gemm_bf16_ker
   }
 }
 
+// Weight slices take the non-temporal policy when K <= 2048: a cell's
+// activations (M x K bf16, re-read by every column tile of the cell) are then
+// about one XCD's L2, and streaming the weights past them saves ~1% on those
+// GEMMs.  With longer K the activations exceed L2 anyway, and the reuse of a
+// weight panel by the cell's row tiles matters more (the hint cost the
+// K = 8192 projections 0.4-2%).
 template <int EPI, int BM, int WTM, int WTN>
 void launch_one(const GemmArgs& a, const GroupTable& tab, hipStream_t stream) {
   const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN) * tab.G;
   constexpr int threads = (BM / WTM) * (BN / WTN) * 64;
-  hipLaunchKernelGGL((gemm_bf16_kernel<EPI, BM, WTM, WTN>), dim3(tiles), dim3(threads), 0, stream, a, tab);
+  if (a.K <= 2048)
+    hipLaunchKernelGGL((gemm_bf16_kernel<EPI, BM, WTM, WTN, true>), dim3(tiles), dim3(threads), 0, stream, a, tab);
+  else
+    hipLaunchKernelGGL((gemm_bf16_kernel<EPI, BM, WTM, WTN, false>), dim3(tiles), dim3(threads), 0, stream, a, tab);
 }
 
 // Tile shapes.  The operand bytes a tile pulls from L2 per MFMA fall as the
