@@ -109,3 +109,35 @@ def test_causal_flag_of_rmt_attention_matches_causal_entry():
     torch.cuda.synchronize()
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_sharp_attention_rescales(causal):
+    """Q and K with std 6: scaled scores spread over ~50 units of log2, so the
+    running reference maximum is raised (and O, l rescaled) many times per
+    row; the result still matches the fp64 oracle on the same bf16 inputs."""
+    import torch
+    import long_context_anti_amd as rmt
+    G, R, Hq, Hkv, hd = 2, 700, 8, 2, 64
+    gu.say(f"[attention] sharp scores, causal={causal}")
+    rng = np.random.default_rng(77)
+    W = (Hq + 2 * Hkv) * hd
+    x = rng.standard_normal((G, R, W))
+    x[:, :, :(Hq + Hkv) * hd] *= 6.0          # Q and K
+    qkv = ri.round_bf16(x.astype(np.float32))
+    out_d = torch.empty((G, R, Hq * hd), dtype=torch.bfloat16, device="cuda")
+    rmt.attention(rdev.bf16_tensor(qkv), out_d, Hq, Hkv, hd, causal=causal)
+    torch.cuda.synchronize()
+    out = _bf16_to_np(out_d)
+    for g in range(G):
+        q = qkv[g, :, :Hq * hd].reshape(R, Hq, hd).astype(np.float64)
+        k = qkv[g, :, Hq * hd:(Hq + Hkv) * hd].reshape(R, Hkv, hd).astype(np.float64)
+        v = qkv[g, :, (Hq + Hkv) * hd:].reshape(R, Hkv, hd).astype(np.float64)
+        if causal:
+            ref = orc.causal_gqa_attention(q, k, v)
+        else:
+            ref = orc.full_mha(q, np.repeat(k, Hq // Hkv, axis=1), np.repeat(v, Hq // Hkv, axis=1))
+        err = np.linalg.norm(out[g] - ref) / np.linalg.norm(ref)
+        gu.say(f"  cell {g}: rel L2 {err:.3e}")
+        assert np.isfinite(out[g]).all()
+        assert err <= 1e-2, err

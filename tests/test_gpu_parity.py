@@ -333,3 +333,23 @@ def test_degenerate_grids(base, L, S):
     assert e_h <= tol and e_m <= tol
     assert np.array_equal(hd, hs) and np.array_equal(md, ms)
     run.close()
+
+
+@pytest.mark.parametrize("w_std", [0.1, 0.15])
+def test_llama_sharp_attention(w_std):
+    """Weights 2-3x the tiny grid's spread: the cells' scaled scores reach tens
+    of log2 units, and in the model's attention (Q prescaled, exponents formed
+    from minus the reference maximum inside the score MFMA) the reference is
+    raised after block 0 for some rows, a path the smaller spreads never take.
+    One layer and one segment against the oracle, so no recurrence amplifies
+    the bf16 differences."""
+    cfg = dataclasses.replace(ri.TINY_LLAMA, name=f"tiny_llama_sharp_{w_std}", L=1, S=1, w_std=w_std)
+    gu.say(f"[parity] {cfg.name}")
+    run = gu.GpuRun(cfg)
+    hd, md = run.run("diagonal")
+    ho, mo = _oracle(cfg, run)
+    e_h, e_m = gu.rel_l2(hd, ho), gu.rel_l2(md, mo)
+    gu.say(f"  rel L2 hidden {e_h:.3e} mem {e_m:.3e}")
+    assert np.isfinite(hd).all() and np.isfinite(md).all()
+    assert e_h <= BF16_TOL and e_m <= BF16_TOL
+    run.close()
