@@ -335,15 +335,17 @@ def test_degenerate_grids(base, L, S):
     run.close()
 
 
-@pytest.mark.parametrize("w_std", [0.1, 0.15])
-def test_llama_sharp_attention(w_std):
-    """Weights 2-3x the tiny grid's spread: the cells' scaled scores reach tens
+@pytest.mark.parametrize("base,w_std", [(ri.TINY_LLAMA, 0.1), (ri.TINY_LLAMA, 0.15),
+                                        (ri.TINY_LLAMA_HD128, 0.15), (ri.TINY_ENCODER, 0.15)],
+                         ids=lambda v: getattr(v, "name", str(v)))
+def test_llama_sharp_attention(base, w_std):
+    """Weights 2-3x the tiny grids' spread: the cells' scaled scores reach tens
     of log2 units, and in the model's attention (Q prescaled, exponents formed
     from minus the reference maximum inside the score MFMA) the reference is
     raised after block 0 for some rows, a path the smaller spreads never take.
     One layer and one segment against the oracle, so no recurrence amplifies
     the bf16 differences."""
-    cfg = dataclasses.replace(ri.TINY_LLAMA, name=f"tiny_llama_sharp_{w_std}", L=1, S=1, w_std=w_std)
+    cfg = dataclasses.replace(base, name=f"{base.name}_sharp_{w_std}", L=1, S=1, w_std=w_std)
     gu.say(f"[parity] {cfg.name}")
     run = gu.GpuRun(cfg)
     hd, md = run.run("diagonal")
