@@ -69,22 +69,22 @@ CELL_ENCODER = 3
 
 
 # ---------------------------------------------------------------------------
-# Schedule: skill page, *Implementation*, the scheduler's diagonal enumeration.
-# For each diagonal index d in [0, L+S-1), walk the layers in ascending order,
-# set s = d - l and keep (l, s) when 0 <= s < S; keep only non-empty diagonals.
+# Schedule.  Cell (l, s) needs (l-1, s) and (l, s-1) and nothing else
+# (skill page, *Architecture Overview*, Dependency Preservation), so every
+# cell can run one step after both of them: on anti-diagonal l + s
+# (*Architecture Overview*, Diagonal Reorganization).  The grid has L + S - 1
+# anti-diagonals, none of them empty.
 # ---------------------------------------------------------------------------
 
 def schedule(L: int, S: int) -> List[List[Tuple[int, int]]]:
-    diagonals = []
-    for d in range(L + S - 1):
-        diagonal = []
-        for l in range(L):
-            s = d - l
-            if 0 <= s < S:
-                diagonal.append((l, s))
-        if diagonal:
-            diagonals.append(diagonal)
-    return diagonals
+    """Every cell of the L x S grid, grouped by its anti-diagonal l + s.
+    Within a diagonal the cells are listed layer-ascending (the order is
+    immaterial to the result; fixing it makes tables comparable)."""
+    by_diagonal: List[List[Tuple[int, int]]] = [[] for _ in range(L + S - 1)]
+    for l in range(L):
+        for s in range(S):
+            by_diagonal[l + s].append((l, s))
+    return by_diagonal
 
 
 def schedule_table(L: int, S: int) -> Tuple[np.ndarray, np.ndarray]:

@@ -37,7 +37,7 @@ _KIND = {
     "w": 1, "b": 2, "x0": 3, "mem0": 4, "wqkv": 5, "wo": 6, "wg": 7, "wu": 8,
     "wd": 9, "embed": 10, "tokens": 11, "gemm_a": 12, "gemm_b": 13,
     "bqkv": 14, "bo": 15, "w1": 16, "b1": 17, "w2": 18, "b2": 19,
-    "ln1_g": 20, "ln1_b": 21, "ln2_g": 22, "ln2_b": 23,
+    "ln1_g": 20, "ln1_b": 21, "ln2_g": 22, "ln2_b": 23, "g1": 24, "g2": 25,
 }
 
 
@@ -70,6 +70,7 @@ class RMTConfig:
     b_std: float = 0.02       # encoder cell: bias std
     ln_std: float = 0.1       # encoder cell: LayerNorm gain spread around 1, and shift std
     post_norm: bool = False   # encoder cell: LayerNorm after each residual add (torch's default)
+    gain_std: float = 0.0     # RMSNorm gains: 1 (LLaMA initialisation) when 0, else 1 + N(0, gain_std)
 
     @property
     def R(self) -> int:
@@ -121,18 +122,20 @@ LLAMA_8B = RMTConfig(
     V=128000, w_std=0.02, mem_std=0.02)
 
 # Small grids that still span several GEMM/attention tiles with ragged tails
-# (R = 240 rows: 128 + 112; widths that are not multiples of 256).
+# (R = 240 rows: 128 + 112; widths that are not multiples of 256).  Their
+# RMSNorm gains are drawn around 1, so that the two norms of a cell differ and
+# a dropped or exchanged gain changes the result.
 TINY_SWIGLU = RMTConfig(
     name="tiny_norm_swiglu", wid=20, cell=CELL_NORM_SWIGLU, dtype=BF16,
-    L=3, S=5, n=200, m=40, d=192, F=320, w_std=0.05, x_std=1.0, mem_std=1.0)
+    L=3, S=5, n=200, m=40, d=192, F=320, w_std=0.05, x_std=1.0, mem_std=1.0, gain_std=0.1)
 TINY_LLAMA = RMTConfig(
     name="tiny_llama", wid=30, cell=CELL_LLAMA, dtype=BF16,
     L=3, S=4, n=200, m=40, d=256, Hq=4, Hkv=1, hd=64, F=384, V=1000,
-    w_std=0.05, mem_std=0.05)
+    w_std=0.05, mem_std=0.05, gain_std=0.1)
 TINY_LLAMA_HD128 = RMTConfig(
     name="tiny_llama_hd128", wid=31, cell=CELL_LLAMA, dtype=BF16,
     L=2, S=3, n=136, m=24, d=512, Hq=4, Hkv=1, hd=128, F=448, V=777,
-    w_std=0.04, mem_std=0.04)
+    w_std=0.04, mem_std=0.04, gain_std=0.1)
 
 # The encoder-layer cell of the skill page's Implementation sketch
 # (nn.TransformerEncoderLayer with a 4x feed-forward), at the 1B width and
@@ -234,14 +237,19 @@ def layer_weights(cfg: RMTConfig, layer: int, seed: int = 0) -> Dict[str, np.nda
             "w2": normal((F, d), cfg.w_std, seed, cfg.wid, "w2", layer, bf),
             "b2": normal((d,), cfg.b_std, seed, cfg.wid, "b2", layer, bf),
         }
+    def gain(kind):
+        if cfg.gain_std == 0.0:
+            return np.ones((d,), np.float32)
+        return (1.0 + normal((d,), cfg.gain_std, seed, cfg.wid, kind, layer, bf)).astype(np.float32)
+
     out = {
-        "g2": np.ones((d,), np.float32),
+        "g2": gain("g2"),
         "wg": normal((d, cfg.F), cfg.w_std, seed, cfg.wid, "wg", layer, bf),
         "wu": normal((d, cfg.F), cfg.w_std, seed, cfg.wid, "wu", layer, bf),
         "wd": normal((cfg.F, d), cfg.w_std, seed, cfg.wid, "wd", layer, bf),
     }
     if cfg.cell == CELL_LLAMA:
-        out["g1"] = np.ones((d,), np.float32)
+        out["g1"] = gain("g1")
         out["wqkv"] = normal((d, cfg.n_qkv), cfg.w_std, seed, cfg.wid, "wqkv", layer, bf)
         out["wo"] = normal((cfg.Hq * cfg.hd, d), cfg.w_std, seed, cfg.wid, "wo", layer, bf)
     return out

@@ -159,6 +159,28 @@ def test_mutation_swapped_gate_up(monkeypatch):
     assert _fails(pins.pin_single_segment_against_torch, ri.TINY_LLAMA)
 
 
+def _swap_gains(w):
+    w = dict(w)
+    w["g1"], w["g2"] = w["g2"], w["g1"]
+    return w
+
+
+def test_mutation_llama_norm_gains_exchanged(monkeypatch):
+    """The two RMSNorms of a LLaMA cell read each other's gain (the tiny grids
+    draw the gains around 1, so the two differ)."""
+    real = orc.cell_llama
+    monkeypatch.setattr(orc, "cell_llama", lambda A, w, *a: real(A, _swap_gains(w), *a))
+    assert _fails(pins.pin_single_segment_against_torch, ri.TINY_LLAMA)
+    assert _fails(pins.pin_single_segment_against_torch, ri.TINY_LLAMA_HD128)
+
+
+@pytest.mark.parametrize("cfg", [ri.TINY_LLAMA, ri.TINY_SWIGLU], ids=lambda c: c.name)
+def test_mutation_rmsnorm_gain_dropped(monkeypatch, cfg):
+    real = orc.rms_norm
+    monkeypatch.setattr(orc, "rms_norm", lambda x, g, eps: real(x, np.ones_like(g), eps))
+    assert _fails(pins.pin_single_segment_against_torch, cfg)
+
+
 def test_mutation_dropped_residual(monkeypatch):
     monkeypatch.setattr(orc, "cell_norm_swiglu",
                         lambda A, w, eps: orc.swiglu(orc.rms_norm(A, w["g2"], eps), w["wg"], w["wu"], w["wd"]))
