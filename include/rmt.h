@@ -21,7 +21,10 @@
  *     message describing the last error is returned by rmt_last_error().
  *   - "device" pointers are HIP device allocations on the current device
  *     (for example torch tensors' data_ptr()); "host" pointers are CPU memory.
- *   - The library never takes ownership of caller memory.  Device work is
+ *   - The library never takes ownership of caller memory and never allocates
+ *     device memory: packed weights and the activation workspace live in
+ *     buffers the caller allocates (for example torch tensors) and attaches
+ *     with rmt_model_bind, sized by rmt_workspace_bytes.  Device work is
  *     queued on the caller's HIP stream and returns before it finishes;
  *     faults inside kernels surface at the caller's next synchronisation.
  *   - Matrices are row-major.  Mathematical weights are W[d_in][d_out], so a
@@ -42,7 +45,8 @@ extern "C" {
 #define RMT_EINVAL (-1)        /* bad argument: sizes, null pointers, ranges      */
 #define RMT_EUNSUPPORTED (-2)  /* valid but not implemented (see each call)       */
 #define RMT_EHIP (-3)          /* a HIP runtime call failed (message has details) */
-#define RMT_ENOMEM (-4)        /* device allocation failed                         */
+#define RMT_ENOMEM (-4)        /* reserved (the library allocates no device memory) */
+#define RMT_EWORKSPACE (-5)    /* a buffer the call needs is not bound, or too small */
 
 /* Cell kinds: what one (layer, segment) cell computes on A [R x d].
  *   LINEAR_GELU  Y = GELU_erf(A W_l + b_l)                        (fp32 only)
@@ -91,10 +95,11 @@ typedef struct rmt_config {
                           MHA(A)), Y = LN2(H + FFN(H)); must be 0 otherwise   */
 } rmt_config;
 
-/* Mathematical-layout weights, stacked over layers (device pointers).  They
- * are read once by rmt_model_create, which packs them into the library's own
- * device layout; the caller may free them afterwards -- except `embed`,
- * which the model keeps borrowing and must outlive it.  Element type of the
+/* Mathematical-layout weights, stacked over layers (device pointers).
+ * rmt_model_create records the pointers; rmt_model_bind(RMT_BUF_WEIGHTS)
+ * packs them into the caller's weight buffer, after which the caller may free
+ * them -- except `embed`, which every forward call reads and which must
+ * outlive the model.  Element type of the
  * matrices: fp32 for RMT_F32 models; bf16 (or fp32, rounded to nearest even
  * while packing) for RMT_BF16 models, as given by `weight_dtype`.  Gains,
  * shifts and biases (g1, g2, b, beta*, b*) are always fp32.  Unused fields
@@ -155,17 +160,47 @@ typedef struct rmt_model rmt_model;
  * exactly one pointer is NULL. */
 int32_t rmt_diag_schedule(int32_t L, int32_t S, int32_t* diag_ptr, int32_t* cells);
 
-/* Create a model on the current HIP device: validates `cfg`, allocates the
- * packed weights and a workspace for one sequence (per-launch buffers for up
- * to min(32, L) cells, independent of S), packs `w` on `stream` (a
- * hipStream_t; NULL = default stream) and waits for the packing to finish.
- * *out receives the handle.
+/* Create a model handle: validates `cfg` and the presence of the weights the
+ * cell needs, records the weight pointers (borrowed) and the stream later
+ * device work is queued on (a hipStream_t; NULL = the default stream), and
+ * sets *out.  Allocates only the host-side handle: no device memory and no
+ * device work (both come with rmt_model_bind).
  * Errors: RMT_EINVAL (bad sizes or NULL weights the cell needs),
  * RMT_EUNSUPPORTED (Hq/Hkv not 1, 2 or a multiple of 4, an ENCODER with
- * n_kv_heads != n_heads, hd not 64/128, widths not multiples of 64, ...),
- * RMT_ENOMEM, RMT_EHIP. */
+ * n_kv_heads != n_heads, hd not 64/128, widths not multiples of 64, ...). */
 int32_t rmt_model_create(const rmt_config* cfg, const rmt_weights* w, void* stream,
                          rmt_model** out);
+
+/* Caller-owned device buffers of a model.
+ *   RMT_BUF_WEIGHTS    the packed weights ([L][N][K] bf16, K contiguous),
+ *                      gains, shifts and biases, the RoPE table and the
+ *                      bad-token flag: fixed by the config, independent of S
+ *                      and of the batch.
+ *   RMT_BUF_WORKSPACE  the activations: per-launch buffers for up to
+ *                      min(32, B L) cells (normalised rows, Q/K/V, attention
+ *                      output, H, U), the X ping-pong pair of every sequence
+ *                      and a second memory buffer [B][L][m][d]; depends on
+ *                      L, R, d, F and the batch B, not on S.
+ * rmt_workspace_bytes writes the size in bytes that `kind` needs for the
+ * model's current batch.  Errors: RMT_EINVAL. */
+#define RMT_BUF_WEIGHTS 0
+#define RMT_BUF_WORKSPACE 1
+int32_t rmt_workspace_bytes(const rmt_model* model, int32_t kind, size_t* bytes);
+
+/* Attach a caller-allocated device buffer (256-byte aligned, at least
+ * rmt_workspace_bytes(kind) bytes) to the model; it is borrowed, must
+ * outlive every call queued on it, and is never freed by the library.
+ *   RMT_BUF_WEIGHTS: packs the weights recorded by rmt_model_create into the
+ *     buffer on the model's stream and waits for the packing to finish (the
+ *     mathematical-layout weights other than `embed` may be freed after
+ *     this returns).  Bound once per model.
+ *   RMT_BUF_WORKSPACE: the activation workspace; may be re-bound at any time
+ *     (calls already queued keep using the previous buffer).  Its contents
+ *     need no initialisation: every forward call writes each workspace byte
+ *     it reads.
+ * Errors: RMT_EINVAL (NULL model or buffer, misaligned buffer, bad kind,
+ * weights bound twice), RMT_EWORKSPACE (buffer too small), RMT_EHIP. */
+int32_t rmt_model_bind(rmt_model* model, int32_t kind, void* buffer, size_t bytes);
 
 /* Re-target the model to S whole segments (T = S*n tokens) per forward call
  * (no allocation). */
@@ -188,16 +223,18 @@ int32_t rmt_model_set_tokens(rmt_model* model, int64_t T);
  * that one sequence leaves short of L cells.  The forward calls' buffers gain
  * a leading [B]: tokens [B][T] (or [B][T][d]), mem0 and out->mem
  * [B][L][m][d], out->hidden [B][T][d]; sequence b's results equal a B = 1
- * run on its inputs, bit for bit.  Synchronises the model's stream and
- * reallocates the workspace (hipMalloc / hipFree) when B changes.
- * Errors: RMT_EINVAL (NULL model, B < 1, sizes too large), RMT_ENOMEM,
- * RMT_EHIP. */
+ * run on its inputs, bit for bit.  Allocates nothing: the workspace a batch
+ * needs grows with B (rmt_workspace_bytes), and a bound workspace too small
+ * for the new B must be replaced (rmt_model_bind) before the next forward
+ * call, which otherwise returns RMT_EWORKSPACE.
+ * Errors: RMT_EINVAL (NULL model, B < 1, sizes too large). */
 int32_t rmt_model_set_batch(rmt_model* model, int32_t B);
 
 /* Queue later forward calls on `stream` (a hipStream_t). */
 int32_t rmt_model_set_stream(rmt_model* model, void* stream);
 
-/* Bytes of device memory the model holds (packed weights + workspace). */
+/* Bytes of the caller's device buffers bound to the model (weights +
+ * workspace). */
 int32_t rmt_model_device_bytes(const rmt_model* model, size_t* bytes);
 
 /* Diagonal-batched forward pass over B sequences (rmt_model_set_batch;
@@ -212,7 +249,8 @@ int32_t rmt_model_device_bytes(const rmt_model* model, size_t* bytes);
  * For every diagonal k the library launches, on the model's stream, one
  * grouped kernel per stage covering all of the diagonal's cells (skill page,
  * Architecture Overview: GroupedGEMM Operations, GPU Kernel Optimization).
- * Asynchronous.  Errors: RMT_EINVAL (NULL pointers), RMT_EHIP. */
+ * Asynchronous.  Errors: RMT_EINVAL (NULL pointers), RMT_EWORKSPACE (no
+ * weight buffer bound, or no workspace large enough for the batch), RMT_EHIP. */
 int32_t rmt_forward_diagonal(rmt_model* model, const void* tokens, const void* mem0,
                              rmt_output* out);
 
@@ -261,8 +299,8 @@ int32_t rmt_model_stage_times(rmt_model* model, double* ms, int64_t* launches, d
 int32_t rmt_model_stage_times_groups(rmt_model* model, int32_t g_lo, int32_t g_hi, double* ms,
                                      int64_t* launches, double* flops, double* bytes);
 
-/* Release the model's device memory (the caller's stream is synchronised
- * first).  NULL is accepted. */
+/* Release the handle (the model's stream is synchronised first).  The bound
+ * buffers are the caller's and are left as they are.  NULL is accepted. */
 int32_t rmt_model_destroy(rmt_model* model);
 
 /* Pack mathematical-layout weights src [L][K][N] (fp32 or bf16 per
@@ -273,15 +311,19 @@ int32_t rmt_pack_weight(int32_t L, int32_t K, int32_t N, const void* src, int32_
                         void* dst, void* stream);
 
 /* The grouped GEMM on its own (Architecture Overview: GroupedGEMM Operations):
- * C_g = A_g B_{layer[g]} for g < G, in one launch, bf16 MFMA with fp32
- * accumulation, bf16 result (round to nearest even).
- *   A           device bf16 [G][M][K]
- *   B           device bf16 [Lw][N][K] as produced by rmt_pack_weight
- *   group_layer host int32 [G], each in [0, Lw) (not checked against Lw)
- *   C           device bf16 [G][M][N]
- * 1 <= G <= 32 per call, K a multiple of 8, N a multiple of 64. */
-int32_t rmt_grouped_gemm(int32_t G, int32_t M, int32_t N, int32_t K, const void* A,
-                         const void* B, const int32_t* group_layer, void* C, void* stream);
+ * C_g = A_g B_{layer[g]} for g < G, in one launch, MFMA with fp32
+ * accumulation, result rounded to nearest even.
+ *   A           device [G][M][K]
+ *   B           device [Lw][N][K] as produced by rmt_pack_weight
+ *   group_layer host int32 [G], each in [0, Lw)
+ *   C           device [G][M][N]
+ *   dtype       element type of A, B and C: RMT_BF16
+ * 1 <= G <= 32 per call, K a multiple of 8, N a multiple of 64.
+ * Errors: RMT_EINVAL (sizes, NULL pointers, a layer index outside [0, Lw)),
+ * RMT_EUNSUPPORTED (dtype), RMT_EHIP. */
+int32_t rmt_grouped_gemm(int32_t G, int32_t M, int32_t N, int32_t K, int32_t Lw, const void* A,
+                         const void* B, const int32_t* group_layer, void* C, int32_t dtype,
+                         void* stream);
 
 /* Causal grouped-query attention on its own, over G cells of R rows each, in
  * one launch (the attention stage of the LLAMA cell; see the cell kinds

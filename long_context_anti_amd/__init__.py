@@ -13,9 +13,9 @@ from typing import Dict, Optional
 import numpy as np
 
 from . import _lib
-from ._lib import (RMT_BF16, RMT_CELL_ENCODER, RMT_CELL_LINEAR_GELU, RMT_CELL_LLAMA,
-                   RMT_CELL_NORM_SWIGLU, RMT_F32, STAGES, RmtConfig, RmtError, RmtOutput, RmtWeights,
-                   check, lib)
+from ._lib import (RMT_BF16, RMT_BUF_WEIGHTS, RMT_BUF_WORKSPACE, RMT_CELL_ENCODER,
+                   RMT_CELL_LINEAR_GELU, RMT_CELL_LLAMA, RMT_CELL_NORM_SWIGLU, RMT_F32, STAGES,
+                   RmtConfig, RmtError, RmtOutput, RmtWeights, check, lib)
 
 __all__ = [
     "RMTModel", "RmtError", "diag_schedule", "grouped_gemm", "pack_weight", "causal_attention",
@@ -27,6 +27,32 @@ __all__ = [
 
 def _ptr(t) -> Optional[C.c_void_p]:
     return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _require(t, name: str, dtypes, shape, device: bool = True) -> None:
+    """Raise ValueError unless `t` is a contiguous tensor of one of `dtypes`
+    and of `shape` (a tuple; None matches any extent), on the GPU unless
+    `device` is False."""
+    if t is None:
+        raise ValueError(f"{name} is required")
+    dtypes = dtypes if isinstance(dtypes, tuple) else (dtypes,)
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {' or '.join(str(d) for d in dtypes)}")
+    if len(t.shape) != len(shape) or any(w is not None and int(v) != w for v, w in zip(t.shape, shape)):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if device and not t.is_cuda:
+        raise ValueError(f"{name} must be a CUDA (HIP) device tensor")
+
+
+def _require_all(specs) -> None:
+    """_require over (tensor, name, dtypes, shape) specs: every dtype and shape
+    first, then placement, so that the message names the first real mismatch."""
+    for spec in specs:
+        _require(*spec, device=False)
+    for spec in specs:
+        _require(*spec)
 
 
 def _stream(stream) -> C.c_void_p:
@@ -49,24 +75,29 @@ def pack_weight(src, dst, stream=None) -> None:
     """src [L, K, N] (fp32 or bf16, device) -> dst [L, N, K] bf16 (device)."""
     import torch
     L, K, N = src.shape
-    assert dst.shape == (L, N, K) and dst.dtype == torch.bfloat16
-    assert src.is_contiguous() and dst.is_contiguous()
+    _require_all([(src, "src", (torch.bfloat16, torch.float32), (L, K, N)),
+                  (dst, "dst", torch.bfloat16, (L, N, K))])
     dt = RMT_BF16 if src.dtype == torch.bfloat16 else RMT_F32
-    assert dt == RMT_BF16 or src.dtype == torch.float32
     check(lib().rmt_pack_weight(L, K, N, _ptr(src), dt, _ptr(dst), _stream(stream)))
 
 
 def grouped_gemm(A, B, group_layer, C_out, stream=None) -> None:
     """C_out[g] = A[g] @ B[group_layer[g]]^T with A [G, M, K], B [Lw, N, K],
-    C_out [G, M, N], all bf16 device tensors; group_layer a host int sequence."""
+    C_out [G, M, N], all bf16 device tensors; group_layer a host int sequence
+    with every entry in [0, Lw)."""
     import torch
     G, M, K = A.shape
-    N = B.shape[1]
-    assert B.shape[2] == K and C_out.shape == (G, M, N)
-    for t in (A, B, C_out):
-        assert t.dtype == torch.bfloat16 and t.is_contiguous()
-    gl = (C.c_int32 * G)(*[int(x) for x in group_layer])
-    check(lib().rmt_grouped_gemm(G, M, N, K, _ptr(A), _ptr(B), gl, _ptr(C_out), _stream(stream)))
+    Lw, N = B.shape[0], B.shape[1]
+    layers = [int(x) for x in group_layer]
+    if len(layers) != G:
+        raise ValueError(f"group_layer has {len(layers)} entries, A has {G} groups")
+    if any(not 0 <= x < Lw for x in layers):
+        raise ValueError(f"group_layer entries must lie in [0, {Lw})")
+    _require_all([(A, "A", torch.bfloat16, (G, M, K)), (B, "B", torch.bfloat16, (Lw, N, K)),
+                  (C_out, "C_out", torch.bfloat16, (G, M, N))])
+    gl = (C.c_int32 * G)(*layers)
+    check(lib().rmt_grouped_gemm(G, M, N, K, Lw, _ptr(A), _ptr(B), gl, _ptr(C_out), RMT_BF16,
+                                 _stream(stream)))
 
 
 def attention(qkv, out, n_heads: int, n_kv_heads: int, head_dim: int, causal: bool = True,
@@ -74,11 +105,9 @@ def attention(qkv, out, n_heads: int, n_kv_heads: int, head_dim: int, causal: bo
     """Attention over G cells, causal or unmasked: qkv [G, R, (Hq+2Hkv)*hd] ->
     out [G, R, Hq*hd], both bf16 device tensors."""
     import torch
-    G, R, W = qkv.shape
-    assert W == (n_heads + 2 * n_kv_heads) * head_dim
-    assert out.shape == (G, R, n_heads * head_dim)
-    for t in (qkv, out):
-        assert t.dtype == torch.bfloat16 and t.is_contiguous()
+    G, R = qkv.shape[0], qkv.shape[1]
+    _require_all([(qkv, "qkv", torch.bfloat16, (G, R, (n_heads + 2 * n_kv_heads) * head_dim)),
+                  (out, "out", torch.bfloat16, (G, R, n_heads * head_dim))])
     check(lib().rmt_attention(G, R, n_heads, n_kv_heads, head_dim, int(bool(causal)), _ptr(qkv),
                               _ptr(out), _stream(stream)))
 
@@ -87,11 +116,9 @@ def causal_attention(qkv, out, n_heads: int, n_kv_heads: int, head_dim: int, str
     """Causal GQA attention over G cells (rmt_causal_attention): qkv
     [G, R, (Hq+2Hkv)*hd] -> out [G, R, Hq*hd], both bf16 device tensors."""
     import torch
-    G, R, W = qkv.shape
-    assert W == (n_heads + 2 * n_kv_heads) * head_dim
-    assert out.shape == (G, R, n_heads * head_dim)
-    for t in (qkv, out):
-        assert t.dtype == torch.bfloat16 and t.is_contiguous()
+    G, R = qkv.shape[0], qkv.shape[1]
+    _require_all([(qkv, "qkv", torch.bfloat16, (G, R, (n_heads + 2 * n_kv_heads) * head_dim)),
+                  (out, "out", torch.bfloat16, (G, R, n_heads * head_dim))])
     check(lib().rmt_causal_attention(G, R, n_heads, n_kv_heads, head_dim, _ptr(qkv), _ptr(out),
                                      _stream(stream)))
 
@@ -100,10 +127,17 @@ class RMTModel:
     """A model handle (rmt_model_create).  `weights` maps the rmt_weights field
     names (w, b, g1, wqkv, wo, g2, wg, wu, wd, embed, and for the encoder cell
     beta1, bqkv, bo, beta2, w1, b1, w2, b2) to contiguous device tensors in the
-    mathematical layout, stacked over layers."""
+    mathematical layout, stacked over layers.
+
+    The library allocates no device memory: this wrapper allocates the packed
+    weight buffer and the activation workspace as torch tensors, of the sizes
+    rmt_workspace_bytes reports, and binds them (rmt_model_bind).  Packing
+    happens at construction, after which only `embed` of `weights` is still
+    read (the wrapper keeps a reference to it)."""
 
     _FIELDS = ("w", "b", "g1", "wqkv", "wo", "g2", "wg", "wu", "wd", "embed",
                "beta1", "bqkv", "bo", "beta2", "w1", "b1", "w2", "b2")
+    _FP32_FIELDS = ("b", "g1", "g2", "beta1", "bqkv", "bo", "beta2", "b1", "b2")
 
     def __init__(self, *, cell: int, dtype: int, L: int, S: int, n: int, m: int, d: int,
                  n_heads: int = 0, n_kv_heads: int = 0, head_dim: int = 0, ffn: int = 0,
@@ -112,33 +146,92 @@ class RMTModel:
         import torch
         self.cfg = RmtConfig(cell, dtype, L, S, n, m, d, n_heads, n_kv_heads, head_dim, ffn, vocab,
                              eps, rope_theta, int(bool(post_norm)))
-        big = [weights[k] for k in ("w", "wqkv", "wo", "wg", "wu", "wd", "w1", "w2")
-               if weights.get(k) is not None]
-        wdt = RMT_BF16 if big and big[0].dtype == torch.bfloat16 else RMT_F32
-        for t in weights.values():
-            if t is not None:
-                assert t.is_contiguous() and t.is_cuda
+        self.batch = 1
+        self.T = S * n
+        self._handle = C.c_void_p()
+        self.weight_buffer = None
+        self.workspace = None
+        wdt = self._check_weights(weights)
         w = RmtWeights(wdt, *[_ptr(weights.get(k)) for k in self._FIELDS])
         self._embed = weights.get("embed")     # borrowed by the library: keep it alive
-        self._handle = C.c_void_p()
         check(lib().rmt_model_create(C.byref(self.cfg), C.byref(w), _stream(stream),
                                      C.byref(self._handle)))
+        nbytes = self.buffer_bytes(RMT_BUF_WEIGHTS)
+        self.weight_buffer = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        check(lib().rmt_model_bind(self._handle, RMT_BUF_WEIGHTS, _ptr(self.weight_buffer), nbytes))
+        self._ensure_workspace()
+
+    def _check_weights(self, weights) -> int:
+        """Dtypes and shapes of the weights the cell reads; returns weight_dtype."""
+        import torch
+        c = self.cfg
+        L, d, F = c.L, c.d, c.ffn
+        hq = c.n_heads * c.head_dim
+        nq = (c.n_heads + 2 * c.n_kv_heads) * c.head_dim
+        if c.cell == RMT_CELL_LINEAR_GELU:
+            shapes = {"w": (L, d, d), "b": (L, d)}
+        elif c.cell == RMT_CELL_ENCODER:
+            shapes = {"g1": (L, d), "beta1": (L, d), "wqkv": (L, d, nq), "bqkv": (L, nq),
+                      "wo": (L, hq, d), "bo": (L, d), "g2": (L, d), "beta2": (L, d),
+                      "w1": (L, d, F), "b1": (L, F), "w2": (L, F, d), "b2": (L, d)}
+        else:
+            shapes = {"g2": (L, d), "wg": (L, d, F), "wu": (L, d, F), "wd": (L, F, d)}
+            if c.cell == RMT_CELL_LLAMA:
+                shapes.update({"g1": (L, d), "wqkv": (L, d, nq), "wo": (L, hq, d),
+                               "embed": (c.vocab, d)})
+        mats = [k for k in shapes if k not in self._FP32_FIELDS and k != "embed"]
+        if c.cell == RMT_CELL_LINEAR_GELU:
+            mat_dtype = torch.float32
+        else:
+            first = weights.get(mats[0])
+            mat_dtype = first.dtype if first is not None else torch.bfloat16
+            if mat_dtype not in (torch.bfloat16, torch.float32):
+                raise ValueError(f"{mats[0]}: dtype {mat_dtype}, expected torch.bfloat16 or torch.float32")
+        specs = []
+        for k, shape in shapes.items():
+            if k in self._FP32_FIELDS:
+                dt = torch.float32
+            elif k == "embed":
+                dt = torch.bfloat16
+            else:
+                dt = mat_dtype
+            specs.append((weights.get(k), k, dt, shape))
+        _require_all(specs)
+        return RMT_BF16 if mat_dtype == torch.bfloat16 else RMT_F32
+
+    def buffer_bytes(self, kind: int) -> int:
+        """rmt_workspace_bytes: bytes the weight buffer (RMT_BUF_WEIGHTS) or the
+        workspace for the current batch (RMT_BUF_WORKSPACE) needs."""
+        v = C.c_size_t()
+        check(lib().rmt_workspace_bytes(self._handle, kind, C.byref(v)))
+        return v.value
+
+    def _ensure_workspace(self) -> None:
+        import torch
+        need = self.buffer_bytes(RMT_BUF_WORKSPACE)
+        if self.workspace is None or self.workspace.numel() < need:
+            self.workspace = torch.empty(need, dtype=torch.uint8, device="cuda")
+            check(lib().rmt_model_bind(self._handle, RMT_BUF_WORKSPACE, _ptr(self.workspace), need))
 
     # -- configuration -----------------------------------------------------
     def set_segments(self, S: int) -> None:
         check(lib().rmt_model_set_segments(self._handle, S))
         self.cfg.S = S
+        self.T = S * self.cfg.n
 
     def set_tokens(self, T: int) -> None:
         """T tokens per sequence: ceil(T / n) segments, the last one short when
         T is not a multiple of n."""
         check(lib().rmt_model_set_tokens(self._handle, T))
         self.cfg.S = -(-T // self.cfg.n)
+        self.T = T
 
     def set_batch(self, B: int) -> None:
-        """B sequences per forward call: inputs and outputs gain a leading [B]."""
+        """B sequences per forward call: inputs and outputs gain a leading [B].
+        A larger workspace is allocated and bound when the batch needs one."""
         check(lib().rmt_model_set_batch(self._handle, B))
         self.batch = B
+        self._ensure_workspace()
 
     def set_stream(self, stream=None) -> None:
         check(lib().rmt_model_set_stream(self._handle, _stream(stream)))
@@ -149,7 +242,28 @@ class RMTModel:
         return v.value
 
     # -- forward -----------------------------------------------------------
+    def _check_io(self, tokens, mem0, hidden, mem) -> None:
+        """Dtypes, shapes and placement of a forward call's buffers: [B, ...]
+        with B sequences, or without the leading B when B = 1."""
+        import torch
+        c, B, T = self.cfg, self.batch, self.T
+
+        def shaped(t, rest):
+            if B == 1 and t is not None and len(t.shape) == len(rest) + 1:
+                return (1,) + rest
+            return ((B,) if B > 1 else ()) + rest
+        if c.cell == RMT_CELL_LLAMA:
+            tok = (tokens, "tokens", torch.int32, shaped(tokens, (T,)))
+        else:
+            dt = torch.float32 if c.dtype == RMT_F32 else torch.bfloat16
+            tok = (tokens, "tokens", dt, shaped(tokens, (T, c.d)))
+        _require_all([tok,
+                      (mem0, "mem0", torch.float32, shaped(mem0, (c.L, c.m, c.d))),
+                      (hidden, "hidden", torch.float32, shaped(hidden, (T, c.d))),
+                      (mem, "mem", torch.float32, shaped(mem, (c.L, c.m, c.d)))])
+
     def _fwd(self, fn, tokens, mem0, hidden, mem) -> None:
+        self._check_io(tokens, mem0, hidden, mem)
         out = RmtOutput(_ptr(hidden), _ptr(mem))
         check(fn(self._handle, _ptr(tokens), _ptr(mem0), C.byref(out)))
 

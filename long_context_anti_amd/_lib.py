@@ -16,6 +16,10 @@ RMT_EINVAL = -1
 RMT_EUNSUPPORTED = -2
 RMT_EHIP = -3
 RMT_ENOMEM = -4
+RMT_EWORKSPACE = -5
+
+RMT_BUF_WEIGHTS = 0
+RMT_BUF_WORKSPACE = 1
 
 RMT_CELL_LINEAR_GELU = 0
 RMT_CELL_NORM_SWIGLU = 1
@@ -57,6 +61,8 @@ SIGNATURES = {
     "rmt_diag_schedule": (C.c_int32, [C.c_int32, C.c_int32, C.c_void_p, C.c_void_p]),
     "rmt_model_create": (C.c_int32, [C.POINTER(RmtConfig), C.POINTER(RmtWeights), C.c_void_p,
                                      C.POINTER(C.c_void_p)]),
+    "rmt_workspace_bytes": (C.c_int32, [C.c_void_p, C.c_int32, C.POINTER(C.c_size_t)]),
+    "rmt_model_bind": (C.c_int32, [C.c_void_p, C.c_int32, C.c_void_p, C.c_size_t]),
     "rmt_model_set_segments": (C.c_int32, [C.c_void_p, C.c_int32]),
     "rmt_model_set_stream": (C.c_int32, [C.c_void_p, C.c_void_p]),
     "rmt_model_set_batch": (C.c_int32, [C.c_void_p, C.c_int32]),
@@ -72,8 +78,9 @@ SIGNATURES = {
     "rmt_model_destroy": (C.c_int32, [C.c_void_p]),
     "rmt_pack_weight": (C.c_int32, [C.c_int32, C.c_int32, C.c_int32, C.c_void_p, C.c_int32,
                                     C.c_void_p, C.c_void_p]),
-    "rmt_grouped_gemm": (C.c_int32, [C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_void_p,
-                                     C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p]),
+    "rmt_grouped_gemm": (C.c_int32, [C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32,
+                                     C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32,
+                                     C.c_void_p]),
     "rmt_causal_attention": (C.c_int32, [C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32,
                                          C.c_void_p, C.c_void_p, C.c_void_p]),
     "rmt_attention": (C.c_int32, [C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32,

@@ -66,10 +66,13 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 struct rmt_model {
   rmt_config cfg{};
   hipStream_t stream = nullptr;
-  void* block = nullptr;   // weights, tables, flag
-  size_t bytes = 0;
-  void* ws = nullptr;      // workspace, sized for the batch
+  rmt_weights src{};       // mathematical-layout weights, borrowed until they are packed
+  // Caller-owned device buffers (rmt_model_bind); the library allocates none.
+  void* wbuf = nullptr;    // packed weights, gains, RoPE table, flag
+  size_t wbuf_bytes = 0;
+  void* ws = nullptr;      // activation workspace, carved for the current batch
   size_t ws_bytes = 0;
+  bool ws_ok = false;      // the bound workspace holds the current batch's pieces
   int batch = 1;           // sequences per forward call
   int n_last = 0;          // rows of the last segment: n, or fewer when T is not a multiple of n
 
@@ -453,9 +456,61 @@ struct Piece {
   size_t bytes;
 };
 
-// (Re)allocate the workspace for B sequences: per-launch buffers for up to
-// min(kMaxGroups, B*L) cells, and per-sequence X ping-pong and memory buffers.
-int32_t alloc_workspace(rmt_model* M, int B) {
+// Lay the pieces out one after another from `base` at 256-byte boundaries
+// (base == nullptr: size only).  Returns the total size.
+size_t carve(const std::vector<Piece>& pieces, void* base) {
+  size_t off = 0;
+  for (const auto& p : pieces) {
+    off = align_up(off, 256);
+    if (base) *p.ptr = (char*)base + off;
+    off += p.bytes;
+  }
+  return align_up(off, 256);
+}
+
+// The packed weights and tables of the model's config: independent of S and B.
+std::vector<Piece> weight_pieces(rmt_model* M) {
+  const rmt_config& c = M->cfg;
+  const size_t L = c.L, d = c.d, R = (size_t)c.n + c.m, F = c.ffn;
+  const size_t NQ = has_attention(c) ? (size_t)nqkv(c) : 0;
+  const size_t HQD = has_attention(c) ? (size_t)c.n_heads * c.head_dim : 0;
+  std::vector<Piece> pieces;
+  if (c.cell == RMT_CELL_LINEAR_GELU) {
+    pieces.push_back({(void**)&M->w32, L * d * d * 4});
+    pieces.push_back({(void**)&M->b32, L * d * 4});
+  } else if (c.cell == RMT_CELL_ENCODER) {
+    // W1 packed [L][F][d] in the `wgu` slot, W2 packed [L][d][F] in `wd`
+    pieces.push_back({(void**)&M->wgu, L * F * d * 2});
+    pieces.push_back({(void**)&M->wd, L * d * F * 2});
+    pieces.push_back({(void**)&M->wqkv, L * NQ * d * 2});
+    pieces.push_back({(void**)&M->wo, L * d * HQD * 2});
+    pieces.push_back({(void**)&M->g1, L * d * 4});
+    pieces.push_back({(void**)&M->beta1, L * d * 4});
+    pieces.push_back({(void**)&M->g2, L * d * 4});
+    pieces.push_back({(void**)&M->beta2, L * d * 4});
+    pieces.push_back({(void**)&M->bqkv, L * NQ * 4});
+    pieces.push_back({(void**)&M->bo, L * d * 4});
+    pieces.push_back({(void**)&M->b1, L * F * 4});
+    pieces.push_back({(void**)&M->b2, L * d * 4});
+  } else {
+    pieces.push_back({(void**)&M->wgu, L * 2 * F * d * 2});
+    pieces.push_back({(void**)&M->wd, L * d * F * 2});
+    pieces.push_back({(void**)&M->g2, L * d * 4});
+    if (c.cell == RMT_CELL_LLAMA) {
+      pieces.push_back({(void**)&M->wqkv, L * NQ * d * 2});
+      pieces.push_back({(void**)&M->wo, L * d * HQD * 2});
+      pieces.push_back({(void**)&M->g1, L * d * 4});
+      pieces.push_back({(void**)&M->rope, R * (c.head_dim / 2) * sizeof(float2)});
+    }
+  }
+  pieces.push_back({(void**)&M->flag, 256});
+  return pieces;
+}
+
+// The activation workspace for B sequences: per-launch buffers for up to
+// min(kMaxGroups, B*L) cells, and per-sequence X ping-pong and memory
+// buffers.  Independent of S.
+std::vector<Piece> workspace_pieces(rmt_model* M, int B) {
   const rmt_config& c = M->cfg;
   const size_t L = c.L, n = c.n, m = c.m, d = c.d, R = n + m, F = c.ffn;
   const size_t cells = std::min<size_t>(kMaxGroups, (size_t)B * L);
@@ -474,31 +529,70 @@ int32_t alloc_workspace(rmt_model* M, int B) {
   pieces.push_back({(void**)&M->xbuf[0], (size_t)B * L * n * d * 4});
   pieces.push_back({(void**)&M->xbuf[1], (size_t)B * L * n * d * 4});
   pieces.push_back({(void**)&M->memw, (size_t)B * L * m * d * 4});
-  size_t total = 0;
-  for (auto& p : pieces) total = align_up(total, 256) + p.bytes;
-  total = align_up(total, 256);
-  // The new block is allocated before the old one is released, so a failure
-  // leaves the model as it was (same batch, same buffers).
-  if (M->ws) HIP_TRY(hipStreamSynchronize(M->stream));
-  void* ws = nullptr;
-  hipError_t e = hipMalloc(&ws, total);
-  if (e != hipSuccess) return fail(RMT_ENOMEM, "hipMalloc(%zu) failed: %s", total, hipGetErrorString(e));
-  if (M->ws) {
-    e = hipFree(M->ws);
-    if (e != hipSuccess) {
-      (void)hipFree(ws);
-      return fail(RMT_EHIP, "hipFree: %s", hipGetErrorString(e));
+  return pieces;
+}
+
+size_t workspace_need(rmt_model* M, int B) { return carve(workspace_pieces(M, B), nullptr); }
+
+// Point the workspace pieces into the bound buffer for the current batch, or
+// mark the workspace unusable when the buffer is too small for it.
+void carve_workspace(rmt_model* M) {
+  const std::vector<Piece> pieces = workspace_pieces(M, M->batch);
+  M->ws_ok = M->ws != nullptr && carve(pieces, nullptr) <= M->ws_bytes;
+  if (M->ws_ok) carve(pieces, M->ws);
+}
+
+// Pack the borrowed mathematical-layout weights into the bound weight buffer
+// (on the model's stream; waits for the packing to finish).
+int32_t pack_weights(rmt_model* M) {
+  const rmt_config& c = M->cfg;
+  const rmt_weights* w = &M->src;
+  const int L = c.L, d = c.d, R = c.n + c.m;
+  const size_t F = (size_t)c.ffn;
+  const size_t NQ = has_attention(c) ? (size_t)nqkv(c) : 0;
+  const size_t HQD = has_attention(c) ? (size_t)c.n_heads * c.head_dim : 0;
+  hipStream_t st = M->stream;
+  HIP_TRY(hipMemsetAsync(M->flag, 0, 256, st));
+  if (c.cell == RMT_CELL_LINEAR_GELU) {
+    HIP_TRY(hipMemcpyAsync(M->w32, w->w, (size_t)L * d * d * 4, hipMemcpyDeviceToDevice, st));
+    HIP_TRY(hipMemcpyAsync(M->b32, w->b, (size_t)L * d * 4, hipMemcpyDeviceToDevice, st));
+  } else if (c.cell == RMT_CELL_ENCODER) {
+    const int bf = w->weight_dtype == RMT_BF16;
+    HIP_TRY(launch_pack(L, d, (int)F, w->w1, nullptr, bf, 0, M->wgu, st));
+    HIP_TRY(launch_pack(L, (int)F, d, w->w2, nullptr, bf, 0, M->wd, st));
+    HIP_TRY(launch_pack(L, d, (int)NQ, w->wqkv, nullptr, bf, 0, M->wqkv, st));
+    HIP_TRY(launch_pack(L, (int)HQD, d, w->wo, nullptr, bf, 0, M->wo, st));
+    const size_t Ld4 = (size_t)L * d * 4;
+    HIP_TRY(hipMemcpyAsync(M->g1, w->g1, Ld4, hipMemcpyDeviceToDevice, st));
+    HIP_TRY(hipMemcpyAsync(M->beta1, w->beta1, Ld4, hipMemcpyDeviceToDevice, st));
+    HIP_TRY(hipMemcpyAsync(M->g2, w->g2, Ld4, hipMemcpyDeviceToDevice, st));
+    HIP_TRY(hipMemcpyAsync(M->beta2, w->beta2, Ld4, hipMemcpyDeviceToDevice, st));
+    HIP_TRY(hipMemcpyAsync(M->bqkv, w->bqkv, (size_t)L * NQ * 4, hipMemcpyDeviceToDevice, st));
+    HIP_TRY(hipMemcpyAsync(M->bo, w->bo, Ld4, hipMemcpyDeviceToDevice, st));
+    HIP_TRY(hipMemcpyAsync(M->b1, w->b1, (size_t)L * F * 4, hipMemcpyDeviceToDevice, st));
+    HIP_TRY(hipMemcpyAsync(M->b2, w->b2, Ld4, hipMemcpyDeviceToDevice, st));
+  } else {
+    const int bf = w->weight_dtype == RMT_BF16;
+    HIP_TRY(launch_pack(L, d, (int)F, w->wg, w->wu, bf, 1, M->wgu, st));
+    HIP_TRY(launch_pack(L, (int)F, d, w->wd, nullptr, bf, 0, M->wd, st));
+    HIP_TRY(hipMemcpyAsync(M->g2, w->g2, (size_t)L * d * 4, hipMemcpyDeviceToDevice, st));
+    if (c.cell == RMT_CELL_LLAMA) {
+      HIP_TRY(launch_pack(L, d, (int)NQ, w->wqkv, nullptr, bf, 0, M->wqkv, st));
+      HIP_TRY(launch_pack(L, (int)HQD, d, w->wo, nullptr, bf, 0, M->wo, st));
+      HIP_TRY(hipMemcpyAsync(M->g1, w->g1, (size_t)L * d * 4, hipMemcpyDeviceToDevice, st));
+      // RoPE table: angle p * theta^(-2i/hd) in double precision.
+      const int half = c.head_dim / 2;
+      std::vector<float2> tab((size_t)R * half);
+      for (int p = 0; p < R; ++p)
+        for (int i = 0; i < half; ++i) {
+          const double ang = (double)p * std::pow((double)c.rope_theta, -2.0 * i / c.head_dim);
+          tab[(size_t)p * half + i] = make_float2((float)std::cos(ang), (float)std::sin(ang));
+        }
+      HIP_TRY(hipMemcpyAsync(M->rope, tab.data(), tab.size() * sizeof(float2), hipMemcpyHostToDevice, st));
+      HIP_TRY(hipStreamSynchronize(st));   // `tab` is host memory of this frame
     }
   }
-  M->ws = ws;
-  M->ws_bytes = total;
-  size_t off = 0;
-  for (auto& p : pieces) {
-    off = align_up(off, 256);
-    *p.ptr = (char*)ws + off;
-    off += p.bytes;
-  }
-  M->batch = B;
+  HIP_TRY(hipStreamSynchronize(st));
   return RMT_OK;
 }
 
@@ -506,6 +600,10 @@ int32_t check_forward_args(rmt_model* M, const void* tokens, const void* mem0, c
   if (!M) return fail(RMT_EINVAL, "model is NULL");
   if (!tokens || !mem0 || !out || !out->hidden || !out->mem)
     return fail(RMT_EINVAL, "tokens, mem0, out, out->hidden and out->mem must be non-NULL");
+  if (!M->wbuf) return fail(RMT_EWORKSPACE, "no weight buffer bound (rmt_model_bind, RMT_BUF_WEIGHTS)");
+  if (!M->ws_ok)
+    return fail(RMT_EWORKSPACE, "no workspace bound for a batch of %d (rmt_model_bind, RMT_BUF_WORKSPACE; "
+                "%zu bytes needed, %zu bound)", M->batch, workspace_need(M, M->batch), M->ws_bytes);
   return RMT_OK;
 }
 
@@ -559,7 +657,6 @@ int32_t rmt_model_create(const rmt_config* cfg, const rmt_weights* w, void* stre
   if (rc != RMT_OK) return rc;
   if (!w) return fail(RMT_EINVAL, "weights are NULL");
   const rmt_config& c = *cfg;
-  const int L = c.L, n = c.n, m = c.m, d = c.d, R = n + m;
   if (c.cell == RMT_CELL_LINEAR_GELU) {
     if (!w->w || !w->b) return fail(RMT_EINVAL, "LINEAR_GELU needs w and b");
     if (w->weight_dtype != RMT_F32) return fail(RMT_EUNSUPPORTED, "LINEAR_GELU weights must be fp32");
@@ -576,121 +673,60 @@ int32_t rmt_model_create(const rmt_config* cfg, const rmt_weights* w, void* stre
     if (w->weight_dtype != RMT_F32 && w->weight_dtype != RMT_BF16)
       return fail(RMT_EINVAL, "weight_dtype must be RMT_F32 or RMT_BF16");
   }
-
+  // No device work and no device memory: the weights stay where the caller
+  // keeps them until rmt_model_bind packs them into the caller's buffer.
   rmt_model* M = new rmt_model();
   M->cfg = c;
   M->n_last = c.n;
   M->stream = (hipStream_t)stream;
-
-  // Carve one allocation.
-  const size_t F = (size_t)c.ffn;
-  const size_t NQ = has_attention(c) ? (size_t)nqkv(c) : 0;
-  const size_t HQD = has_attention(c) ? (size_t)c.n_heads * c.head_dim : 0;
-  std::vector<Piece> pieces;
-  if (c.cell == RMT_CELL_LINEAR_GELU) {
-    pieces.push_back({(void**)&M->w32, (size_t)L * d * d * 4});
-    pieces.push_back({(void**)&M->b32, (size_t)L * d * 4});
-  } else if (c.cell == RMT_CELL_ENCODER) {
-    // W1 packed [L][F][d] in the `wgu` slot, W2 packed [L][d][F] in `wd`
-    pieces.push_back({(void**)&M->wgu, (size_t)L * F * d * 2});
-    pieces.push_back({(void**)&M->wd, (size_t)L * d * F * 2});
-    pieces.push_back({(void**)&M->wqkv, (size_t)L * NQ * d * 2});
-    pieces.push_back({(void**)&M->wo, (size_t)L * d * HQD * 2});
-    pieces.push_back({(void**)&M->g1, (size_t)L * d * 4});
-    pieces.push_back({(void**)&M->beta1, (size_t)L * d * 4});
-    pieces.push_back({(void**)&M->g2, (size_t)L * d * 4});
-    pieces.push_back({(void**)&M->beta2, (size_t)L * d * 4});
-    pieces.push_back({(void**)&M->bqkv, (size_t)L * NQ * 4});
-    pieces.push_back({(void**)&M->bo, (size_t)L * d * 4});
-    pieces.push_back({(void**)&M->b1, (size_t)L * F * 4});
-    pieces.push_back({(void**)&M->b2, (size_t)L * d * 4});
-  } else {
-    pieces.push_back({(void**)&M->wgu, (size_t)L * 2 * F * d * 2});
-    pieces.push_back({(void**)&M->wd, (size_t)L * d * F * 2});
-    pieces.push_back({(void**)&M->g2, (size_t)L * d * 4});
-    if (c.cell == RMT_CELL_LLAMA) {
-      pieces.push_back({(void**)&M->wqkv, (size_t)L * NQ * d * 2});
-      pieces.push_back({(void**)&M->wo, (size_t)L * d * HQD * 2});
-      pieces.push_back({(void**)&M->g1, (size_t)L * d * 4});
-      pieces.push_back({(void**)&M->rope, (size_t)R * (c.head_dim / 2) * sizeof(float2)});
-    }
-  }
-  pieces.push_back({(void**)&M->flag, 256});
-  size_t total = 0;
-  for (auto& p : pieces) total = align_up(total, 256) + p.bytes;
-  total = align_up(total, 256);
-  hipError_t e = hipMalloc(&M->block, total);
-  if (e != hipSuccess) {
-    delete M;
-    return fail(RMT_ENOMEM, "hipMalloc(%zu) failed: %s", total, hipGetErrorString(e));
-  }
-  M->bytes = total;
-  size_t off = 0;
-  for (auto& p : pieces) {
-    off = align_up(off, 256);
-    *p.ptr = (char*)M->block + off;
-    off += p.bytes;
-  }
-
-  auto bail = [&](int32_t code) {
-    (void)hipFree(M->block);
-    (void)hipFree(M->ws);
-    delete M;
-    return code;
-  };
-  if (int32_t rc_ws = alloc_workspace(M, 1); rc_ws != RMT_OK) return bail(rc_ws);
-#define CREATE_TRY(expr)                                                              \
-  do {                                                                                \
-    hipError_t e_ = (expr);                                                           \
-    if (e_ != hipSuccess) return bail(fail(RMT_EHIP, "%s: %s", #expr, hipGetErrorString(e_))); \
-  } while (0)
-
-  hipStream_t st = M->stream;
-  CREATE_TRY(hipMemsetAsync(M->flag, 0, 256, st));
-  if (c.cell == RMT_CELL_LINEAR_GELU) {
-    CREATE_TRY(hipMemcpyAsync(M->w32, w->w, (size_t)L * d * d * 4, hipMemcpyDeviceToDevice, st));
-    CREATE_TRY(hipMemcpyAsync(M->b32, w->b, (size_t)L * d * 4, hipMemcpyDeviceToDevice, st));
-  } else if (c.cell == RMT_CELL_ENCODER) {
-    const int bf = w->weight_dtype == RMT_BF16;
-    CREATE_TRY(launch_pack(L, d, (int)F, w->w1, nullptr, bf, 0, M->wgu, st));
-    CREATE_TRY(launch_pack(L, (int)F, d, w->w2, nullptr, bf, 0, M->wd, st));
-    CREATE_TRY(launch_pack(L, d, (int)NQ, w->wqkv, nullptr, bf, 0, M->wqkv, st));
-    CREATE_TRY(launch_pack(L, (int)HQD, d, w->wo, nullptr, bf, 0, M->wo, st));
-    const size_t Ld4 = (size_t)L * d * 4;
-    CREATE_TRY(hipMemcpyAsync(M->g1, w->g1, Ld4, hipMemcpyDeviceToDevice, st));
-    CREATE_TRY(hipMemcpyAsync(M->beta1, w->beta1, Ld4, hipMemcpyDeviceToDevice, st));
-    CREATE_TRY(hipMemcpyAsync(M->g2, w->g2, Ld4, hipMemcpyDeviceToDevice, st));
-    CREATE_TRY(hipMemcpyAsync(M->beta2, w->beta2, Ld4, hipMemcpyDeviceToDevice, st));
-    CREATE_TRY(hipMemcpyAsync(M->bqkv, w->bqkv, (size_t)L * NQ * 4, hipMemcpyDeviceToDevice, st));
-    CREATE_TRY(hipMemcpyAsync(M->bo, w->bo, Ld4, hipMemcpyDeviceToDevice, st));
-    CREATE_TRY(hipMemcpyAsync(M->b1, w->b1, (size_t)L * F * 4, hipMemcpyDeviceToDevice, st));
-    CREATE_TRY(hipMemcpyAsync(M->b2, w->b2, Ld4, hipMemcpyDeviceToDevice, st));
-  } else {
-    const int bf = w->weight_dtype == RMT_BF16;
-    CREATE_TRY(launch_pack(L, d, (int)F, w->wg, w->wu, bf, 1, M->wgu, st));
-    CREATE_TRY(launch_pack(L, (int)F, d, w->wd, nullptr, bf, 0, M->wd, st));
-    CREATE_TRY(hipMemcpyAsync(M->g2, w->g2, (size_t)L * d * 4, hipMemcpyDeviceToDevice, st));
-    if (c.cell == RMT_CELL_LLAMA) {
-      CREATE_TRY(launch_pack(L, d, (int)NQ, w->wqkv, nullptr, bf, 0, M->wqkv, st));
-      CREATE_TRY(launch_pack(L, (int)HQD, d, w->wo, nullptr, bf, 0, M->wo, st));
-      CREATE_TRY(hipMemcpyAsync(M->g1, w->g1, (size_t)L * d * 4, hipMemcpyDeviceToDevice, st));
-      M->embed = (const uint16_t*)w->embed;
-      // RoPE table: angle p * theta^(-2i/hd) in double precision.
-      const int half = c.head_dim / 2;
-      std::vector<float2> tab((size_t)R * half);
-      for (int p = 0; p < R; ++p)
-        for (int i = 0; i < half; ++i) {
-          const double ang = (double)p * std::pow((double)c.rope_theta, -2.0 * i / c.head_dim);
-          tab[(size_t)p * half + i] = make_float2((float)std::cos(ang), (float)std::sin(ang));
-        }
-      CREATE_TRY(hipMemcpyAsync(M->rope, tab.data(), tab.size() * sizeof(float2),
-                                hipMemcpyHostToDevice, st));
-      CREATE_TRY(hipStreamSynchronize(st));   // `tab` is host stack memory
-    }
-  }
-  CREATE_TRY(hipStreamSynchronize(st));
-#undef CREATE_TRY
+  M->src = *w;
+  M->embed = (const uint16_t*)w->embed;
   *out = M;
+  return RMT_OK;
+}
+
+int32_t rmt_workspace_bytes(const rmt_model* model, int32_t kind, size_t* bytes) {
+  if (!model || !bytes) return fail(RMT_EINVAL, "model and bytes must be non-NULL");
+  rmt_model* M = const_cast<rmt_model*>(model);
+  // size queries only: carve() writes no pointer when the base is NULL
+  if (kind == RMT_BUF_WEIGHTS) *bytes = carve(weight_pieces(M), nullptr);
+  else if (kind == RMT_BUF_WORKSPACE) *bytes = workspace_need(M, M->batch);
+  else return fail(RMT_EINVAL, "kind must be RMT_BUF_WEIGHTS or RMT_BUF_WORKSPACE (got %d)", kind);
+  return RMT_OK;
+}
+
+int32_t rmt_model_bind(rmt_model* M, int32_t kind, void* buffer, size_t bytes) {
+  if (!M) return fail(RMT_EINVAL, "model is NULL");
+  if (kind != RMT_BUF_WEIGHTS && kind != RMT_BUF_WORKSPACE)
+    return fail(RMT_EINVAL, "kind must be RMT_BUF_WEIGHTS or RMT_BUF_WORKSPACE (got %d)", kind);
+  if (!buffer) return fail(RMT_EINVAL, "buffer is NULL");
+  if ((uintptr_t)buffer % 256 != 0) return fail(RMT_EINVAL, "buffer must be 256-byte aligned");
+  if (kind == RMT_BUF_WEIGHTS) {
+    if (M->wbuf) return fail(RMT_EINVAL, "the weights are already packed into a bound buffer");
+    const std::vector<Piece> pieces = weight_pieces(M);
+    const size_t need = carve(pieces, nullptr);
+    if (bytes < need) return fail(RMT_EWORKSPACE, "weight buffer of %zu bytes, %zu needed", bytes, need);
+    carve(pieces, buffer);
+    M->wbuf = buffer;
+    M->wbuf_bytes = bytes;
+    const int32_t rc = pack_weights(M);
+    if (rc != RMT_OK) {
+      M->wbuf = nullptr;
+      M->wbuf_bytes = 0;
+      return rc;
+    }
+    // only the embedding is read after packing
+    const void* embed = M->src.embed;
+    M->src = rmt_weights{};
+    M->src.embed = embed;
+    return RMT_OK;
+  }
+  const size_t need = workspace_need(M, M->batch);
+  if (bytes < need)
+    return fail(RMT_EWORKSPACE, "workspace of %zu bytes, %zu needed for a batch of %d", bytes, need, M->batch);
+  M->ws = buffer;
+  M->ws_bytes = bytes;
+  carve_workspace(M);
   return RMT_OK;
 }
 
@@ -727,8 +763,9 @@ int32_t rmt_model_set_batch(rmt_model* model, int32_t B) {
   const rmt_config& c = model->cfg;
   if ((int64_t)B * c.S * c.n > ((int64_t)1 << 40) / std::max(1, c.d))
     return fail(RMT_EINVAL, "B * S * n * d is too large");
-  if (B == model->batch) return RMT_OK;
-  return alloc_workspace(model, B);
+  model->batch = B;
+  carve_workspace(model);   // keeps the bound workspace if it is large enough for B
+  return RMT_OK;
 }
 
 int32_t rmt_model_set_stream(rmt_model* model, void* stream) {
@@ -739,7 +776,7 @@ int32_t rmt_model_set_stream(rmt_model* model, void* stream) {
 
 int32_t rmt_model_device_bytes(const rmt_model* model, size_t* bytes) {
   if (!model || !bytes) return fail(RMT_EINVAL, "model and bytes must be non-NULL");
-  *bytes = model->bytes + model->ws_bytes;
+  *bytes = model->wbuf_bytes + model->ws_bytes;
   return RMT_OK;
 }
 
@@ -787,6 +824,7 @@ int32_t rmt_forward_sequential(rmt_model* M, const void* tokens, const void* mem
 
 int32_t rmt_model_check(rmt_model* M, int32_t* bad_tokens) {
   if (!M || !bad_tokens) return fail(RMT_EINVAL, "model and bad_tokens must be non-NULL");
+  if (!M->wbuf) return fail(RMT_EWORKSPACE, "no weight buffer bound");
   int32_t v = 0;
   HIP_TRY(hipMemcpyAsync(&v, M->flag, sizeof(v), hipMemcpyDeviceToHost, M->stream));
   HIP_TRY(hipStreamSynchronize(M->stream));
@@ -859,16 +897,13 @@ int32_t rmt_model_stage_times_groups(rmt_model* M, int32_t g_lo, int32_t g_hi, d
 
 int32_t rmt_model_destroy(rmt_model* M) {
   if (!M) return RMT_OK;
-  hipError_t e1 = hipStreamSynchronize(M->stream);
+  // The bound buffers belong to the caller: nothing to free on the device.
+  // Device work is queued only once the weights are bound (packing, forward
+  // calls), so a model without them has nothing to wait for.
+  hipError_t e1 = M->wbuf ? hipStreamSynchronize(M->stream) : hipSuccess;
   for (hipEvent_t e : M->events) (void)hipEventDestroy(e);
-  hipError_t e2 = hipFree(M->block);
-  if (M->ws) {
-    const hipError_t e3 = hipFree(M->ws);
-    if (e2 == hipSuccess) e2 = e3;
-  }
   delete M;
   if (e1 != hipSuccess) return fail(RMT_EHIP, "hipStreamSynchronize: %s", hipGetErrorString(e1));
-  if (e2 != hipSuccess) return fail(RMT_EHIP, "hipFree: %s", hipGetErrorString(e2));
   return RMT_OK;
 }
 
@@ -883,18 +918,22 @@ int32_t rmt_pack_weight(int32_t L, int32_t K, int32_t N, const void* src, int32_
   return RMT_OK;
 }
 
-int32_t rmt_grouped_gemm(int32_t G, int32_t Mr, int32_t N, int32_t K, const void* A, const void* B,
-                         const int32_t* group_layer, void* C, void* stream) {
+int32_t rmt_grouped_gemm(int32_t G, int32_t Mr, int32_t N, int32_t K, int32_t Lw, const void* A,
+                         const void* B, const int32_t* group_layer, void* C, int32_t dtype, void* stream) {
   if (G < 1 || G > kMaxGroups) return fail(RMT_EINVAL, "G must be in [1, %d] (got %d)", kMaxGroups, G);
   if (Mr < 1 || K < 8 || K % 8 != 0 || N < 64 || N % 64 != 0)
     return fail(RMT_EINVAL, "need M >= 1, K a positive multiple of 8, N a positive multiple of 64");
+  if (Lw < 1) return fail(RMT_EINVAL, "Lw must be >= 1 (got %d)", Lw);
   if ((int64_t)G * Mr * std::max(N, K) > INT32_MAX) return fail(RMT_EINVAL, "sizes overflow int32");
   if (!A || !B || !C || !group_layer) return fail(RMT_EINVAL, "A, B, C and group_layer must be non-NULL");
+  if (dtype != RMT_BF16) return fail(RMT_EUNSUPPORTED, "dtype must be RMT_BF16 (got %d)", dtype);
+  for (int g = 0; g < G; ++g)
+    if (group_layer[g] < 0 || group_layer[g] >= Lw)
+      return fail(RMT_EINVAL, "group_layer[%d] = %d is outside [0, %d)", g, group_layer[g], Lw);
   GroupTable tab;
   std::memset(&tab, 0, sizeof(tab));
   tab.G = G;
   for (int g = 0; g < G; ++g) {
-    if (group_layer[g] < 0) return fail(RMT_EINVAL, "group_layer[%d] < 0", g);
     tab.layer[g] = group_layer[g];
     tab.out_lo[g] = (uint16_t*)C + (size_t)g * Mr * N;
   }

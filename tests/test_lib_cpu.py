@@ -164,11 +164,20 @@ def test_grouped_gemm_rejects_bad_shapes():
     h = L.lib()
     gl = (C.c_int32 * 1)(0)
     p = C.c_void_p(16)
-    assert h.rmt_grouped_gemm(0, 128, 256, 64, p, p, gl, p, None) == L.RMT_EINVAL
-    assert h.rmt_grouped_gemm(33, 128, 256, 64, p, p, gl, p, None) == L.RMT_EINVAL
-    assert h.rmt_grouped_gemm(1, 128, 250, 64, p, p, gl, p, None) == L.RMT_EINVAL
-    assert h.rmt_grouped_gemm(1, 128, 256, 60, p, p, gl, p, None) == L.RMT_EINVAL
-    assert h.rmt_grouped_gemm(1, 128, 256, 64, None, p, gl, p, None) == L.RMT_EINVAL
+    bf = L.RMT_BF16
+    assert h.rmt_grouped_gemm(0, 128, 256, 64, 1, p, p, gl, p, bf, None) == L.RMT_EINVAL
+    assert h.rmt_grouped_gemm(33, 128, 256, 64, 1, p, p, gl, p, bf, None) == L.RMT_EINVAL
+    assert h.rmt_grouped_gemm(1, 128, 250, 64, 1, p, p, gl, p, bf, None) == L.RMT_EINVAL
+    assert h.rmt_grouped_gemm(1, 128, 256, 60, 1, p, p, gl, p, bf, None) == L.RMT_EINVAL
+    assert h.rmt_grouped_gemm(1, 128, 256, 64, 1, None, p, gl, p, bf, None) == L.RMT_EINVAL
+    assert h.rmt_grouped_gemm(1, 128, 256, 64, 0, p, p, gl, p, bf, None) == L.RMT_EINVAL
+    assert h.rmt_grouped_gemm(1, 128, 256, 64, 1, p, p, gl, p, L.RMT_F32, None) == L.RMT_EUNSUPPORTED
+    # a layer index outside [0, Lw) is refused before any device work
+    g3 = (C.c_int32 * 2)(0, 3)
+    assert h.rmt_grouped_gemm(2, 128, 256, 64, 3, p, p, g3, p, bf, None) == L.RMT_EINVAL
+    assert b"group_layer[1] = 3" in h.rmt_last_error()
+    gneg = (C.c_int32 * 1)(-1)
+    assert h.rmt_grouped_gemm(1, 128, 256, 64, 3, p, p, gneg, p, bf, None) == L.RMT_EINVAL
     assert h.rmt_pack_weight(1, 60, 64, p, 0, p, None) == L.RMT_EINVAL
 
 
