@@ -373,7 +373,7 @@ def main():
             model.set_segments(Sp)
             mp = torch.empty_like(mem)
             hp = torch.empty((Sp * cfg.n, cfg.d), dtype=torch.float32, device="cuda")
-            model.forward_diagonal(tok_d, mem0_d, hp, mp)
+            model.forward_diagonal(tok_d[:Sp * cfg.n], mem0_d, hp, mp)
             torch.cuda.synchronize()
             model.set_segments(cfg.S)
             return mp.cpu().numpy().astype(np.float64)

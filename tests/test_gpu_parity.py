@@ -142,7 +142,7 @@ def _gpu_state_after(run, s):
     run.model.set_segments(s)
     h = torch.empty((s * cfg.n, cfg.d), dtype=torch.float32, device="cuda")
     m = torch.empty_like(run.mem)
-    run.model.forward_diagonal(run.tokens, run.mem0_dev, h, m)
+    run.model.forward_diagonal(run.tokens[:s * cfg.n], run.mem0_dev, h, m)
     torch.cuda.synchronize()
     run.model.set_segments(run.S)
     return m.cpu().numpy()

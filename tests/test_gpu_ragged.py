@@ -65,7 +65,7 @@ def test_short_last_segment(cfg, T):
     S_full = T // cfg.n
     if S_full:
         model.set_segments(S_full)
-        hp, _ = _run(model, x_d, mem0_d, S_full * cfg.n, cfg)
+        hp, _ = _run(model, x_d[:S_full * cfg.n], mem0_d, S_full * cfg.n, cfg)
         assert np.array_equal(hd[:S_full * cfg.n], hp)
     model.close()
 
