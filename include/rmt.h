@@ -254,6 +254,23 @@ int32_t rmt_model_device_bytes(const rmt_model* model, size_t* bytes);
 int32_t rmt_forward_diagonal(rmt_model* model, const void* tokens, const void* mem0,
                              rmt_output* out);
 
+/* rmt_forward_diagonal for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same arguments, the same kernels and bitwise the same
+ * results, but the activation workspace is the library's own static device
+ * array of 64 MiB (per device, held until the process ends) instead of the
+ * buffer bound with RMT_BUF_WORKSPACE, which this call neither needs nor
+ * touches.  The weight buffer must be bound as for rmt_forward_diagonal.
+ * The call allocates nothing and records no timing events.  Calls that
+ * overlap on one device share that array and race: serialise them (for
+ * example on one stream).  The array's contents carry over from call to
+ * call; every call writes each workspace byte before reading it.
+ * Errors: RMT_EINVAL (NULL pointers), RMT_EWORKSPACE (no weight buffer
+ * bound, or rmt_workspace_bytes(RMT_BUF_WORKSPACE) above 64 MiB for the
+ * current batch -- checked before any device call), RMT_EHIP. */
+int32_t rmt_forward_diagonal_static(rmt_model* model, const void* tokens, const void* mem0,
+                                    rmt_output* out);
+
 /* The same computation cell by cell, segment-major (for b: for s: for l:),
  * one cell per launch: the sequential RMT schedule that the abstract of the
  * catalogue record compares diagonal batching against.  Same arguments and

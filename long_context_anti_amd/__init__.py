@@ -273,6 +273,12 @@ class RMTModel:
     def forward_sequential(self, tokens, mem0, hidden, mem) -> None:
         self._fwd(lib().rmt_forward_sequential, tokens, mem0, hidden, mem)
 
+    def forward_diagonal_static(self, tokens, mem0, hidden, mem) -> None:
+        """rmt_forward_diagonal with the library's static 64 MiB workspace
+        instead of the bound one: allocates nothing (for callers that cannot);
+        overlapping calls on one device race."""
+        self._fwd(lib().rmt_forward_diagonal_static, tokens, mem0, hidden, mem)
+
     def bad_tokens(self) -> bool:
         v = C.c_int32()
         check(lib().rmt_model_check(self._handle, C.byref(v)))

@@ -18,6 +18,9 @@ RMT_EHIP = -3
 RMT_ENOMEM = -4
 RMT_EWORKSPACE = -5
 
+# bytes of the static workspace behind rmt_forward_diagonal_static
+STATIC_SCRATCH_BYTES = 64 << 20
+
 RMT_BUF_WEIGHTS = 0
 RMT_BUF_WORKSPACE = 1
 
@@ -70,6 +73,8 @@ SIGNATURES = {
     "rmt_model_device_bytes": (C.c_int32, [C.c_void_p, C.POINTER(C.c_size_t)]),
     "rmt_forward_diagonal": (C.c_int32, [C.c_void_p, C.c_void_p, C.c_void_p, C.POINTER(RmtOutput)]),
     "rmt_forward_sequential": (C.c_int32, [C.c_void_p, C.c_void_p, C.c_void_p, C.POINTER(RmtOutput)]),
+    "rmt_forward_diagonal_static": (C.c_int32, [C.c_void_p, C.c_void_p, C.c_void_p,
+                                                C.POINTER(RmtOutput)]),
     "rmt_model_check": (C.c_int32, [C.c_void_p, C.POINTER(C.c_int32)]),
     "rmt_model_enable_timing": (C.c_int32, [C.c_void_p, C.c_int32]),
     "rmt_model_stage_times": (C.c_int32, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p]),

@@ -30,6 +30,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -37,6 +38,12 @@
 #include "kernels.h"
 
 using namespace rmt;
+
+// Activation workspace of rmt_forward_diagonal_static, for callers that cannot
+// allocate device memory.  Each device the library runs on holds its own copy
+// until the process ends; calls that overlap on one device share it.
+constexpr size_t kStaticScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
 
 namespace {
 
@@ -621,6 +628,60 @@ int32_t start_forward(rmt_model* M, const void* mem0, const rmt_output* out) {
   return RMT_OK;
 }
 
+// Queue every diagonal of the sweep: per diagonal, the regular cells in
+// launches of up to kMaxGroups (layer-major, sequence fastest), then the cells
+// of a short last segment in launches of their own.  Uses no heap memory.
+int32_t sweep_diagonals(rmt_model* M, const void* tokens, const rmt_output* out) {
+  const int L = M->cfg.L, S = M->cfg.S, B = M->batch;
+  const bool ragged = M->n_last != M->cfg.n;
+  Cell chunk[kMaxGroups];
+  for (int k = 0; k < L + S - 1; ++k) {
+    const int l_lo = std::max(0, k - S + 1), l_hi = std::min(L - 1, k);
+    for (int pass = 0; pass < 2; ++pass) {      // 0: regular cells, 1: short cells
+      int G = 0;
+      for (int l = l_lo; l <= l_hi; ++l) {
+        const bool short_cell = ragged && k - l == S - 1;
+        if (short_cell != (pass == 1)) continue;
+        for (int b = 0; b < B; ++b) {
+          chunk[G++] = Cell{l, k - l, b};
+          if (G == kMaxGroups) {
+            const int32_t rc = run_cells(M, chunk, G, tokens, out);
+            if (rc != RMT_OK) return rc;
+            G = 0;
+          }
+        }
+      }
+      if (G > 0) {
+        const int32_t rc = run_cells(M, chunk, G, tokens, out);
+        if (rc != RMT_OK) return rc;
+      }
+    }
+  }
+  return RMT_OK;
+}
+
+// Device address of `scratch` on each device, looked up once per device (with
+// that device current) and kept: in host code the array's name is only a
+// host-side stand-in, never a device address.
+std::mutex g_scratch_mu;
+std::vector<void*> g_scratch_ptr;   // by device ordinal; nullptr until looked up
+
+int32_t scratch_address(void** out) {
+  int dev = 0;
+  HIP_TRY(hipGetDevice(&dev));
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (dev < 0) return fail(RMT_EHIP, "hipGetDevice returned %d", dev);
+  if ((size_t)dev >= g_scratch_ptr.size()) g_scratch_ptr.resize((size_t)dev + 1, nullptr);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    HIP_TRY(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    if (!p) return fail(RMT_EHIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return RMT_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -785,26 +846,37 @@ int32_t rmt_forward_diagonal(rmt_model* M, const void* tokens, const void* mem0,
   if (rc != RMT_OK) return rc;
   rc = start_forward(M, mem0, out);
   if (rc != RMT_OK) return rc;
-  const int L = M->cfg.L, S = M->cfg.S, B = M->batch;
-  std::vector<Cell> diag;
-  for (int k = 0; k < L + S - 1; ++k) {
-    const int l_lo = std::max(0, k - S + 1), l_hi = std::min(L - 1, k);
-    diag.clear();
-    for (int l = l_lo; l <= l_hi; ++l)
-      for (int b = 0; b < B; ++b) diag.push_back(Cell{l, k - l, b});
-    // cells of a short last segment have fewer rows: they get launches of their own
-    const auto short_cell = [&](const Cell& x) { return x.s == S - 1 && M->n_last != M->cfg.n; };
-    std::stable_partition(diag.begin(), diag.end(), [&](const Cell& x) { return !short_cell(x); });
-    const size_t n_regular =
-        (size_t)std::count_if(diag.begin(), diag.end(), [&](const Cell& x) { return !short_cell(x); });
-    for (const auto& part : {std::make_pair((size_t)0, n_regular), std::make_pair(n_regular, diag.size())})
-      for (size_t c0 = part.first; c0 < part.second; c0 += kMaxGroups) {
-        const int G = (int)std::min<size_t>(kMaxGroups, part.second - c0);
-        rc = run_cells(M, diag.data() + c0, G, tokens, out);
-        if (rc != RMT_OK) return rc;
-      }
-  }
-  return RMT_OK;
+  return sweep_diagonals(M, tokens, out);
+}
+
+int32_t rmt_forward_diagonal_static(rmt_model* M, const void* tokens, const void* mem0,
+                                    rmt_output* out) {
+  if (!M) return fail(RMT_EINVAL, "model is NULL");
+  const size_t need = workspace_need(M, M->batch);
+  if (need > kStaticScratchBytes)
+    return fail(RMT_EWORKSPACE,
+                "this model needs %zu bytes of workspace for a batch of %d; the static scratch of "
+                "rmt_forward_diagonal_static holds %zu",
+                need, M->batch, kStaticScratchBytes);
+  void* base = nullptr;
+  int32_t rc = scratch_address(&base);
+  if (rc != RMT_OK) return rc;
+  // The scratch stands in for the bound workspace during this call only.
+  void* const ws = M->ws;
+  const size_t ws_bytes = M->ws_bytes;
+  const bool timing = M->timing;
+  M->ws = base;
+  M->ws_bytes = kStaticScratchBytes;
+  M->timing = false;        // no event is created or recorded
+  carve_workspace(M);
+  rc = check_forward_args(M, tokens, mem0, out);
+  if (rc == RMT_OK) rc = start_forward(M, mem0, out);
+  if (rc == RMT_OK) rc = sweep_diagonals(M, tokens, out);
+  M->ws = ws;
+  M->ws_bytes = ws_bytes;
+  M->timing = timing;
+  carve_workspace(M);
+  return rc;
 }
 
 int32_t rmt_forward_sequential(rmt_model* M, const void* tokens, const void* mem0, rmt_output* out) {

@@ -163,6 +163,26 @@ def test_workspace_too_small_after_batch_grows():
     lib.rmt_model_destroy(h)
 
 
+def test_static_forward_refuses_models_beyond_its_scratch():
+    """rmt_forward_diagonal_static compares the workspace a model needs with
+    its 64 MiB array before any device call."""
+    Lib = _L()
+    h = _create(ri.LLAMA_1B)
+    need = _bytes(h, Lib.RMT_BUF_WORKSPACE)
+    assert need > Lib.STATIC_SCRATCH_BYTES
+    out = Lib.RmtOutput(FAKE, FAKE)
+    p = C.c_void_p(FAKE)
+    assert Lib.lib().rmt_forward_diagonal_static(h, p, p, C.byref(out)) == Lib.RMT_EWORKSPACE
+    assert b"static scratch" in Lib.lib().rmt_last_error()
+    assert Lib.lib().rmt_forward_diagonal_static(None, p, p, C.byref(out)) == Lib.RMT_EINVAL
+    Lib.lib().rmt_model_destroy(h)
+    # the tiny grids fit
+    for cfg in (ri.TINY_LLAMA, ri.TINY_ENCODER_POSTNORM, ri.TINY_LINEAR_GELU):
+        h = _create(cfg)
+        assert _bytes(h, Lib.RMT_BUF_WORKSPACE) <= Lib.STATIC_SCRATCH_BYTES
+        Lib.lib().rmt_model_destroy(h)
+
+
 # ---------------------------------------------------------------------------
 # The Python binding's own checks (no library call is reached)
 # ---------------------------------------------------------------------------
