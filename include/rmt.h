@@ -70,13 +70,24 @@ extern "C" {
 #define RMT_CELL_LLAMA 2
 #define RMT_CELL_ENCODER 3
 
-/* Storage / arithmetic types. */
+/* Storage / arithmetic types.  A model's dtype is the type of its 16-bit
+ * storage and MFMA operands (weights, normalised rows, Q/K/V, probabilities,
+ * attention output, SwiGLU output); the residual stream, accumulation and
+ * norm/softmax arithmetic are fp32 in every case.
+ *   RMT_F32   LINEAR_GELU cells: everything fp32.
+ *   RMT_BF16  bf16 operands (the other cells).
+ *   RMT_F16   IEEE half operands, LLAMA cells only: the same MFMA rate and
+ *             three more mantissa bits than bf16.  bf16 weights convert
+ *             exactly unless their magnitude is below 2^-17 (rounded to
+ *             fp16's 2^-24 grid) or above 65504 (rejected by no check:
+ *             they become infinite). */
 #define RMT_F32 0
 #define RMT_BF16 1
+#define RMT_F16 2
 
 typedef struct rmt_config {
   int32_t cell;        /* RMT_CELL_*                                          */
-  int32_t dtype;       /* RMT_F32 (LINEAR_GELU) or RMT_BF16 (the other cells) */
+  int32_t dtype;       /* RMT_F32 (LINEAR_GELU), RMT_BF16, or RMT_F16 (LLAMA) */
   int32_t L;           /* layers                                              */
   int32_t S;           /* segments per forward call                           */
   int32_t n;           /* segment tokens                                      */
@@ -100,8 +111,9 @@ typedef struct rmt_config {
  * packs them into the caller's weight buffer, after which the caller may free
  * them -- except `embed`, which every forward call reads and which must
  * outlive the model.  Element type of the
- * matrices: fp32 for RMT_F32 models; bf16 (or fp32, rounded to nearest even
- * while packing) for RMT_BF16 models, as given by `weight_dtype`.  Gains,
+ * matrices: fp32 for RMT_F32 models; bf16 or fp32 for RMT_BF16 and RMT_F16
+ * models, as given by `weight_dtype`, rounded to nearest even into the
+ * model's 16-bit type while packing.  Gains,
  * shifts and biases (g1, g2, b, beta*, b*) are always fp32.  Unused fields
  * may be NULL.
  *   LINEAR_GELU: w [L][d][d], b [L][d]
@@ -334,7 +346,7 @@ int32_t rmt_pack_weight(int32_t L, int32_t K, int32_t N, const void* src, int32_
  *   B           device [Lw][N][K] as produced by rmt_pack_weight
  *   group_layer host int32 [G], each in [0, Lw)
  *   C           device [G][M][N]
- *   dtype       element type of A, B and C: RMT_BF16
+ *   dtype       element type of A, B and C: RMT_BF16 or RMT_F16
  * 1 <= G <= 32 per call, K a multiple of 8, N a multiple of 64.
  * Errors: RMT_EINVAL (sizes, NULL pointers, a layer index outside [0, Lw)),
  * RMT_EUNSUPPORTED (dtype), RMT_EHIP. */

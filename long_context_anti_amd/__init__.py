@@ -13,7 +13,7 @@ from typing import Dict, Optional
 import numpy as np
 
 from . import _lib
-from ._lib import (RMT_BF16, RMT_BUF_WEIGHTS, RMT_BUF_WORKSPACE, RMT_CELL_ENCODER,
+from ._lib import (RMT_BF16, RMT_F16, RMT_BUF_WEIGHTS, RMT_BUF_WORKSPACE, RMT_CELL_ENCODER,
                    RMT_CELL_LINEAR_GELU, RMT_CELL_LLAMA, RMT_CELL_NORM_SWIGLU, RMT_F32, STAGES,
                    RmtConfig, RmtError, RmtOutput, RmtWeights, check, lib)
 
@@ -21,7 +21,7 @@ __all__ = [
     "RMTModel", "RmtError", "diag_schedule", "grouped_gemm", "pack_weight", "causal_attention",
     "attention", "STAGES",
     "RMT_CELL_LINEAR_GELU", "RMT_CELL_NORM_SWIGLU", "RMT_CELL_LLAMA", "RMT_CELL_ENCODER", "RMT_F32",
-    "RMT_BF16",
+    "RMT_BF16", "RMT_F16",
 ]
 
 
@@ -83,8 +83,8 @@ def pack_weight(src, dst, stream=None) -> None:
 
 def grouped_gemm(A, B, group_layer, C_out, stream=None) -> None:
     """C_out[g] = A[g] @ B[group_layer[g]]^T with A [G, M, K], B [Lw, N, K],
-    C_out [G, M, N], all bf16 device tensors; group_layer a host int sequence
-    with every entry in [0, Lw)."""
+    C_out [G, M, N], all bf16 or all fp16 device tensors; group_layer a host
+    int sequence with every entry in [0, Lw)."""
     import torch
     G, M, K = A.shape
     Lw, N = B.shape[0], B.shape[1]
@@ -93,11 +93,11 @@ def grouped_gemm(A, B, group_layer, C_out, stream=None) -> None:
         raise ValueError(f"group_layer has {len(layers)} entries, A has {G} groups")
     if any(not 0 <= x < Lw for x in layers):
         raise ValueError(f"group_layer entries must lie in [0, {Lw})")
-    _require_all([(A, "A", torch.bfloat16, (G, M, K)), (B, "B", torch.bfloat16, (Lw, N, K)),
-                  (C_out, "C_out", torch.bfloat16, (G, M, N))])
+    dt = A.dtype if A.dtype in (torch.bfloat16, torch.float16) else torch.bfloat16
+    _require_all([(A, "A", dt, (G, M, K)), (B, "B", dt, (Lw, N, K)), (C_out, "C_out", dt, (G, M, N))])
     gl = (C.c_int32 * G)(*layers)
-    check(lib().rmt_grouped_gemm(G, M, N, K, Lw, _ptr(A), _ptr(B), gl, _ptr(C_out), RMT_BF16,
-                                 _stream(stream)))
+    check(lib().rmt_grouped_gemm(G, M, N, K, Lw, _ptr(A), _ptr(B), gl, _ptr(C_out),
+                                 RMT_F16 if dt == torch.float16 else RMT_BF16, _stream(stream)))
 
 
 def attention(qkv, out, n_heads: int, n_kv_heads: int, head_dim: int, causal: bool = True,

@@ -30,6 +30,7 @@ RMT_CELL_LLAMA = 2
 RMT_CELL_ENCODER = 3
 RMT_F32 = 0
 RMT_BF16 = 1
+RMT_F16 = 2
 
 STAGES = ["gather", "norm1", "qkv", "attn", "oproj", "norm2", "gateup", "down", "linear"]
 RMT_NUM_STAGES = len(STAGES)

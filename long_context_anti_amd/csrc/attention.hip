@@ -39,8 +39,6 @@
 namespace rmt {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -52,12 +50,39 @@ constexpr int BUF_FLAGS = 0x00020000;        // raw buffer, 32-bit data format
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-  bf16x2 v;
-  v[0] = (__bf16)lo;              // v_cvt_pk_bf16_f32: round to nearest even
-  v[1] = (__bf16)hi;
-  return __builtin_bit_cast(uint32_t, v);
-}
+// The 16-bit type of Q/K/V, the probabilities and the output: bf16, or IEEE
+// half (F16).  `pack` rounds two fp32 values to nearest even
+// (v_cvt_pk_bf16_f32 / v_cvt_pk_f16_f32); `one2` is a packed pair of ones.
+template <bool F16>
+struct Half16 {
+  typedef __bf16 x8 __attribute__((ext_vector_type(8)));
+  typedef __bf16 x2 __attribute__((ext_vector_type(2)));
+  static constexpr uint32_t one2 = 0x3F803F80u;
+  static __device__ __forceinline__ f32x4 mfma(x8 a, x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ uint32_t pack(float lo, float hi) {
+    x2 v;
+    v[0] = (__bf16)lo;
+    v[1] = (__bf16)hi;
+    return __builtin_bit_cast(uint32_t, v);
+  }
+};
+template <>
+struct Half16<true> {
+  typedef _Float16 x8 __attribute__((ext_vector_type(8)));
+  typedef _Float16 x2 __attribute__((ext_vector_type(2)));
+  static constexpr uint32_t one2 = 0x3C003C00u;
+  static __device__ __forceinline__ f32x4 mfma(x8 a, x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ uint32_t pack(float lo, float hi) {
+    x2 v;
+    v[0] = (_Float16)lo;
+    v[1] = (_Float16)hi;
+    return __builtin_bit_cast(uint32_t, v);
+  }
+};
 
 // Maximum over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (the four lane groups
 // that hold one query column), with the gfx950 cross-row lane swaps.
@@ -95,10 +120,12 @@ __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rs, uint8_t* d
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)dst, 16, voff, soff, 0, 0);
 }
 
-template <int HD, int QB, bool CAUSAL, bool QPRE>
+template <int HD, int QB, bool CAUSAL, bool QPRE, bool F16>
 __global__ __launch_bounds__(256, HD == 64 ? 4 : 2) void attention_kernel(const uint16_t* __restrict__ qkv,
                                                            uint16_t* __restrict__ out, int R,
                                                            int Hq, int Hkv, float scale_log2) {
+  using H = Half16<F16>;
+  typedef typename H::x8 op8;
   constexpr int QT = QB / 16;     // query tiles of 16 per wave
   constexpr int KS = HD / 32;     // k-steps of 32 over the head dimension
   constexpr int HT = HD / 16;     // head-dimension tiles of 16 in O^T
@@ -141,7 +168,7 @@ __global__ __launch_bounds__(256, HD == 64 ? 4 : 2) void attention_kernel(const 
   const uint16_t* base = qkv + (size_t)g * R * ld;
 
   // Q^T as the B operand: lane holds Q[q0 + 16 qt + c16][32 ks + 8 g4 + 0..7].
-  bf16x8 qf[QT][KS];
+  op8 qf[QT][KS];
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
     const int q = q0 + 16 * qt + c16;
@@ -149,7 +176,7 @@ __global__ __launch_bounds__(256, HD == 64 ? 4 : 2) void attention_kernel(const 
     for (int ks = 0; ks < KS; ++ks) {
       u32x4 v = {0u, 0u, 0u, 0u};
       if (q < R) v = *(const u32x4*)(base + (size_t)q * ld + (size_t)h * HD + 32 * ks + 8 * g4);
-      qf[qt][ks] = __builtin_bit_cast(bf16x8, v);
+      qf[qt][ks] = __builtin_bit_cast(op8, v);
     }
   }
 
@@ -173,8 +200,8 @@ __global__ __launch_bounds__(256, HD == 64 ? 4 : 2) void attention_kernel(const 
     osum[qt] = f32x4{0.f, 0.f, 0.f, 0.f};
     c0[qt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  const uint32_t one2 = c16 == 0 ? 0x3F803F80u : 0u;   // two bf16 ones, or zeros
-  const bf16x8 ones_row = __builtin_bit_cast(bf16x8, u32x4{one2, one2, one2, one2});
+  const uint32_t one2 = c16 == 0 ? H::one2 : 0u;   // two ones, or zeros
+  const op8 ones_row = __builtin_bit_cast(op8, u32x4{one2, one2, one2, one2});
 
   // K/V block loads straight into LDS: wave-wide load q of a block moves
   // 1 KiB, rows RPL q .. RPL q + RPL - 1, lane L landing at byte 16 L, i.e.
@@ -232,12 +259,11 @@ __global__ __launch_bounds__(256, HD == 64 ? 4 : 2) void attention_kernel(const 
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) {
-        const bf16x8 kf = __builtin_bit_cast(
-            bf16x8, *(const u32x4*)(K_ + (16 * kt + c16) * ROWB + 16 * ((4 * ks + g4) ^ kswz)));
+        const op8 kf = __builtin_bit_cast(
+            op8, *(const u32x4*)(K_ + (16 * kt + c16) * ROWB + 16 * ((4 * ks + g4) ^ kswz)));
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt)
-          s[kt][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[qt][ks], ks == 0 ? c0[qt] : s[kt][qt],
-                                                              0, 0, 0);
+          s[kt][qt] = H::mfma(kf, qf[qt][ks], ks == 0 ? c0[qt] : s[kt][qt]);
       }
     if ((CAUSAL && k0 + KB - 1 > q0) || (k0 + KB > R)) {   // wave-uniform
       // element (kt, j) holds key k0 + 16 kt + 4 g4 + j: it is masked when
@@ -357,16 +383,16 @@ __global__ __launch_bounds__(256, HD == 64 ? 4 : 2) void attention_kernel(const 
     const int vswz = swz<HD>(tr_row);        // rows 32 ks2 + tr_row (+ 16): same permutation
 #pragma unroll
     for (int ks2 = 0; ks2 < 2; ++ks2) {
-      bf16x8 pf[QT];
+      op8 pf[QT];
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt) {
         u32x4 w;
-        w[0] = pack_bf16(s[2 * ks2][qt][0], s[2 * ks2][qt][1]);
-        w[1] = pack_bf16(s[2 * ks2][qt][2], s[2 * ks2][qt][3]);
-        w[2] = pack_bf16(s[2 * ks2 + 1][qt][0], s[2 * ks2 + 1][qt][1]);
-        w[3] = pack_bf16(s[2 * ks2 + 1][qt][2], s[2 * ks2 + 1][qt][3]);
-        pf[qt] = __builtin_bit_cast(bf16x8, w);
-        osum[qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones_row, pf[qt], osum[qt], 0, 0, 0);
+        w[0] = H::pack(s[2 * ks2][qt][0], s[2 * ks2][qt][1]);
+        w[1] = H::pack(s[2 * ks2][qt][2], s[2 * ks2][qt][3]);
+        w[2] = H::pack(s[2 * ks2 + 1][qt][0], s[2 * ks2 + 1][qt][1]);
+        w[3] = H::pack(s[2 * ks2 + 1][qt][2], s[2 * ks2 + 1][qt][3]);
+        pf[qt] = __builtin_bit_cast(op8, w);
+        osum[qt] = H::mfma(ones_row, pf[qt], osum[qt]);
       }
 #pragma unroll
       for (int ht = 0; ht < HT; ++ht) {
@@ -382,10 +408,10 @@ __global__ __launch_bounds__(256, HD == 64 ? 4 : 2) void attention_kernel(const 
         w[1] = wl[1];
         w[2] = wh[0];
         w[3] = wh[1];
-        const bf16x8 vf = __builtin_bit_cast(bf16x8, w);
+        const op8 vf = __builtin_bit_cast(op8, w);
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt)
-          o[ht][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[qt], o[ht][qt], 0, 0, 0);
+          o[ht][qt] = H::mfma(vf, pf[qt], o[ht][qt]);
       }
     }
 
@@ -403,8 +429,8 @@ __global__ __launch_bounds__(256, HD == 64 ? 4 : 2) void attention_kernel(const 
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
       u32x2 w;
-      w[0] = pack_bf16(o[ht][qt][0] * inv, o[ht][qt][1] * inv);
-      w[1] = pack_bf16(o[ht][qt][2] * inv, o[ht][qt][3] * inv);
+      w[0] = H::pack(o[ht][qt][0] * inv, o[ht][qt][1] * inv);
+      w[1] = H::pack(o[ht][qt][2] * inv, o[ht][qt][3] * inv);
       *(u32x2*)(orow + 16 * ht + 4 * g4) = w;
     }
   }
@@ -413,13 +439,14 @@ __global__ __launch_bounds__(256, HD == 64 ? 4 : 2) void attention_kernel(const 
 }  // namespace
 
 hipError_t launch_attention(const uint16_t* qkv, uint16_t* out, int G, int R, int Hq, int Hkv,
-                            int hd, bool causal, bool q_prescaled, hipStream_t stream) {
+                            int hd, bool causal, bool q_prescaled, hipStream_t stream, bool f16) {
   if (G == 0 || R == 0) return hipSuccess;
   if (Hkv < 1 || Hq < 1 || R < 0 || Hq % Hkv != 0) return hipErrorInvalidValue;
   const int rep = Hq / Hkv;
   if (!(rep == 1 || rep == 2 || rep % 4 == 0)) return hipErrorInvalidValue;
   // K/V loads address one cell's rows with 32-bit buffer offsets
   if ((size_t)R * (size_t)(Hq + 2 * Hkv) * (size_t)hd * 2 > (size_t)INT32_MAX) return hipErrorInvalidValue;
+  if (f16 && !(causal && q_prescaled)) return hipErrorInvalidValue;   // fp16: the LLaMA cell's stage only
   const float scale_log2 = attention_scale_log2(hd);
   constexpr int QB = 32;   // measured faster than 64: lower register use, more waves
   const int hw = rep >= 4 ? 4 : rep;
@@ -430,20 +457,22 @@ hipError_t launch_attention(const uint16_t* qkv, uint16_t* out, int G, int R, in
     hipLaunchKernelGGL(kern, grid, dim3(256), 0, stream, qkv, out, R, Hq, Hkv, scale_log2);
   };
   if (hd == 64) {
-    if (q_prescaled) {
-      if (causal) go(attention_kernel<64, QB, true, true>);
-      else go(attention_kernel<64, QB, false, true>);
+    if (f16) go(attention_kernel<64, QB, true, true, true>);
+    else if (q_prescaled) {
+      if (causal) go(attention_kernel<64, QB, true, true, false>);
+      else go(attention_kernel<64, QB, false, true, false>);
     } else {
-      if (causal) go(attention_kernel<64, QB, true, false>);
-      else go(attention_kernel<64, QB, false, false>);
+      if (causal) go(attention_kernel<64, QB, true, false, false>);
+      else go(attention_kernel<64, QB, false, false, false>);
     }
   } else if (hd == 128) {
-    if (q_prescaled) {
-      if (causal) go(attention_kernel<128, QB, true, true>);
-      else go(attention_kernel<128, QB, false, true>);
+    if (f16) go(attention_kernel<128, QB, true, true, true>);
+    else if (q_prescaled) {
+      if (causal) go(attention_kernel<128, QB, true, true, false>);
+      else go(attention_kernel<128, QB, false, true, false>);
     } else {
-      if (causal) go(attention_kernel<128, QB, true, false>);
-      else go(attention_kernel<128, QB, false, false>);
+      if (causal) go(attention_kernel<128, QB, true, false, false>);
+      else go(attention_kernel<128, QB, false, false, false>);
     }
   } else {
     return hipErrorInvalidValue;

@@ -14,6 +14,13 @@ typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
 // fp32 -> bf16, round to nearest even (v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint16_t to_bf16(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 
+// fp32 -> the 16-bit type of a launch: bf16, or fp16 (F16), round to nearest even.
+template <bool F16>
+__device__ __forceinline__ uint16_t to_16(float f) {
+  if constexpr (F16) return __builtin_bit_cast(uint16_t, (_Float16)f);
+  else return to_bf16(f);
+}
+
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
 __device__ __forceinline__ float wave_sum(float v) {
@@ -35,7 +42,8 @@ enum NormMode : int { NORM_RMS = 0, NORM_LAYER = 1, NORM_CAST = 2 };
 //               (the centred second pass keeps the variance accurate for
 //               rows with a large mean)
 //   NORM_CAST:  y = x (a bf16 copy of the rows)
-template <int VPL, int MODE, bool F32OUT>
+// F16: the packed 16-bit result is fp16 instead of bf16.
+template <int VPL, int MODE, bool F32OUT, bool F16 = false>
 __global__ __launch_bounds__(256) void norm_kernel(int total_rows, int R, int d, int split_in,
                                                    int split_out, GroupTable tab,
                                                    const float* __restrict__ gamma,
@@ -109,10 +117,10 @@ __global__ __launch_bounds__(256) void norm_kernel(int total_rows, int R, int d,
     if constexpr (LAYER) y += sh;
     if (dst) {
       u16x4 o;
-      o[0] = to_bf16(y[0]);
-      o[1] = to_bf16(y[1]);
-      o[2] = to_bf16(y[2]);
-      o[3] = to_bf16(y[3]);
+      o[0] = to_16<F16>(y[0]);
+      o[1] = to_16<F16>(y[1]);
+      o[2] = to_16<F16>(y[2]);
+      o[3] = to_16<F16>(y[3]);
       *(u16x4*)(dst + c) = o;
     }
     if constexpr (F32OUT) *(f32x4*)(dst32 + c) = y;
@@ -195,8 +203,9 @@ __global__ __launch_bounds__(256) void linear_gelu_f32_kernel(int R, int d, int 
   o[col] = y;
 }
 
-// dst[l][r][k] (bf16) from src[l][k][col(r)] through a 64 x 64 LDS tile.
-template <bool SRC_BF16>
+// dst[l][r][k] (bf16, or fp16 with DST_F16) from src[l][k][col(r)] through a
+// 64 x 64 LDS tile.
+template <bool SRC_BF16, bool DST_F16>
 __global__ __launch_bounds__(256) void pack_kernel(int K, int N_src, const void* __restrict__ src0,
                                                    const void* __restrict__ src1, int interleave,
                                                    uint16_t* __restrict__ dst) {
@@ -221,8 +230,13 @@ __global__ __launch_bounds__(256) void pack_kernel(int K, int N_src, const void*
     uint16_t v = 0;
     if (k < K && r < N_dst) {
       const size_t idx = ((size_t)l * K + k) * N_src + col;
-      if (SRC_BF16) v = ((const uint16_t*)src)[idx];
-      else v = to_bf16(((const float*)src)[idx]);
+      if constexpr (DST_F16) {
+        const float x = SRC_BF16 ? bf16_to_f32(((const uint16_t*)src)[idx]) : ((const float*)src)[idx];
+        v = to_16<true>(x);
+      } else {
+        if (SRC_BF16) v = ((const uint16_t*)src)[idx];
+        else v = to_bf16(((const float*)src)[idx]);
+      }
     }
     tile[i][tx] = v;
   }
@@ -236,7 +250,7 @@ __global__ __launch_bounds__(256) void pack_kernel(int K, int N_src, const void*
 
 }  // namespace
 
-template <int MODE, bool F32OUT>
+template <int MODE, bool F32OUT, bool F16 = false>
 hipError_t launch_norm(int G, int R, int d, int split_in, int split_out, const GroupTable& tab,
                        const float* gamma, const float* beta, float eps, uint16_t* out,
                        hipStream_t stream) {
@@ -245,16 +259,17 @@ hipError_t launch_norm(int G, int R, int d, int split_in, int split_out, const G
   // 8 (16) float4 per lane keep rows of up to 2048 (4096) elements in
   // registers; the smaller variant leaves room for more waves per SIMD
   if (d <= 2048)
-    hipLaunchKernelGGL((norm_kernel<8, MODE, F32OUT>), dim3((rows + 3) / 4), dim3(256), 0, stream,
+    hipLaunchKernelGGL((norm_kernel<8, MODE, F32OUT, F16>), dim3((rows + 3) / 4), dim3(256), 0, stream,
                        rows, R, d, split_in, split_out, tab, gamma, beta, eps, out);
   else
-    hipLaunchKernelGGL((norm_kernel<16, MODE, F32OUT>), dim3((rows + 3) / 4), dim3(256), 0, stream,
+    hipLaunchKernelGGL((norm_kernel<16, MODE, F32OUT, F16>), dim3((rows + 3) / 4), dim3(256), 0, stream,
                        rows, R, d, split_in, split_out, tab, gamma, beta, eps, out);
   return hipGetLastError();
 }
 
 hipError_t launch_rmsnorm(int G, int R, int d, int split_in, const GroupTable& tab,
-                          const float* gamma, float eps, uint16_t* out, hipStream_t stream) {
+                          const float* gamma, float eps, uint16_t* out, hipStream_t stream, bool f16) {
+  if (f16) return launch_norm<NORM_RMS, false, true>(G, R, d, split_in, R, tab, gamma, nullptr, eps, out, stream);
   return launch_norm<NORM_RMS, false>(G, R, d, split_in, R, tab, gamma, nullptr, eps, out, stream);
 }
 
@@ -302,15 +317,20 @@ hipError_t launch_linear_gelu_f32(int G, int R, int d, int split_in, int split_o
 }
 
 hipError_t launch_pack(int L, int K, int N_src, const void* src0, const void* src1,
-                       int src_is_bf16, int interleave, uint16_t* dst, hipStream_t stream) {
+                       int src_is_bf16, int interleave, uint16_t* dst, hipStream_t stream,
+                       int dst_f16) {
   const int N_dst = interleave ? 2 * N_src : N_src;
   dim3 grid((N_dst + 63) / 64, (K + 63) / 64, L);
-  if (src_is_bf16)
-    hipLaunchKernelGGL(pack_kernel<true>, grid, dim3(256), 0, stream, K, N_src, src0, src1,
-                       interleave, dst);
-  else
-    hipLaunchKernelGGL(pack_kernel<false>, grid, dim3(256), 0, stream, K, N_src, src0, src1,
-                       interleave, dst);
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, grid, dim3(256), 0, stream, K, N_src, src0, src1, interleave, dst);
+  };
+  if (src_is_bf16) {
+    if (dst_f16) go(pack_kernel<true, true>);
+    else go(pack_kernel<true, false>);
+  } else {
+    if (dst_f16) go(pack_kernel<false, true>);
+    else go(pack_kernel<false, false>);
+  }
   return hipGetLastError();
 }
 

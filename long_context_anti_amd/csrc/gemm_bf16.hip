@@ -34,12 +34,10 @@
 namespace rmt {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int BN = 256;
 constexpr int BK = 64;
@@ -51,13 +49,38 @@ constexpr int BUF_FLAGS = 0x00020000;        // raw buffer, 32-bit data format
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-// Two fp32 -> packed bf16, round to nearest even (v_cvt_pk_bf16_f32).
-__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-  bf16x2 v;
-  v[0] = (__bf16)lo;
-  v[1] = (__bf16)hi;
-  return __builtin_bit_cast(uint32_t, v);
-}
+// The 16-bit type of a launch's operands and 16-bit results: bf16, or IEEE
+// half (fp16: three more mantissa bits, the same MFMA rate).  `pack` turns
+// two fp32 values into the packed pair, rounding to nearest even
+// (v_cvt_pk_bf16_f32 / v_cvt_pk_f16_f32).
+template <bool F16>
+struct Half16 {
+  typedef __bf16 x8 __attribute__((ext_vector_type(8)));
+  typedef __bf16 x2 __attribute__((ext_vector_type(2)));
+  static __device__ __forceinline__ f32x16 mfma(x8 a, x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ uint32_t pack(float lo, float hi) {
+    x2 v;
+    v[0] = (__bf16)lo;
+    v[1] = (__bf16)hi;
+    return __builtin_bit_cast(uint32_t, v);
+  }
+};
+template <>
+struct Half16<true> {
+  typedef _Float16 x8 __attribute__((ext_vector_type(8)));
+  typedef _Float16 x2 __attribute__((ext_vector_type(2)));
+  static __device__ __forceinline__ f32x16 mfma(x8 a, x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ uint32_t pack(float lo, float hi) {
+    x2 v;
+    v[0] = (_Float16)lo;
+    v[1] = (_Float16)hi;
+    return __builtin_bit_cast(uint32_t, v);
+  }
+};
 
 // Chunk permutation of LDS row r: logical 16-byte chunk c sits at physical
 // position c ^ swz(r).  It depends only on r mod 32, and 16-byte reads of 32
@@ -88,9 +111,12 @@ __device__ __forceinline__ int xcd_remap(int bid, int nb) {
 // BM x BN output tile per workgroup; WTM x WTN is one wave's sub-tile and the
 // workgroup has one wave per sub-tile.
 // BNT: weight slices are loaded with the non-temporal policy (see launch_one).
-template <int EPI, int BM, int WTM, int WTN, bool BNT>
+// F16: operands and 16-bit results in fp16 instead of bf16.
+template <int EPI, int BM, int WTM, int WTN, bool BNT, bool F16>
 __global__ __launch_bounds__((BM / WTM) * (BN / WTN) * 64, 1) void gemm_bf16_kernel(
     GemmArgs a, GroupTable tab) {
+  using H = Half16<F16>;
+  typedef typename H::x8 op8;
   constexpr int STAGE_BYTES = (BM + BN) * ROWB;
   // The MFMAs take the operands swapped, so the accumulator holds C^T blocks
   // and every lane owns four consecutive output columns of one row: the
@@ -208,15 +234,15 @@ __global__ __launch_bounds__((BM / WTM) * (BN / WTN) * 64, 1) void gemm_bf16_ker
   const int b_row = BM * ROWB + (wn * WTN + r32) * ROWB;
   auto compute = [&](int stage) __attribute__((always_inline)) {
     const uint8_t* sbase = smem + stage * STAGE_BYTES;
-    bf16x8 af[2][MI], bfr[2][NI];
+    op8 af[2][MI], bfr[2][NI];
     auto frags = [&](int j, int buf) __attribute__((always_inline)) {
       const int cb = ((c0 + j) ^ sw) * 16;
 #pragma unroll
       for (int i = 0; i < MI; ++i)
-        af[buf][i] = __builtin_bit_cast(bf16x8, *(const u32x4*)(sbase + a_row + i * 32 * ROWB + cb));
+        af[buf][i] = __builtin_bit_cast(op8, *(const u32x4*)(sbase + a_row + i * 32 * ROWB + cb));
 #pragma unroll
       for (int t = 0; t < NI; ++t)
-        bfr[buf][t] = __builtin_bit_cast(bf16x8, *(const u32x4*)(sbase + b_row + t * 32 * ROWB + cb));
+        bfr[buf][t] = __builtin_bit_cast(op8, *(const u32x4*)(sbase + b_row + t * 32 * ROWB + cb));
     };
     frags(0, 0);
 #pragma unroll
@@ -227,9 +253,9 @@ __global__ __launch_bounds__((BM / WTM) * (BN / WTN) * 64, 1) void gemm_bf16_ker
 #pragma unroll
         for (int t = 0; t < NI; ++t)
           if constexpr (SWAP)
-            acc[i][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j & 1][t], af[j & 1][i], acc[i][t], 0, 0, 0);
+            acc[i][t] = H::mfma(bfr[j & 1][t], af[j & 1][i], acc[i][t]);
           else
-            acc[i][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[j & 1][i], bfr[j & 1][t], acc[i][t], 0, 0, 0);
+            acc[i][t] = H::mfma(af[j & 1][i], bfr[j & 1][t], acc[i][t]);
       // let the scheduler interleave LDS reads with the MFMA chain
       __builtin_amdgcn_iglp_opt(1);
     }
@@ -401,7 +427,7 @@ __global__ __launch_bounds__((BM / WTM) * (BN / WTN) * 64, 1) void gemm_bf16_ker
           }
           if constexpr (EPI == EPI_BIAS_BF16) x *= qs[t];
           const int c = (t * 4 + e4) ^ swz_o(r32);
-          *(u32x2*)(sp + r32 * WTN + c * 8 + half_lane) = u32x2{pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3])};
+          *(u32x2*)(sp + r32 * WTN + c * 8 + half_lane) = u32x2{H::pack(x[0], x[1]), H::pack(x[2], x[3])};
         }
       lds_sync();
       // OCH lanes per staged row, 64 / OCH rows per access.
@@ -448,8 +474,8 @@ __global__ __launch_bounds__((BM / WTM) * (BN / WTN) * 64, 1) void gemm_bf16_ker
             x1 *= a.q_scale;
             x2 *= a.q_scale;
           }
-          *(u32x2*)(C + (size_t)row * a.ld_out + col) = u32x2{pack_bf16(x1[0], x1[1]), pack_bf16(x1[2], x1[3])};
-          *(u32x2*)(C + (size_t)row * a.ld_out + col2) = u32x2{pack_bf16(x2[0], x2[1]), pack_bf16(x2[2], x2[3])};
+          *(u32x2*)(C + (size_t)row * a.ld_out + col) = u32x2{H::pack(x1[0], x1[1]), H::pack(x1[2], x1[3])};
+          *(u32x2*)(C + (size_t)row * a.ld_out + col2) = u32x2{H::pack(x2[0], x2[1]), H::pack(x2[2], x2[3])};
         }
       }
       lds_sync();
@@ -479,7 +505,7 @@ __global__ __launch_bounds__((BM / WTM) * (BN / WTN) * 64, 1) void gemm_bf16_ker
             }
             const int chunk = e4 ^ ((r32 >> 2) & 3);
             *(u32x2*)(piece + r32 * 32 + chunk * 8 + half_lane) =
-                u32x2{pack_bf16(u[0], u[1]), pack_bf16(u[2], u[3])};
+                u32x2{H::pack(u[0], u[1]), H::pack(u[2], u[3])};
           }
         }
       lds_sync();
@@ -532,14 +558,14 @@ __global__ __launch_bounds__((BM / WTM) * (BN / WTN) * 64, 1) void gemm_bf16_ker
 // GEMMs.  With longer K the activations exceed L2 anyway, and the reuse of a
 // weight panel by the cell's row tiles matters more (the hint cost the
 // K = 8192 projections 0.4-2%, and 2-4% at K = 4096).
-template <int EPI, int BM, int WTM, int WTN>
+template <int EPI, bool F16, int BM, int WTM, int WTN>
 void launch_one(const GemmArgs& a, const GroupTable& tab, hipStream_t stream) {
   const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN) * tab.G;
   constexpr int threads = (BM / WTM) * (BN / WTN) * 64;
   if (a.K <= 2048)
-    hipLaunchKernelGGL((gemm_bf16_kernel<EPI, BM, WTM, WTN, true>), dim3(tiles), dim3(threads), 0, stream, a, tab);
+    hipLaunchKernelGGL((gemm_bf16_kernel<EPI, BM, WTM, WTN, true, F16>), dim3(tiles), dim3(threads), 0, stream, a, tab);
   else
-    hipLaunchKernelGGL((gemm_bf16_kernel<EPI, BM, WTM, WTN, false>), dim3(tiles), dim3(threads), 0, stream, a, tab);
+    hipLaunchKernelGGL((gemm_bf16_kernel<EPI, BM, WTM, WTN, false, F16>), dim3(tiles), dim3(threads), 0, stream, a, tab);
 }
 
 // Tile shapes.  The operand bytes a tile pulls from L2 per MFMA fall as the
@@ -575,7 +601,7 @@ double tile_cost(const GemmArgs& a, int G, int bm, double speed) {
   return (double)rounds * bm / speed;
 }
 
-template <int EPI>
+template <int EPI, bool F16>
 void launch_epi(const GemmArgs& a, const GroupTable& tab, hipStream_t stream) {
   const bool wide_heads = EPI == EPI_QKV_ROPE && a.hd == 128;
   const double c288 = wide_heads ? 1e300 : tile_cost(a, tab.G, 288, 1.00);
@@ -583,35 +609,45 @@ void launch_epi(const GemmArgs& a, const GroupTable& tab, hipStream_t stream) {
   const double c192 = wide_heads ? 1e300 : tile_cost(a, tab.G, 192, 0.85);
   const double c128 = tile_cost(a, tab.G, 128, 0.72);
   if (c288 <= c256 && c288 <= c192 && c288 <= c128) {
-    launch_one<EPI, 288, 96, 64>(a, tab, stream);
+    launch_one<EPI, F16, 288, 96, 64>(a, tab, stream);
   } else if (c256 <= c192 && c256 <= c128) {
-    launch_one<EPI, 256, 64, 128>(a, tab, stream);
+    launch_one<EPI, F16, 256, 64, 128>(a, tab, stream);
   } else if (c192 <= c128) {
-    launch_one<EPI, 192, 96, 64>(a, tab, stream);
+    launch_one<EPI, F16, 192, 96, 64>(a, tab, stream);
   } else if (wide_heads) {
-    launch_one<EPI, 128, 32, 128>(a, tab, stream);
+    launch_one<EPI, F16, 128, 32, 128>(a, tab, stream);
   } else {
-    launch_one<EPI, 128, 64, 64>(a, tab, stream);
+    launch_one<EPI, F16, 128, 64, 64>(a, tab, stream);
   }
 }
 
 }  // namespace
 
-hipError_t launch_gemm_bf16(int epilogue, const GemmArgs& a, const GroupTable& tab,
-                            hipStream_t stream) {
+hipError_t launch_gemm(int epilogue, const GemmArgs& a, const GroupTable& tab, hipStream_t stream) {
   if (tab.G == 0 || a.M == 0 || a.N == 0) return hipSuccess;
   const bool plain_store = epilogue == EPI_STORE_BF16 || epilogue == EPI_BIAS_BF16 ||
                            epilogue == EPI_BIAS_RELU_BF16;
   if (plain_store && a.N % 8 != 0) return hipErrorInvalidValue;   // whole 16-byte output chunks
   if (a.q_cols < 0 || a.q_cols % 32 != 0) return hipErrorInvalidValue;   // whole 32-column blocks
+  if (a.f16) {
+    // fp16 operands: the epilogues of the LLaMA-shaped cell and the plain store
+    switch (epilogue) {
+      case EPI_STORE_BF16: launch_epi<EPI_STORE_BF16, true>(a, tab, stream); break;
+      case EPI_QKV_ROPE: launch_epi<EPI_QKV_ROPE, true>(a, tab, stream); break;
+      case EPI_SWIGLU: launch_epi<EPI_SWIGLU, true>(a, tab, stream); break;
+      case EPI_RESID_F32: launch_epi<EPI_RESID_F32, true>(a, tab, stream); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
   switch (epilogue) {
-    case EPI_STORE_BF16: launch_epi<EPI_STORE_BF16>(a, tab, stream); break;
-    case EPI_QKV_ROPE: launch_epi<EPI_QKV_ROPE>(a, tab, stream); break;
-    case EPI_SWIGLU: launch_epi<EPI_SWIGLU>(a, tab, stream); break;
-    case EPI_RESID_F32: launch_epi<EPI_RESID_F32>(a, tab, stream); break;
-    case EPI_BIAS_BF16: launch_epi<EPI_BIAS_BF16>(a, tab, stream); break;
-    case EPI_BIAS_RELU_BF16: launch_epi<EPI_BIAS_RELU_BF16>(a, tab, stream); break;
-    case EPI_RESID_BIAS_F32: launch_epi<EPI_RESID_BIAS_F32>(a, tab, stream); break;
+    case EPI_STORE_BF16: launch_epi<EPI_STORE_BF16, false>(a, tab, stream); break;
+    case EPI_QKV_ROPE: launch_epi<EPI_QKV_ROPE, false>(a, tab, stream); break;
+    case EPI_SWIGLU: launch_epi<EPI_SWIGLU, false>(a, tab, stream); break;
+    case EPI_RESID_F32: launch_epi<EPI_RESID_F32, false>(a, tab, stream); break;
+    case EPI_BIAS_BF16: launch_epi<EPI_BIAS_BF16, false>(a, tab, stream); break;
+    case EPI_BIAS_RELU_BF16: launch_epi<EPI_BIAS_RELU_BF16, false>(a, tab, stream); break;
+    case EPI_RESID_BIAS_F32: launch_epi<EPI_RESID_BIAS_F32, false>(a, tab, stream); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

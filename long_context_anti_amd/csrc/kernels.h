@@ -51,6 +51,8 @@ struct GemmArgs {
   const float* bias;   // EPI_*BIAS*: fp32 [Lw][N], row layer[g] added to every output row
   int q_cols;          // EPI_QKV_ROPE, EPI_BIAS_BF16: columns [0, q_cols) (a multiple of 32)
   float q_scale;       //   are multiplied by q_scale before the bf16 rounding (0 cols: none)
+  int f16;             // 1: A, B and 16-bit results are fp16 instead of bf16 (EPI_STORE_BF16,
+                       //    EPI_QKV_ROPE, EPI_SWIGLU, EPI_RESID_F32 only)
 };
 
 // Softmax scale of attention in the base-2 domain, log2(e) / sqrt(hd).  The
@@ -58,12 +60,13 @@ struct GemmArgs {
 // both sides must use this one value.
 inline float attention_scale_log2(int hd) { return 1.4426950408889634f / sqrtf((float)hd); }
 
-hipError_t launch_gemm_bf16(int epilogue, const GemmArgs& a, const GroupTable& tab,
-                            hipStream_t stream);
+hipError_t launch_gemm(int epilogue, const GemmArgs& a, const GroupTable& tab, hipStream_t stream);
 
-// Row-wise RMSNorm of every group's R rows (fp32 in, bf16 out, packed).
+// Row-wise RMSNorm of every group's R rows (fp32 in, bf16 -- or fp16 when
+// f16 is set -- out, packed).
 hipError_t launch_rmsnorm(int G, int R, int d, int split_in, const GroupTable& tab,
-                          const float* gamma, float eps, uint16_t* out, hipStream_t stream);
+                          const float* gamma, float eps, uint16_t* out, hipStream_t stream,
+                          bool f16 = false);
 // Row-wise LayerNorm (gain gamma, shift beta, both [Lw][d]), same layout.
 hipError_t launch_layernorm(int G, int R, int d, int split_in, const GroupTable& tab,
                             const float* gamma, const float* beta, float eps, uint16_t* out,
@@ -85,20 +88,25 @@ hipError_t launch_copy_rows_bf16(int n, int d, const uint16_t* src, float* dst,
 
 // Attention over each group's R rows, causal or unmasked; Hq / Hkv must be
 // 1, 2 or a multiple of 4.  q_prescaled: Q already carries the softmax scale
-// attention_scale_log2(hd) (the QKV epilogue applied it).
+// attention_scale_log2(hd) (the QKV epilogue applied it).  f16: Q/K/V, the
+// probabilities and the output are fp16 instead of bf16 (causal, prescaled
+// only: the LLaMA-shaped cell).
 hipError_t launch_attention(const uint16_t* qkv, uint16_t* out, int G, int R, int Hq, int Hkv,
-                            int hd, bool causal, bool q_prescaled, hipStream_t stream);
+                            int hd, bool causal, bool q_prescaled, hipStream_t stream,
+                            bool f16 = false);
 
 // fp32 linear + bias + GELU cell with the split write-back.
 hipError_t launch_linear_gelu_f32(int G, int R, int d, int split_in, int split_out,
                                   const GroupTable& tab, const float* W, const float* bias,
                                   hipStream_t stream);
 
-// Weight packing: dst[l][r][k] = src_sel(r)[l][k][col(r)] as bf16.
+// Weight packing: dst[l][r][k] = src_sel(r)[l][k][col(r)] as bf16, or as fp16
+// when dst_f16 is set (from fp32 or bf16, rounded to nearest even).
 // interleave == 0: dst row r <- src0 column r (N_dst = N_src).
 // interleave == 1: dst row r in block r/64: first 32 rows <- src0 columns,
 //                  last 32 rows <- src1 columns (N_dst = 2 N_src).
 hipError_t launch_pack(int L, int K, int N_src, const void* src0, const void* src1,
-                       int src_is_bf16, int interleave, uint16_t* dst, hipStream_t stream);
+                       int src_is_bf16, int interleave, uint16_t* dst, hipStream_t stream,
+                       int dst_f16 = 0);
 
 }  // namespace rmt

@@ -149,7 +149,8 @@ int32_t validate_config(const rmt_config* c) {
   }
   if (c->cell != RMT_CELL_NORM_SWIGLU && c->cell != RMT_CELL_LLAMA && c->cell != RMT_CELL_ENCODER)
     return fail(RMT_EINVAL, "unknown cell kind %d", c->cell);
-  if (c->dtype != RMT_BF16) return fail(RMT_EUNSUPPORTED, "this cell kind runs in bf16 only");
+  if (c->dtype != RMT_BF16 && !(c->dtype == RMT_F16 && c->cell == RMT_CELL_LLAMA))
+    return fail(RMT_EUNSUPPORTED, "this cell kind runs in bf16 only (fp16 operands: LLAMA cells)");
   if (c->d % 64 != 0) return fail(RMT_EUNSUPPORTED, "d must be a multiple of 64 (got %d)", c->d);
   if (c->ffn < 1 || c->ffn % 32 != 0)
     return fail(RMT_EUNSUPPORTED, "ffn must be a positive multiple of 32 (got %d)", c->ffn);
@@ -293,11 +294,13 @@ int32_t run_cells(rmt_model* M, const Cell* cells, int G, const void* tokens, co
   GemmArgs ga;
   std::memset(&ga, 0, sizeof(ga));
 
+  const bool f16 = c.dtype == RMT_F16;   // LLAMA cells only: every 16-bit operand in fp16
+  ga.f16 = f16;
   if (c.cell == RMT_CELL_LLAMA) {
     const int hd = c.head_dim, Hq = c.n_heads, Hkv = c.n_kv_heads, NQ = nqkv(c);
     // RMSNorm 1 of [M(l, s-1); X(l-1, s)]
     set_io(in_lo, in_hi, nullptr, nullptr);
-    LAUNCH(launch_rmsnorm(G, R, d, m, tab, M->g1, c.eps, M->abuf, M->stream));
+    LAUNCH(launch_rmsnorm(G, R, d, m, tab, M->g1, c.eps, M->abuf, M->stream, f16));
     MARK(RMT_STAGE_NORM1, 0.0, rows * d * 6);
     // QKV projection + RoPE on Q and K
     for (int g = 0; g < G; ++g) packed_out[g] = M->qkv + (size_t)g * R * NQ;
@@ -306,24 +309,24 @@ int32_t run_cells(rmt_model* M, const Cell* cells, int G, const void* tokens, co
     ga.split_in = R; ga.split_out = R; ga.ld_res = 0; ga.ld_out = NQ;
     ga.rope = M->rope; ga.rope_cols = (Hq + Hkv) * hd; ga.hd = hd;
     ga.q_cols = Hq * hd; ga.q_scale = attention_scale_log2(hd);   // Q leaves with the softmax scale
-    LAUNCH(launch_gemm_bf16(EPI_QKV_ROPE, ga, tab, M->stream));
+    LAUNCH(launch_gemm(EPI_QKV_ROPE, ga, tab, M->stream));
     ga.q_cols = 0;
     MARK(RMT_STAGE_QKV, 2.0 * rows * d * NQ, rows * d * 2 + G_ * NQ * d * 2 + rows * NQ * 2);
     // causal GQA attention inside each cell
-    LAUNCH(launch_attention(M->qkv, M->att, G, R, Hq, Hkv, hd, true, true, M->stream));
+    LAUNCH(launch_attention(M->qkv, M->att, G, R, Hq, Hkv, hd, true, true, M->stream, f16));
     MARK(RMT_STAGE_ATTN, 2.0 * G_ * Hq * hd * (double)R * (R + 1), rows * NQ * 2 + rows * Hq * hd * 2);
     // O projection + residual A -> H
     for (int g = 0; g < G; ++g) packed_out[g] = M->hbuf + (size_t)g * R * d;
     set_io(in_lo, in_hi, packed_out, nullptr);
     ga.A = M->att; ga.B = M->wo; ga.M = R; ga.N = d; ga.K = Hq * hd;
     ga.split_in = m; ga.split_out = R; ga.ld_res = d; ga.ld_out = d;
-    LAUNCH(launch_gemm_bf16(EPI_RESID_F32, ga, tab, M->stream));
+    LAUNCH(launch_gemm(EPI_RESID_F32, ga, tab, M->stream));
     MARK(RMT_STAGE_OPROJ, 2.0 * rows * Hq * hd * d,
          rows * Hq * hd * 2 + G_ * d * Hq * hd * 2 + rows * d * 8);
     // RMSNorm 2 of H
     for (int g = 0; g < G; ++g) packed_lo[g] = M->hbuf + (size_t)g * R * d;
     set_io(packed_lo, packed_lo, nullptr, nullptr);
-    LAUNCH(launch_rmsnorm(G, R, d, R, tab, M->g2, c.eps, M->abuf, M->stream));
+    LAUNCH(launch_rmsnorm(G, R, d, R, tab, M->g2, c.eps, M->abuf, M->stream, f16));
     MARK(RMT_STAGE_NORM2, 0.0, rows * d * 6);
   } else if (c.cell == RMT_CELL_ENCODER && c.post_norm) {
     const int hd = c.head_dim, H = c.n_heads, NQ = nqkv(c);
@@ -337,7 +340,7 @@ int32_t run_cells(rmt_model* M, const Cell* cells, int G, const void* tokens, co
     ga.A = M->abuf; ga.B = M->wqkv; ga.M = R; ga.N = NQ; ga.K = d;
     ga.split_in = R; ga.split_out = R; ga.ld_res = 0; ga.ld_out = NQ; ga.bias = M->bqkv;
     ga.q_cols = H * hd; ga.q_scale = attention_scale_log2(hd);    // Q leaves with the softmax scale
-    LAUNCH(launch_gemm_bf16(EPI_BIAS_BF16, ga, tab, M->stream));
+    LAUNCH(launch_gemm(EPI_BIAS_BF16, ga, tab, M->stream));
     ga.q_cols = 0;
     MARK(RMT_STAGE_QKV, 2.0 * rows * d * NQ, rows * d * 2 + G_ * NQ * d * 2 + rows * NQ * 2);
     LAUNCH(launch_attention(M->qkv, M->att, G, R, H, H, hd, false, true, M->stream));
@@ -347,7 +350,7 @@ int32_t run_cells(rmt_model* M, const Cell* cells, int G, const void* tokens, co
     set_io(in_lo, in_hi, packed_out, nullptr);
     ga.A = M->att; ga.B = M->wo; ga.M = R; ga.N = d; ga.K = H * hd;
     ga.split_in = m; ga.split_out = R; ga.ld_res = d; ga.ld_out = d; ga.bias = M->bo;
-    LAUNCH(launch_gemm_bf16(EPI_RESID_BIAS_F32, ga, tab, M->stream));
+    LAUNCH(launch_gemm(EPI_RESID_BIAS_F32, ga, tab, M->stream));
     MARK(RMT_STAGE_OPROJ, 2.0 * rows * H * hd * d, rows * H * hd * 2 + G_ * d * H * hd * 2 + rows * d * 8);
     // H = LayerNorm 1 -> h2buf (fp32, the residual stream) and abuf (bf16, the W1 operand)
     const void* hb_lo[kMaxGroups];
@@ -364,7 +367,7 @@ int32_t run_cells(rmt_model* M, const Cell* cells, int G, const void* tokens, co
     set_io(nullptr, nullptr, packed_out, nullptr);
     ga.A = M->abuf; ga.B = M->wgu; ga.M = R; ga.N = F; ga.K = d;
     ga.split_in = R; ga.split_out = R; ga.ld_res = 0; ga.ld_out = F; ga.bias = M->b1;
-    LAUNCH(launch_gemm_bf16(EPI_BIAS_RELU_BF16, ga, tab, M->stream));
+    LAUNCH(launch_gemm(EPI_BIAS_RELU_BF16, ga, tab, M->stream));
     MARK(RMT_STAGE_GATEUP, 2.0 * rows * d * F, rows * d * 2 + G_ * F * d * 2 + rows * F * 2);
     // W2 + bias + residual H -> hbuf (before LayerNorm 2)
     const void* h2_lo[kMaxGroups];
@@ -376,7 +379,7 @@ int32_t run_cells(rmt_model* M, const Cell* cells, int G, const void* tokens, co
     set_io(h2_lo, h2_lo, hb_out, hb_out);
     ga.A = M->ubuf; ga.B = M->wd; ga.M = R; ga.N = d; ga.K = F;
     ga.split_in = R; ga.split_out = R; ga.ld_res = d; ga.ld_out = d; ga.bias = M->b2;
-    LAUNCH(launch_gemm_bf16(EPI_RESID_BIAS_F32, ga, tab, M->stream));
+    LAUNCH(launch_gemm(EPI_RESID_BIAS_F32, ga, tab, M->stream));
     MARK(RMT_STAGE_DOWN, 2.0 * rows * F * d, rows * F * 2 + G_ * d * F * 2 + rows * d * 8);
     // Y = LayerNorm 2; rows [0, n) -> X(l, s), rows [n, R) -> M(l, s)
     set_io(hb_lo, hb_lo, x_out, m_out);
@@ -395,7 +398,7 @@ int32_t run_cells(rmt_model* M, const Cell* cells, int G, const void* tokens, co
     ga.A = M->abuf; ga.B = M->wqkv; ga.M = R; ga.N = NQ; ga.K = d;
     ga.split_in = R; ga.split_out = R; ga.ld_res = 0; ga.ld_out = NQ; ga.bias = M->bqkv;
     ga.q_cols = H * hd; ga.q_scale = attention_scale_log2(hd);    // Q leaves with the softmax scale
-    LAUNCH(launch_gemm_bf16(EPI_BIAS_BF16, ga, tab, M->stream));
+    LAUNCH(launch_gemm(EPI_BIAS_BF16, ga, tab, M->stream));
     ga.q_cols = 0;
     MARK(RMT_STAGE_QKV, 2.0 * rows * d * NQ, rows * d * 2 + G_ * NQ * d * 2 + rows * NQ * 2);
     // unmasked multi-head attention inside each cell
@@ -406,7 +409,7 @@ int32_t run_cells(rmt_model* M, const Cell* cells, int G, const void* tokens, co
     set_io(in_lo, in_hi, packed_out, nullptr);
     ga.A = M->att; ga.B = M->wo; ga.M = R; ga.N = d; ga.K = H * hd;
     ga.split_in = m; ga.split_out = R; ga.ld_res = d; ga.ld_out = d; ga.bias = M->bo;
-    LAUNCH(launch_gemm_bf16(EPI_RESID_BIAS_F32, ga, tab, M->stream));
+    LAUNCH(launch_gemm(EPI_RESID_BIAS_F32, ga, tab, M->stream));
     MARK(RMT_STAGE_OPROJ, 2.0 * rows * H * hd * d, rows * H * hd * 2 + G_ * d * H * hd * 2 + rows * d * 8);
     // LayerNorm 2 of H
     for (int g = 0; g < G; ++g) packed_lo[g] = M->hbuf + (size_t)g * R * d;
@@ -418,13 +421,13 @@ int32_t run_cells(rmt_model* M, const Cell* cells, int G, const void* tokens, co
     set_io(nullptr, nullptr, packed_out, nullptr);
     ga.A = M->abuf; ga.B = M->wgu; ga.M = R; ga.N = F; ga.K = d;
     ga.split_in = R; ga.split_out = R; ga.ld_res = 0; ga.ld_out = F; ga.bias = M->b1;
-    LAUNCH(launch_gemm_bf16(EPI_BIAS_RELU_BF16, ga, tab, M->stream));
+    LAUNCH(launch_gemm(EPI_BIAS_RELU_BF16, ga, tab, M->stream));
     MARK(RMT_STAGE_GATEUP, 2.0 * rows * d * F, rows * d * 2 + G_ * F * d * 2 + rows * F * 2);
     // W2 + bias + residual H; rows [0, n) -> X(l, s), rows [n, R) -> M(l, s)
     set_io(packed_lo, packed_lo, x_out, m_out);
     ga.A = M->ubuf; ga.B = M->wd; ga.M = R; ga.N = d; ga.K = F;
     ga.split_in = R; ga.split_out = ns; ga.ld_res = d; ga.ld_out = d; ga.bias = M->b2;
-    LAUNCH(launch_gemm_bf16(EPI_RESID_BIAS_F32, ga, tab, M->stream));
+    LAUNCH(launch_gemm(EPI_RESID_BIAS_F32, ga, tab, M->stream));
     MARK(RMT_STAGE_DOWN, 2.0 * rows * F * d, rows * F * 2 + G_ * d * F * 2 + rows * d * 8);
     return RMT_OK;
   } else {
@@ -439,7 +442,7 @@ int32_t run_cells(rmt_model* M, const Cell* cells, int G, const void* tokens, co
   set_io(nullptr, nullptr, packed_out, nullptr);
   ga.A = M->abuf; ga.B = M->wgu; ga.M = R; ga.N = 2 * F; ga.K = d;
   ga.split_in = R; ga.split_out = R; ga.ld_res = 0; ga.ld_out = F;
-  LAUNCH(launch_gemm_bf16(EPI_SWIGLU, ga, tab, M->stream));
+  LAUNCH(launch_gemm(EPI_SWIGLU, ga, tab, M->stream));
   MARK(RMT_STAGE_GATEUP, 2.0 * rows * d * 2 * F, rows * d * 2 + G_ * 2 * F * d * 2 + rows * F * 2);
 
   // down projection + residual; rows [0, n) -> X(l, s), rows [n, R) -> M(l, s)
@@ -453,7 +456,7 @@ int32_t run_cells(rmt_model* M, const Cell* cells, int G, const void* tokens, co
   }
   ga.A = M->ubuf; ga.B = M->wd; ga.M = R; ga.N = d; ga.K = F;
   ga.split_out = ns; ga.ld_res = d; ga.ld_out = d;
-  LAUNCH(launch_gemm_bf16(EPI_RESID_F32, ga, tab, M->stream));
+  LAUNCH(launch_gemm(EPI_RESID_F32, ga, tab, M->stream));
   MARK(RMT_STAGE_DOWN, 2.0 * rows * F * d, rows * F * 2 + G_ * d * F * 2 + rows * d * 8);
   return RMT_OK;
 }
@@ -580,12 +583,13 @@ int32_t pack_weights(rmt_model* M) {
     HIP_TRY(hipMemcpyAsync(M->b2, w->b2, Ld4, hipMemcpyDeviceToDevice, st));
   } else {
     const int bf = w->weight_dtype == RMT_BF16;
-    HIP_TRY(launch_pack(L, d, (int)F, w->wg, w->wu, bf, 1, M->wgu, st));
-    HIP_TRY(launch_pack(L, (int)F, d, w->wd, nullptr, bf, 0, M->wd, st));
+    const int f16 = c.dtype == RMT_F16;   // operands packed as fp16
+    HIP_TRY(launch_pack(L, d, (int)F, w->wg, w->wu, bf, 1, M->wgu, st, f16));
+    HIP_TRY(launch_pack(L, (int)F, d, w->wd, nullptr, bf, 0, M->wd, st, f16));
     HIP_TRY(hipMemcpyAsync(M->g2, w->g2, (size_t)L * d * 4, hipMemcpyDeviceToDevice, st));
     if (c.cell == RMT_CELL_LLAMA) {
-      HIP_TRY(launch_pack(L, d, (int)NQ, w->wqkv, nullptr, bf, 0, M->wqkv, st));
-      HIP_TRY(launch_pack(L, (int)HQD, d, w->wo, nullptr, bf, 0, M->wo, st));
+      HIP_TRY(launch_pack(L, d, (int)NQ, w->wqkv, nullptr, bf, 0, M->wqkv, st, f16));
+      HIP_TRY(launch_pack(L, (int)HQD, d, w->wo, nullptr, bf, 0, M->wo, st, f16));
       HIP_TRY(hipMemcpyAsync(M->g1, w->g1, (size_t)L * d * 4, hipMemcpyDeviceToDevice, st));
       // RoPE table: angle p * theta^(-2i/hd) in double precision.
       const int half = c.head_dim / 2;
@@ -998,7 +1002,8 @@ int32_t rmt_grouped_gemm(int32_t G, int32_t Mr, int32_t N, int32_t K, int32_t Lw
   if (Lw < 1) return fail(RMT_EINVAL, "Lw must be >= 1 (got %d)", Lw);
   if ((int64_t)G * Mr * std::max(N, K) > INT32_MAX) return fail(RMT_EINVAL, "sizes overflow int32");
   if (!A || !B || !C || !group_layer) return fail(RMT_EINVAL, "A, B, C and group_layer must be non-NULL");
-  if (dtype != RMT_BF16) return fail(RMT_EUNSUPPORTED, "dtype must be RMT_BF16 (got %d)", dtype);
+  if (dtype != RMT_BF16 && dtype != RMT_F16)
+    return fail(RMT_EUNSUPPORTED, "dtype must be RMT_BF16 or RMT_F16 (got %d)", dtype);
   for (int g = 0; g < G; ++g)
     if (group_layer[g] < 0 || group_layer[g] >= Lw)
       return fail(RMT_EINVAL, "group_layer[%d] = %d is outside [0, %d)", g, group_layer[g], Lw);
@@ -1012,8 +1017,8 @@ int32_t rmt_grouped_gemm(int32_t G, int32_t Mr, int32_t N, int32_t K, int32_t Lw
   GemmArgs ga;
   std::memset(&ga, 0, sizeof(ga));
   ga.A = (const uint16_t*)A; ga.B = (const uint16_t*)B; ga.M = Mr; ga.N = N; ga.K = K;
-  ga.split_in = Mr; ga.split_out = Mr; ga.ld_out = N;
-  HIP_TRY(launch_gemm_bf16(EPI_STORE_BF16, ga, tab, (hipStream_t)stream));
+  ga.split_in = Mr; ga.split_out = Mr; ga.ld_out = N; ga.f16 = dtype == RMT_F16;
+  HIP_TRY(launch_gemm(EPI_STORE_BF16, ga, tab, (hipStream_t)stream));
   return RMT_OK;
 }
 

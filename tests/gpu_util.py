@@ -40,7 +40,9 @@ def inputs(cfg, S=None, seed=0):
 class GpuRun:
     """A model built from seeded weights, with device inputs for S segments."""
 
-    def __init__(self, cfg, S=None, seed=0, layers=None, embed=None, x=None, mem0=None):
+    def __init__(self, cfg, S=None, seed=0, layers=None, embed=None, x=None, mem0=None, dtype=None):
+        """dtype: the model's 16-bit type (RMT_BF16 or RMT_F16) when it is not
+        the workload's own."""
         import torch
         import long_context_anti_amd as rmt
         self.cfg = cfg
@@ -49,7 +51,10 @@ class GpuRun:
             layers, x, mem0, embed = inputs(cfg, self.S, seed)
         self.layers, self.x, self.mem0, self.embed = layers, x, mem0, embed
         dw = rdev.device_weights(cfg, layers, embed)
-        self.model = rmt.RMTModel(**rdev.model_kwargs(cfg, self.S), weights=dw)
+        kw = rdev.model_kwargs(cfg, self.S)
+        if dtype is not None:
+            kw["dtype"] = dtype
+        self.model = rmt.RMTModel(**kw, weights=dw)
         self.embed_dev = dw.get("embed")
         del dw
         self.tokens = rdev.segment_inputs(cfg, x)

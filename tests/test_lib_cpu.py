@@ -99,6 +99,24 @@ def test_model_create_rejects_bad_configs(kw, code):
     assert not handle.value
 
 
+def test_fp16_operands_are_a_llama_cell_option():
+    """RMT_F16 (fp16 operands) is accepted for LLAMA cells and refused for the
+    others; create makes no device call, so this runs on the CPU."""
+    L = _lib()
+    w = L.RmtWeights()
+    for name, _ in L.RmtWeights._fields_[1:]:
+        setattr(w, name, 1 << 20)
+    h = C.c_void_p()
+    cfg = _cfg(dtype=L.RMT_F16)
+    assert L.lib().rmt_model_create(C.byref(cfg), C.byref(w), None, C.byref(h)) == L.RMT_OK
+    assert L.lib().rmt_model_destroy(h) == L.RMT_OK
+    for cell, extra in ((L.RMT_CELL_NORM_SWIGLU, {}), (L.RMT_CELL_ENCODER, dict(n_kv_heads=4, ffn=1024))):
+        cfg = _cfg(cell=cell, dtype=L.RMT_F16, **extra)
+        h = C.c_void_p()
+        assert L.lib().rmt_model_create(C.byref(cfg), C.byref(w), None, C.byref(h)) == L.RMT_EUNSUPPORTED
+        assert b"fp16" in L.lib().rmt_last_error()
+
+
 def test_model_create_rejects_missing_weights():
     L = _lib()
     cfg = _cfg()
