@@ -13,7 +13,7 @@ bf16 dense MFMA peak, the isolated 1152 x 2048 x 8192 grouped GEMM at
 G = 1, 4, 8, 16, and the CPU oracle timed on a prefix of the sequence.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu] [--no-seq]
-                    [--workload llama1b|llama8b|norm_swiglu_1b|encoder1b]
+                    [--workload llama1b|llama8b|norm_swiglu_1b|encoder1b] [--dtype bf16|f16]
 
 The default workload is the 1B-shaped one above; --workload selects the
 8B-shaped RMT (32 layers, d = 4096, segments of 2048 + 128 rows, 64 segments,
@@ -48,10 +48,10 @@ ENCODER_STAGE_NAMES = {"norm1": "layernorm1", "norm2": "layernorm2", "gateup": "
 # post-norm: the first norm-stage launch is the bf16 copy of A, the second stage holds both LayerNorms
 POSTNORM_STAGE_NAMES = {"norm1": "cast_a_bf16", "norm2": "layernorms", "gateup": "ffn_w1", "down": "ffn_w2"}
 GEMM_KERNELS = {
-    "llama": {"qkv": "QKV stage + RoPE epilogue (gemm_bf16_kernel<1>)",
-              "oproj": "O stage + residual epilogue (gemm_bf16_kernel<3>)",
-              "gateup": "gate/up stage + SwiGLU epilogue (gemm_bf16_kernel<2>)",
-              "down": "down stage + residual epilogue (gemm_bf16_kernel<3>)"},
+    "llama": {"qkv": "QKV stage + RoPE epilogue (gemm_bf16_kernel<1, ...>)",
+              "oproj": "O stage + residual epilogue (gemm_bf16_kernel<3, ...>)",
+              "gateup": "gate/up stage + SwiGLU epilogue (gemm_bf16_kernel<2, ...>)",
+              "down": "down stage + residual epilogue (gemm_bf16_kernel<3, ...>)"},
     "encoder": {"qkv": "QKV stage + bias epilogue (gemm_bf16_kernel<4>)",
                 "oproj": "O stage + bias + residual epilogue (gemm_bf16_kernel<6>)",
                 "gateup": "W1 stage + bias + ReLU epilogue (gemm_bf16_kernel<5>)",
@@ -162,11 +162,13 @@ def cpu_baseline(cfg, layers, tokens, mem0, embed, gpu_hidden, gpu_mem_prefix_fn
     from oracle import rmt_oracle as orc
     threads = max([i.get("num_threads", 1) for i in threadpool_info()
                    if i.get("user_api") == "blas"] or [1])
+    host_cores = len(os.sched_getaffinity(0))
     t0 = time.perf_counter()
     h, m = orc.forward_sequential(cfg, layers, tokens[:S_prefix * cfg.n], mem0, embed)
     dt = time.perf_counter() - t0
     toks = S_prefix * cfg.n
-    res = {"value": round(toks / dt, 2), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+    res = {"value": round(toks / dt, 2), "unit": "tokens/s", "cores": int(threads),
+           "host_cores": host_cores, "blas_threads": int(threads), "kind": "oracle",
            "sample": f"first {S_prefix} of {cfg.S} segments through all {cfg.L} layers "
                      f"({toks} tokens, NumPy fp32, {dt:.1f} s); per-segment cost is constant in s",
            "seconds": round(dt, 2)}
@@ -192,6 +194,9 @@ def main():
     ap.add_argument("--batch", type=int, default=1,
                     help="B sequences through the same diagonals (rmt_model_set_batch); "
                          "tokens/s then counts all B sequences")
+    ap.add_argument("--dtype", default=None, choices=["bf16", "f16"],
+                    help="16-bit operand type of the LLaMA-shaped cell (default: the workload's bf16); "
+                         "f16 is the precision that meets the 2e-2 gate at the 8B shape")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy, the reference for HBM byte counters")
     args = ap.parse_args()
@@ -219,7 +224,14 @@ def main():
     tokens, mem0 = toks_b[0], mems_b[0]
     log(f"[bench] {cfg.name}: inputs generated in {time.perf_counter() - t0:.1f} s")
     dw = rdev.device_weights(cfg, layers, embed)
-    model = rmt.RMTModel(**rdev.model_kwargs(cfg), weights=dw)
+    kw = rdev.model_kwargs(cfg)
+    f16 = args.dtype == "f16"
+    if f16:
+        if not llama:
+            print("--dtype f16 applies to the LLaMA-shaped workloads only", file=sys.stderr)
+            sys.exit(2)
+        kw["dtype"] = rmt.RMT_F16
+    model = rmt.RMTModel(**kw, weights=dw)
     emb_dev = dw.get("embed")
     del dw
     if B == 1:
@@ -305,7 +317,8 @@ def main():
             "linear_gelu" if cfg.cell == ri.CELL_LINEAR_GELU else "norm_swiglu")
     dom = max((s for s in GEMM_KERNELS[kind] if stages[s]["launches"]), key=lambda s: stages[s]["ms"])
     # the committed counter summary covers the 1B-shaped workload's gate/up kernel only
-    traffic = measured_traffic() if args.workload == "llama1b" and dom == "gateup" else None
+    traffic = (measured_traffic() if args.workload == "llama1b" and dom == "gateup" and not f16 and B == 1
+               else None)
     gu = stages[dom]
     achieved = gu["flops"] / gu["launches"] / (gu["ms"] / 1e3 / gu["launches"]) / 1e12
     alu = kind == "linear_gelu"      # fp32 arithmetic on the vector ALUs, no matrix cores
@@ -313,6 +326,10 @@ def main():
     roofline = {"kernel": ("" if alu else "grouped GEMM, ") + GEMM_KERNELS[kind][dom],
                 "bound": "alu" if alu else "mfma", "achieved": round(achieved, 3), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(achieved / peak, 5), "traffic": traffic,
+                "traffic_source": ("HBM-side bytes per launch from the committed rocprofv3 FETCH_SIZE / "
+                                   "WRITE_SIZE summary profiles/llama1b_rmt_L16_S128_gateup_hbm_traffic.md, "
+                                   "valid for the GEMM source hash recorded there (not measured in this run)")
+                if traffic else None,
                 "avg_launch_us": round(gu["ms"] / gu["launches"] * 1e3, 2),
                 "flops_per_launch": gu["flops"] / gu["launches"]}
 
@@ -334,7 +351,7 @@ def main():
         config["vocab"] = cfg.V
     data = ("synthetic (seeded random weights, token ids uniform over the vocabulary)" if llama
             else "synthetic (seeded random weights and input embeddings)")
-    dtype = "f32" if cfg.dtype != ri.BF16 else "bf16"
+    dtype = "f32" if cfg.dtype != ri.BF16 else ("f16" if f16 else "bf16")
     result = {
         "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 2),
