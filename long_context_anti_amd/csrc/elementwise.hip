@@ -138,12 +138,42 @@ __global__ __launch_bounds__(256) void norm_kernel(int total_rows, int R, int d,
          LAYER ? *(const f32x4*)(bt + c) : zero);
 }
 
+// RMSNorm side outputs of four consecutive columns c..c+3 of a row, held by
+// one thread of a block that covers the row 1024 columns at a time (thread t
+// holds columns 4 t + 1024 j): the 16-bit copy y * gamma, and, from the 16
+// threads that share a 64-column chunk, the chunk's sum of squares (a fixed
+// butterfly, so every one of the 16 gets the same bits; the chunk's first
+// thread stores it).  The 16 threads of a chunk are consecutive lanes of one
+// wave, and every lane reaches the exchange (d is a multiple of 64).
+// dss points at the row's sum of chunk 0; chunk j's sum is at dss[j * ss_ld].
+template <bool F16>
+__device__ __forceinline__ void row_side_outputs(const f32x4& y, int c, const float* __restrict__ gamma,
+                                                 uint16_t* __restrict__ dst16, float* __restrict__ dss,
+                                                 int ss_ld) {
+  float ss = (y[0] * y[0] + y[1] * y[1]) + (y[2] * y[2] + y[3] * y[3]);
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) ss += __shfl_xor(ss, o);
+  if (c % kChunk == 0) dss[(size_t)(c / kChunk) * ss_ld] = ss;
+  const f32x4 g = *(const f32x4*)(gamma + c);
+  u16x4 o;
+  o[0] = to_16<F16>(y[0] * g[0]);
+  o[1] = to_16<F16>(y[1] * g[1]);
+  o[2] = to_16<F16>(y[2] * g[2]);
+  o[3] = to_16<F16>(y[3] * g[3]);
+  *(u16x4*)(dst16 + c) = o;
+}
+
 // Embedding lookup of one segment's n token ids into an fp32 slot.  An id
-// outside [0, V) reads as a zero row and raises *bad_flag.
+// outside [0, V) reads as a zero row and raises *bad_flag.  With AUX the
+// rows' RMSNorm side outputs go to dst16 / dss as well (gain row `gamma`).
+template <bool AUX, bool F16>
 __global__ __launch_bounds__(256) void gather_tokens_kernel(int d, const int32_t* __restrict__ ids,
                                                             int V, const uint16_t* __restrict__ embed,
                                                             float* __restrict__ dst,
-                                                            int32_t* __restrict__ bad_flag) {
+                                                            int32_t* __restrict__ bad_flag,
+                                                            const float* __restrict__ gamma,
+                                                            uint16_t* __restrict__ dst16,
+                                                            float* __restrict__ dss, int ss_ld) {
   const int i = (int)blockIdx.x;
   const int id = ids[i];
   const bool ok = id >= 0 && id < V;
@@ -160,7 +190,55 @@ __global__ __launch_bounds__(256) void gather_tokens_kernel(int d, const int32_t
       v[3] = bf16_to_f32(h[3]);
     }
     *(f32x4*)(o + c) = v;
+    if constexpr (AUX)
+      row_side_outputs<F16>(v, c, gamma, dst16 + (size_t)i * d, dss + i, ss_ld);
   }
+}
+
+// RMSNorm side outputs of fp32 rows that no GEMM epilogue wrote (the initial
+// memory M(l, -1)): one block per row; row r uses gain row
+// layer0 + (r / rows_per_layer) % L.
+template <bool F16>
+__global__ __launch_bounds__(256) void norm_aux_rows_kernel(int d, const float* __restrict__ src,
+                                                            int rows_per_layer, int L, int layer0,
+                                                            const float* __restrict__ gamma,
+                                                            uint16_t* __restrict__ dst16,
+                                                            float* __restrict__ dss) {
+  const int r = (int)blockIdx.x;
+  const int q = r / rows_per_layer, i = r - q * rows_per_layer;
+  const float* gm = gamma + (size_t)(layer0 + q % L) * d;
+  float* ss = dss + (size_t)q * rows_per_layer * (d / kChunk) + i;
+  for (int c = (int)threadIdx.x * 4; c < d; c += 1024)
+    row_side_outputs<F16>(*(const f32x4*)(src + (size_t)r * d + c), c, gm, dst16 + (size_t)r * d, ss,
+                          rows_per_layer);
+}
+
+// 1 / sqrt(mean of squares + eps) of every row of every group from its chunk
+// sums, added in chunk order (the same formula as norm_kernel's).  Block
+// (x, g) covers rows x * 256 .. of group g, so the group's pointers are
+// wave-uniform; the chunk sums of a row are fetched 16 at a time (independent
+// loads in flight together) and then added in order.
+__global__ __launch_bounds__(256) void row_rinv_kernel(int R, int d, int split, NormAux aux, float eps,
+                                                       float* __restrict__ rinv) {
+  const int g = (int)blockIdx.y;
+  const int r = (int)blockIdx.x * 256 + (int)threadIdx.x;
+  if (r >= R) return;
+  const int nc = d / kChunk;
+  const bool lo = r < split;
+  const float* ss = lo ? aux.ss_lo[g] + r : aux.ss_hi[g] + (r - split);
+  const size_t ld = lo ? (size_t)aux.ss_ld_lo : (size_t)aux.ss_ld_hi;
+  constexpr int BATCH = 16;
+  float t = 0.f;
+  int j = 0;
+  for (; j + BATCH <= nc; j += BATCH) {
+    float v[BATCH];
+#pragma unroll
+    for (int u = 0; u < BATCH; ++u) v[u] = ss[(size_t)(j + u) * ld];
+#pragma unroll
+    for (int u = 0; u < BATCH; ++u) t += v[u];
+  }
+  for (; j < nc; ++j) t += ss[(size_t)j * ld];
+  rinv[(size_t)g * R + r] = 1.0f / sqrtf(t / (float)d + eps);
 }
 
 // bf16 input rows -> fp32 slot (the attention-free cell's segment inputs).
@@ -292,10 +370,39 @@ hipError_t launch_cast_rows(int G, int R, int d, int split_in, const GroupTable&
 }
 
 hipError_t launch_gather_tokens(int n, int d, const int32_t* ids, int V, const uint16_t* embed,
-                                float* dst, int32_t* bad_flag, hipStream_t stream) {
+                                float* dst, int32_t* bad_flag, hipStream_t stream, const float* gamma,
+                                uint16_t* dst16, float* dss, int ss_ld, bool f16) {
   if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(gather_tokens_kernel, dim3(n), dim3(256), 0, stream, d, ids, V, embed, dst,
-                     bad_flag);
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, dim3(n), dim3(256), 0, stream, d, ids, V, embed, dst, bad_flag, gamma, dst16, dss,
+                       ss_ld);
+  };
+  if (!dst16) go(gather_tokens_kernel<false, false>);
+  else if (d % kChunk != 0 || !gamma || !dss || ss_ld < n) return hipErrorInvalidValue;
+  else if (f16) go(gather_tokens_kernel<true, true>);
+  else go(gather_tokens_kernel<true, false>);
+  return hipGetLastError();
+}
+
+hipError_t launch_norm_aux_rows(int rows, int d, const float* src, int rows_per_layer, int L, int layer0,
+                                const float* gamma, uint16_t* dst16, float* dss, bool f16,
+                                hipStream_t stream) {
+  if (rows == 0) return hipSuccess;
+  if (d % kChunk != 0 || rows_per_layer < 1 || L < 1) return hipErrorInvalidValue;
+  if (f16)
+    hipLaunchKernelGGL(norm_aux_rows_kernel<true>, dim3(rows), dim3(256), 0, stream, d, src, rows_per_layer, L,
+                       layer0, gamma, dst16, dss);
+  else
+    hipLaunchKernelGGL(norm_aux_rows_kernel<false>, dim3(rows), dim3(256), 0, stream, d, src, rows_per_layer, L,
+                       layer0, gamma, dst16, dss);
+  return hipGetLastError();
+}
+
+hipError_t launch_row_rinv(int G, int R, int d, int split, const NormAux& aux, float eps, float* rinv,
+                           hipStream_t stream) {
+  if (G == 0 || R == 0) return hipSuccess;
+  if (d % kChunk != 0 || G > kMaxGroups) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(row_rinv_kernel, dim3((R + 255) / 256, G), dim3(256), 0, stream, R, d, split, aux, eps, rinv);
   return hipGetLastError();
 }
 

@@ -99,6 +99,23 @@ __device__ __forceinline__ void wait_vmem() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (0 << 8) | ((N >> 4) << 14));
 }
 
+// Global-memory pointers (address space 1), so that stores through them stay
+// global stores rather than flat ones (flat stores also count against the
+// LDS wait counter).
+typedef __attribute__((address_space(1))) uint16_t gu16;
+typedef __attribute__((address_space(1))) float gf32;
+typedef __attribute__((address_space(1))) u32x2 gu32x2;
+typedef __attribute__((address_space(1))) f32x4 gf32x4;
+
+// A pointer that is the same in every lane, moved to scalar registers.
+template <typename T>
+__device__ __forceinline__ T* uniform_ptr(const void* p) {
+  const uint64_t v = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (T*)(((uint64_t)hi << 32) | lo);
+}
+
 // Workgroups are handed to the 8 XCDs round-robin (id mod 8).  Renumber them
 // so that each XCD receives one contiguous run of tiles: tiles that share a
 // weight panel then share that XCD's L2.
@@ -114,7 +131,7 @@ __device__ __forceinline__ int xcd_remap(int bid, int nb) {
 // F16: operands and 16-bit results in fp16 instead of bf16.
 template <int EPI, int BM, int WTM, int WTN, bool BNT, bool F16>
 __global__ __launch_bounds__((BM / WTM) * (BN / WTN) * 64, 1) void gemm_bf16_kernel(
-    GemmArgs a, GroupTable tab) {
+    GemmArgs a, GroupTable tab, NormAux aux) {
   using H = Half16<F16>;
   typedef typename H::x8 op8;
   constexpr int STAGE_BYTES = (BM + BN) * ROWB;
@@ -134,7 +151,15 @@ __global__ __launch_bounds__((BM / WTM) * (BN / WTN) * 64, 1) void gemm_bf16_ker
   static_assert(A_LOADS * RPI == BM && ALL_LOADS * RPI == BM + BN, "load split");
   // vmcnt-based waits for slices still in flight need the same count per wave
   static_assert(STAGES == 2 || ALL_LOADS % NWAVES == 0, "uneven load split needs a two-slice ring");
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * STAGE_BYTES];
+  constexpr bool SIDE = EPI == EPI_RESID_NORM_F32;   // RMSNorm side outputs
+  // One LDS array for everything.  A second __shared__ object makes the
+  // compiler tag LDS accesses with alias scopes, and it then drains every
+  // in-flight direct-to-LDS load before the first LDS read of each K slice,
+  // which serialises the ring; the waits below already order the slices.
+  constexpr int GSM_OFF = STAGES * STAGE_BYTES;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[GSM_OFF + (SIDE ? 2 * BN * 4 : 0)];
+  // side outputs: the tile's gains for its lo rows ([0, BN)) and hi rows
+  float* const gsm = (float*)(smem + GSM_OFF);
 
   const int tiles_m = (a.M + BM - 1) / BM;
   const int tiles_n = (a.N + BN - 1) / BN;
@@ -155,11 +180,29 @@ __global__ __launch_bounds__((BM / WTM) * (BN / WTN) * 64, 1) void gemm_bf16_ker
   const int n_valid = min(BN, a.N - tn * BN);
   // Buffer resources clipped to the tile's valid rows: the hardware returns
   // zeros for anything outside, so ragged M / N / K edges need no branches.
-  const uint16_t* Ag = a.A + ((size_t)g * a.M + (size_t)tm * BM) * K;
   const uint16_t* Bg = a.B + ((size_t)tab.layer[g] * a.N + (size_t)tn * BN) * K;
   const int a_bytes = m_valid * K * 2;
   const int b_bytes = n_valid * K * 2;
-  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc((void*)Ag, (short)0, a_bytes, BUF_FLAGS);
+  // A split (QKV of the LLaMA cell): the tile's rows below a_split come from
+  // in_lo[g] (the cell's memory rows), the others from in_hi[g] (its segment
+  // rows).  ra covers the lo rows of the tile, ra_hi all of its rows as they
+  // sit in in_hi (the rows below a_split are never read through it, so its
+  // base may point before in_hi).  Each wave-wide load spans 8 rows and
+  // a_split is a multiple of 8, so a load lies wholly in one part.
+  constexpr bool SPLIT_A = EPI == EPI_QKV_ROPE;
+  const bool split_a = SPLIT_A && a.a_split > 0;
+  __amdgpu_buffer_rsrc_t ra, ra_hi;
+  if (split_a) {
+    const int lo_rows = max(0, min(m_valid, a.a_split - tm * BM));
+    const uint16_t* lo = (const uint16_t*)tab.in_lo[g] + (size_t)tm * BM * K;
+    const uintptr_t hi = (uintptr_t)tab.in_hi[g] + (intptr_t)(tm * BM - a.a_split) * K * 2;
+    ra = __builtin_amdgcn_make_buffer_rsrc((void*)lo, (short)0, lo_rows * K * 2, BUF_FLAGS);
+    ra_hi = __builtin_amdgcn_make_buffer_rsrc((void*)hi, (short)0, a_bytes, BUF_FLAGS);
+  } else {
+    const uint16_t* Ag = a.A + ((size_t)g * a.M + (size_t)tm * BM) * K;
+    ra = __builtin_amdgcn_make_buffer_rsrc((void*)Ag, (short)0, a_bytes, BUF_FLAGS);
+    ra_hi = ra;
+  }
   const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc((void*)Bg, (short)0, b_bytes, BUF_FLAGS);
 
   // Global -> LDS without registers: each wave-wide load moves 1 KiB, lane L
@@ -199,11 +242,13 @@ __global__ __launch_bounds__((BM / WTM) * (BN / WTN) * 64, 1) void gemm_bf16_ker
         const int row = (is_a ? q : q - A_LOADS) * RPI + lrow;
         if (k0 + 8 * (lp ^ swz(row)) >= K) off = is_a ? a_bytes : b_bytes;
       }
+      // rows of load q start at tm * BM + q * RPI (wave-uniform)
+      const __amdgpu_buffer_rsrc_t rsa = SPLIT_A && tm * BM + q * RPI >= a.a_split ? ra_hi : ra;
       if constexpr (BNT) {
-        if (is_a) __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(sbase + q * 1024), 16, off, 0, 0, 0);
+        if (is_a) __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_ptr_t)(sbase + q * 1024), 16, off, 0, 0, 0);
         else __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(sbase + q * 1024), 16, off, 0, 0, 2);
       } else {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(is_a ? ra : rb, (lds_ptr_t)(sbase + q * 1024), 16, off, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(is_a ? rsa : rb, (lds_ptr_t)(sbase + q * 1024), 16, off, 0, 0, 0);
       }
     }
   };
@@ -261,6 +306,29 @@ __global__ __launch_bounds__((BM / WTM) * (BN / WTN) * 64, 1) void gemm_bf16_ker
     }
   };
 
+  // Row scales (an RMSNorm's 1/rms per output row) are requested now and
+  // applied to the accumulators after the main loop.
+  constexpr bool ROWSCALE = EPI == EPI_QKV_ROPE || EPI == EPI_SWIGLU;
+  float rsc[ROWSCALE ? MI : 1];
+  if constexpr (ROWSCALE) {
+    if (a.row_scale) {
+#pragma unroll
+      for (int i = 0; i < MI; ++i) {
+        const int row = tm * BM + wm * WTM + i * 32 + r32;
+        rsc[i] = row < a.M ? a.row_scale[(size_t)g * a.M + row] : 0.f;
+      }
+    }
+  }
+  // Side-output gains of the tile's columns, for its lo and hi rows, into LDS
+  // beside the ring (the main loop's first barrier publishes them).
+  if constexpr (SIDE) {
+    for (int j = tid; j < 2 * BN; j += NWAVES * 64) {
+      const int part = j / BN, c = j % BN, col = tn * BN + c;
+      const int lay = part ? aux.layer_hi[g] : aux.layer_lo[g];
+      gsm[part * BN + c] = col < a.N ? a.aux_gamma[(size_t)lay * a.N + col] : 0.f;
+    }
+  }
+
   // Ring of STAGES LDS slices: slice kt+STAGES-1 is requested while the
   // MFMAs consume slice kt.  One barrier per slice; it also certifies that
   // every wave has finished reading the stage about to be refilled.
@@ -293,7 +361,16 @@ __global__ __launch_bounds__((BM / WTM) * (BN / WTN) * 64, 1) void gemm_bf16_ker
   // accumulators and stage bf16 results; RoPE stages the two fp32 blocks of
   // a rotation pair and rotates after the read-back.  The fp32 residual
   // epilogues work straight from the accumulator layout.
-  if constexpr (EPI != EPI_RESID_F32 && EPI != EPI_RESID_BIAS_F32) {
+  if constexpr (ROWSCALE) {
+    if (a.row_scale) {
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int t = 0; t < NI; ++t) acc[i][t] *= rsc[i];
+    }
+  }
+  constexpr bool RESID = EPI == EPI_RESID_F32 || EPI == EPI_RESID_BIAS_F32 || SIDE;
+  if constexpr (!RESID || SIDE) {   // SIDE stages its 16-bit copies through the ring
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();      // the ring is free once every wave is past its last slice
     asm volatile("" ::: "memory");
@@ -319,65 +396,145 @@ __global__ __launch_bounds__((BM / WTM) * (BN / WTN) * 64, 1) void gemm_bf16_ker
           f32x4{blk[4 * e4], blk[4 * e4 + 1], blk[4 * e4 + 2], blk[4 * e4 + 3]};
   };
 
-  if constexpr (EPI == EPI_RESID_F32 || EPI == EPI_RESID_BIAS_F32) {
-    if constexpr (EPI == EPI_RESID_BIAS_F32) {
-      // The bias first (acc + b, then + residual): it depends on the column
-      // only, so one load per column group serves every row block.
-      // One 32-column block at a time (the empty asm keeps the compiler from
-      // hoisting every block's loads at once, which would spill).
-      const float* bl = a.bias + (size_t)tab.layer[g] * a.N;
-#pragma unroll
-      for (int t = 0; t < NI; ++t) {
-        f32x4 bv[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int col = wcol0 + t * 32 + 8 * q + half_lane;
-          bv[q] = col < a.N ? *(const f32x4*)(bl + col) : f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-          for (int i = 0; i < MI; ++i)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) acc[i][t][4 * q + e] += bv[q][e];
-        asm volatile("" ::: "memory");
-      }
+  if constexpr (RESID) {
+    // The group's side-output pointers, read once as wave-uniform values (a
+    // per-lane choice between the table's entries would otherwise become a
+    // per-lane load from the argument block inside every row block).
+    gu16* aux_rows_lo = nullptr;
+    gu16* aux_rows_hi = nullptr;
+    gf32* aux_ss_lo = nullptr;
+    gf32* aux_ss_hi = nullptr;
+    if constexpr (SIDE) {
+      aux_rows_lo = uniform_ptr<gu16>(aux.rows_lo[g]);
+      aux_rows_hi = uniform_ptr<gu16>(aux.rows_hi[g]);
+      aux_ss_lo = uniform_ptr<gf32>(aux.ss_lo[g]);
+      aux_ss_hi = uniform_ptr<gf32>(aux.ss_hi[g]);
     }
     // Straight from the accumulator layout.  All residual loads of a 32-row
     // block are issued before any of its stores: the compiler cannot prove
     // that `out` does not alias `res`, and would otherwise wait out one full
-    // memory round trip per load.
+    // memory round trip per load.  The group's row pointers are read once as
+    // wave-uniform values and chosen per lane by value (choosing between
+    // table entries per lane would load the pointer per lane, in every row
+    // block, before the residual loads could start).
+    const gf32* res_lo = uniform_ptr<const gf32>(tab.in_lo[g]);
+    const gf32* res_hi = uniform_ptr<const gf32>(tab.in_hi[g]);
+    gf32* out_lo = uniform_ptr<gf32>(tab.out_lo[g]);
+    gf32* out_hi = uniform_ptr<gf32>(tab.out_hi[g]);
+    constexpr bool BIAS_R = EPI == EPI_RESID_BIAS_F32;
+    const gf32* bias_l = BIAS_R ? (const gf32*)(a.bias + (size_t)tab.layer[g] * a.N) : nullptr;
+    // The code below is straight-line per 32-row block: column validity is
+    // decided per 32-column block (N is a multiple of 32 on these paths,
+    // checked at launch), which is the same for the whole wave, and every
+    // side output has a destination.  Per-lane branches here would leave the
+    // compiler's wait counting no choice but to drain every store before each
+    // of the next stores' residuals is used.
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
-      const int row = wrow0 + i * 32 + r32;
-      if (row >= a.M) continue;
-      const float* res = row < a.split_in
-                             ? (const float*)tab.in_lo[g] + (size_t)row * a.ld_res
-                             : (const float*)tab.in_hi[g] + (size_t)(row - a.split_in) * a.ld_res;
-      float* out = row < a.split_out
-                       ? (float*)tab.out_lo[g] + (size_t)row * a.ld_out
-                       : (float*)tab.out_hi[g] + (size_t)(row - a.split_out) * a.ld_out;
+      // Every lane stays active (the staged read-back below hands rows to
+      // other lanes): rows past M load from the last valid row and store
+      // nothing.
+      const int row_t = wrow0 + i * 32 + r32;
+      const bool row_ok = row_t < a.M;
+      const int row = row_ok ? row_t : a.M - 1;
+      const gf32* res = row < a.split_in ? res_lo + (size_t)row * a.ld_res
+                                         : res_hi + (size_t)(row - a.split_in) * a.ld_res;
+      gf32* out = row < a.split_out ? out_lo + (size_t)row * a.ld_out
+                                    : out_hi + (size_t)(row - a.split_out) * a.ld_out;
       f32x4 rv[NI][4];
 #pragma unroll
       for (int t = 0; t < NI; ++t)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int col = wcol0 + t * 32 + 8 * q + half_lane;
-          rv[t][q] = col < a.N ? *(const f32x4*)(res + col) : f32x4{0.f, 0.f, 0.f, 0.f};
+          rv[t][q] = wcol0 + t * 32 < a.N ? *(const gf32x4*)(res + col) : f32x4{0.f, 0.f, 0.f, 0.f};
         }
+      // The bias (EPI_RESID_BIAS_F32) is loaded again for every row block, a
+      // cache hit after the first: kept live across the row blocks, its
+      // vectors would be spilled.
+      f32x4 bv[BIAS_R ? NI : 1][4];
+      if constexpr (BIAS_R) {
+#pragma unroll
+        for (int t = 0; t < NI; ++t)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int col = wcol0 + t * 32 + 8 * q + half_lane;
+            bv[t][q] = wcol0 + t * 32 < a.N ? *(const gf32x4*)(bias_l + col) : f32x4{0.f, 0.f, 0.f, 0.f};
+          }
+      }
+      // y = residual + acc (+ bias: residual + (acc + bias)) in rv, then the
+      // fp32 stores of the row block
 #pragma unroll
       for (int t = 0; t < NI; ++t)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int col = wcol0 + t * 32 + 8 * q + half_lane;
-          if (col >= a.N) continue;
-          f32x4 r = rv[t][q];
-          r[0] += acc[i][t][4 * q + 0];
-          r[1] += acc[i][t][4 * q + 1];
-          r[2] += acc[i][t][4 * q + 2];
-          r[3] += acc[i][t][4 * q + 3];
-          *(f32x4*)(out + col) = r;
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if constexpr (BIAS_R) rv[t][q][e] += acc[i][t][4 * q + e] + bv[t][q][e];
+            else rv[t][q][e] += acc[i][t][4 * q + e];
+          }
+      if (row_ok) {
+#pragma unroll
+        for (int t = 0; t < NI; ++t) {
+          if (wcol0 + t * 32 >= a.N) break;      // wave-uniform
+#pragma unroll
+          for (int q = 0; q < 4; ++q) *(gf32x4*)(out + wcol0 + t * 32 + 8 * q + half_lane) = rv[t][q];
         }
+      }
+      if constexpr (SIDE) {
+        // Side outputs (EPI_RESID_NORM_F32).  The 64-column chunk sums: both
+        // half-lanes of a row add their 32 squares, in the same order, and
+        // store the same value to the same place.  The 16-bit copies y * g go
+        // through the wave's LDS region (32 rows of WTN values, 16-byte chunks
+        // XOR-swizzled by row) and leave as row segments, 8 rows of WTN * 2
+        // bytes per store, like the bf16 epilogues' results.
+        const bool lo_part = row < a.split_out;
+        const int rr_own = lo_part ? row : row - a.split_out;
+        gf32* xss = (lo_part ? aux_ss_lo : aux_ss_hi) + rr_own;
+        const int ss_ld = lo_part ? aux.ss_ld_lo : aux.ss_ld_hi;
+        constexpr int OCH = WTN / 8;
+        auto swz_s = [](int r) { return OCH == 8 ? ((r >> 1) & 7) : (r & (OCH - 1)); };
+        uint16_t* sp = (uint16_t*)(smem + wave * 32 * WTN * 2);
+        float chunk_ss = 0.f;
+#pragma unroll
+        for (int t = 0; t < NI; ++t) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const f32x4 r = rv[t][q];
+            const int col = wcol0 + t * 32 + 8 * q + half_lane;
+            chunk_ss += (r[0] * r[0] + r[1] * r[1]) + (r[2] * r[2] + r[3] * r[3]);
+            const f32x4 gw = *(const f32x4*)&gsm[(lo_part ? 0 : BN) + col - tn * BN];
+            const int c = (t * 4 + q) ^ swz_s(r32);
+            *(u32x2*)(sp + r32 * WTN + c * 8 + half_lane) =
+                u32x2{H::pack(r[0] * gw[0], r[1] * gw[1]), H::pack(r[2] * gw[2], r[3] * gw[3])};
+          }
+          if (t & 1) {
+            const float other = __shfl_xor(chunk_ss, 32);
+            const float tot = lane < 32 ? chunk_ss + other : other + chunk_ss;
+            if (row_ok && wcol0 + t * 32 < a.N)
+              __builtin_nontemporal_store(tot, xss + (size_t)((wcol0 + t * 32) / kChunk) * ss_ld);
+            chunk_ss = 0.f;
+          }
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        // read back row-major: OCH lanes per staged row, 64 / OCH rows per
+        // access; each row's part decides its destination
+        const int rc = lane % OCH;
+        const int ocol = wcol0 + rc * 8;
+#pragma unroll
+        for (int k = 0; k < 32 * OCH / 64; ++k) {
+          const int rr = k * (64 / OCH) + lane / OCH;
+          const u32x4 v = *(const u32x4*)(sp + rr * WTN + (rc ^ swz_s(rr)) * 8);
+          const int orow = wrow0 + i * 32 + rr;
+          if (orow < a.M && ocol < a.N) {
+            gu16* dst = orow < a.split_out ? aux_rows_lo + (size_t)orow * a.N
+                                           : aux_rows_hi + (size_t)(orow - a.split_out) * a.N;
+            // non-temporal: read two launches later, not by this one's tiles
+            __builtin_nontemporal_store(v, (__attribute__((address_space(1))) u32x4*)(dst + ocol));
+          }
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      }
     }
   } else if constexpr (EPI == EPI_STORE_BF16 || EPI == EPI_BIAS_BF16 || EPI == EPI_BIAS_RELU_BF16) {
     // Bias and ReLU run on the accumulators (a lane's four consecutive
@@ -559,13 +716,15 @@ __global__ __launch_bounds__((BM / WTM) * (BN / WTN) * 64, 1) void gemm_bf16_ker
 // weight panel by the cell's row tiles matters more (the hint cost the
 // K = 8192 projections 0.4-2%, and 2-4% at K = 4096).
 template <int EPI, bool F16, int BM, int WTM, int WTN>
-void launch_one(const GemmArgs& a, const GroupTable& tab, hipStream_t stream) {
+void launch_one(const GemmArgs& a, const GroupTable& tab, const NormAux& aux, hipStream_t stream) {
   const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN) * tab.G;
   constexpr int threads = (BM / WTM) * (BN / WTN) * 64;
   if (a.K <= 2048)
-    hipLaunchKernelGGL((gemm_bf16_kernel<EPI, BM, WTM, WTN, true, F16>), dim3(tiles), dim3(threads), 0, stream, a, tab);
+    hipLaunchKernelGGL((gemm_bf16_kernel<EPI, BM, WTM, WTN, true, F16>), dim3(tiles), dim3(threads), 0, stream, a, tab,
+                       aux);
   else
-    hipLaunchKernelGGL((gemm_bf16_kernel<EPI, BM, WTM, WTN, false, F16>), dim3(tiles), dim3(threads), 0, stream, a, tab);
+    hipLaunchKernelGGL((gemm_bf16_kernel<EPI, BM, WTM, WTN, false, F16>), dim3(tiles), dim3(threads), 0, stream, a,
+                       tab, aux);
 }
 
 // Tile shapes.  The operand bytes a tile pulls from L2 per MFMA fall as the
@@ -602,52 +761,68 @@ double tile_cost(const GemmArgs& a, int G, int bm, double speed) {
 }
 
 template <int EPI, bool F16>
-void launch_epi(const GemmArgs& a, const GroupTable& tab, hipStream_t stream) {
+void launch_epi(const GemmArgs& a, const GroupTable& tab, const NormAux& aux, hipStream_t stream) {
   const bool wide_heads = EPI == EPI_QKV_ROPE && a.hd == 128;
   const double c288 = wide_heads ? 1e300 : tile_cost(a, tab.G, 288, 1.00);
   const double c256 = tile_cost(a, tab.G, 256, 0.95);
   const double c192 = wide_heads ? 1e300 : tile_cost(a, tab.G, 192, 0.85);
   const double c128 = tile_cost(a, tab.G, 128, 0.72);
   if (c288 <= c256 && c288 <= c192 && c288 <= c128) {
-    launch_one<EPI, F16, 288, 96, 64>(a, tab, stream);
+    launch_one<EPI, F16, 288, 96, 64>(a, tab, aux, stream);
   } else if (c256 <= c192 && c256 <= c128) {
-    launch_one<EPI, F16, 256, 64, 128>(a, tab, stream);
+    launch_one<EPI, F16, 256, 64, 128>(a, tab, aux, stream);
   } else if (c192 <= c128) {
-    launch_one<EPI, F16, 192, 96, 64>(a, tab, stream);
+    launch_one<EPI, F16, 192, 96, 64>(a, tab, aux, stream);
   } else if (wide_heads) {
-    launch_one<EPI, F16, 128, 32, 128>(a, tab, stream);
+    launch_one<EPI, F16, 128, 32, 128>(a, tab, aux, stream);
   } else {
-    launch_one<EPI, F16, 128, 64, 64>(a, tab, stream);
+    launch_one<EPI, F16, 128, 64, 64>(a, tab, aux, stream);
   }
 }
 
 }  // namespace
 
-hipError_t launch_gemm(int epilogue, const GemmArgs& a, const GroupTable& tab, hipStream_t stream) {
+hipError_t launch_gemm(int epilogue, const GemmArgs& a, const GroupTable& tab, hipStream_t stream,
+                       const NormAux* aux_in) {
   if (tab.G == 0 || a.M == 0 || a.N == 0) return hipSuccess;
   const bool plain_store = epilogue == EPI_STORE_BF16 || epilogue == EPI_BIAS_BF16 ||
                            epilogue == EPI_BIAS_RELU_BF16;
   if (plain_store && a.N % 8 != 0) return hipErrorInvalidValue;   // whole 16-byte output chunks
   if (a.q_cols < 0 || a.q_cols % 32 != 0) return hipErrorInvalidValue;   // whole 32-column blocks
+  if (a.a_split < 0 || a.a_split % 8 != 0 || (a.a_split > 0 && epilogue != EPI_QKV_ROPE))
+    return hipErrorInvalidValue;   // whole 8-row loads on each side of the split
+  const bool resid = epilogue == EPI_RESID_F32 || epilogue == EPI_RESID_BIAS_F32 || epilogue == EPI_RESID_NORM_F32;
+  if (resid && a.N % 32 != 0) return hipErrorInvalidValue;   // whole 32-column blocks
+  if (epilogue == EPI_RESID_NORM_F32 && (!aux_in || !a.aux_gamma || a.N % kChunk != 0))
+    return hipErrorInvalidValue;
+  if (epilogue == EPI_RESID_NORM_F32) {
+    for (int g = 0; g < tab.G; ++g)      // every side output has a destination
+      if (!aux_in->rows_lo[g] || !aux_in->rows_hi[g] || !aux_in->ss_lo[g] || !aux_in->ss_hi[g])
+        return hipErrorInvalidValue;
+  }
+  static const NormAux none{};
+  const NormAux& aux = aux_in ? *aux_in : none;
   if (a.f16) {
     // fp16 operands: the epilogues of the LLaMA-shaped cell and the plain store
     switch (epilogue) {
-      case EPI_STORE_BF16: launch_epi<EPI_STORE_BF16, true>(a, tab, stream); break;
-      case EPI_QKV_ROPE: launch_epi<EPI_QKV_ROPE, true>(a, tab, stream); break;
-      case EPI_SWIGLU: launch_epi<EPI_SWIGLU, true>(a, tab, stream); break;
-      case EPI_RESID_F32: launch_epi<EPI_RESID_F32, true>(a, tab, stream); break;
+      case EPI_STORE_BF16: launch_epi<EPI_STORE_BF16, true>(a, tab, aux, stream); break;
+      case EPI_QKV_ROPE: launch_epi<EPI_QKV_ROPE, true>(a, tab, aux, stream); break;
+      case EPI_SWIGLU: launch_epi<EPI_SWIGLU, true>(a, tab, aux, stream); break;
+      case EPI_RESID_F32: launch_epi<EPI_RESID_F32, true>(a, tab, aux, stream); break;
+      case EPI_RESID_NORM_F32: launch_epi<EPI_RESID_NORM_F32, true>(a, tab, aux, stream); break;
       default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
   }
   switch (epilogue) {
-    case EPI_STORE_BF16: launch_epi<EPI_STORE_BF16, false>(a, tab, stream); break;
-    case EPI_QKV_ROPE: launch_epi<EPI_QKV_ROPE, false>(a, tab, stream); break;
-    case EPI_SWIGLU: launch_epi<EPI_SWIGLU, false>(a, tab, stream); break;
-    case EPI_RESID_F32: launch_epi<EPI_RESID_F32, false>(a, tab, stream); break;
-    case EPI_BIAS_BF16: launch_epi<EPI_BIAS_BF16, false>(a, tab, stream); break;
-    case EPI_BIAS_RELU_BF16: launch_epi<EPI_BIAS_RELU_BF16, false>(a, tab, stream); break;
-    case EPI_RESID_BIAS_F32: launch_epi<EPI_RESID_BIAS_F32, false>(a, tab, stream); break;
+    case EPI_STORE_BF16: launch_epi<EPI_STORE_BF16, false>(a, tab, aux, stream); break;
+    case EPI_QKV_ROPE: launch_epi<EPI_QKV_ROPE, false>(a, tab, aux, stream); break;
+    case EPI_SWIGLU: launch_epi<EPI_SWIGLU, false>(a, tab, aux, stream); break;
+    case EPI_RESID_F32: launch_epi<EPI_RESID_F32, false>(a, tab, aux, stream); break;
+    case EPI_RESID_NORM_F32: launch_epi<EPI_RESID_NORM_F32, false>(a, tab, aux, stream); break;
+    case EPI_BIAS_BF16: launch_epi<EPI_BIAS_BF16, false>(a, tab, aux, stream); break;
+    case EPI_BIAS_RELU_BF16: launch_epi<EPI_BIAS_RELU_BF16, false>(a, tab, aux, stream); break;
+    case EPI_RESID_BIAS_F32: launch_epi<EPI_RESID_BIAS_F32, false>(a, tab, aux, stream); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

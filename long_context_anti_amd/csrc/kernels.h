@@ -27,6 +27,29 @@ struct GroupTable {
   void* out_hi[kMaxGroups];
 };
 
+// Side outputs that prepare the next RMSNorm (the residual epilogues, the
+// segment gather and the memory preparation write them): for output row y of
+// group g -- split like out_lo / out_hi -- the bf16 copy y * gamma[layer] and
+// the sums of y^2 over each 64-column chunk of the row (N / 64 floats per
+// row, each summed in one fixed order).  The consumer reduces the chunks in
+// order to 1 / sqrt(mean(y^2) + eps) and scales its GEMM rows by it.  Every
+// pointer must be valid (rows nobody reads go to a discard area).
+// The chunk sums are stored chunk-major, ss[j * ss_ld + r] for row r and
+// chunk j, so that a wave's sums for 32 consecutive rows of one chunk fill
+// whole 128-byte lines (row-major, the 4-byte sums of one row would come
+// from as many workgroups as the row has chunks, each leaving its line
+// partly written).
+constexpr int kChunk = 64;
+struct NormAux {
+  void* rows_lo[kMaxGroups];       // 16-bit [rows][N]
+  void* rows_hi[kMaxGroups];
+  float* ss_lo[kMaxGroups];        // fp32 [N / kChunk][ss_ld_lo]
+  float* ss_hi[kMaxGroups];        // fp32 [N / kChunk][ss_ld_hi]
+  int32_t layer_lo[kMaxGroups];    // gain row for the lo / hi rows
+  int32_t layer_hi[kMaxGroups];
+  int32_t ss_ld_lo, ss_ld_hi;      // row capacity of the lo / hi sum regions
+};
+
 enum GemmEpilogue : int {
   EPI_STORE_BF16 = 0,  // C = bf16(acc)
   EPI_QKV_ROPE = 1,    // C = bf16(rope(acc)) on Q/K columns, bf16(acc) on V
@@ -35,6 +58,7 @@ enum GemmEpilogue : int {
   EPI_BIAS_BF16 = 4,        // C = bf16(acc + bias)
   EPI_BIAS_RELU_BF16 = 5,   // C = bf16(max(acc + bias, 0))
   EPI_RESID_BIAS_F32 = 6,   // C = residual + (acc + bias), fp32, split row destinations
+  EPI_RESID_NORM_F32 = 7,   // EPI_RESID_F32 plus the NormAux side outputs of the rows
 };
 
 struct GemmArgs {
@@ -53,6 +77,12 @@ struct GemmArgs {
   float q_scale;       //   are multiplied by q_scale before the bf16 rounding (0 cols: none)
   int f16;             // 1: A, B and 16-bit results are fp16 instead of bf16 (EPI_STORE_BF16,
                        //    EPI_QKV_ROPE, EPI_SWIGLU, EPI_RESID_F32 only)
+  int a_split;         // EPI_QKV_ROPE: > 0: A rows [0, a_split) of group g from tab.in_lo[g],
+                       //   rows from a_split on from tab.in_hi[g] (16-bit rows of K; a
+                       //   multiple of 8); 0: A packed per group as above
+  const float* row_scale;  // EPI_QKV_ROPE, EPI_SWIGLU: non-null: output row r of group g is
+                           //   multiplied by row_scale[g * M + r] first (an RMSNorm's 1/rms)
+  const float* aux_gamma;  // EPI_RESID_NORM_F32: gains [Lw][N] of the side outputs
 };
 
 // Softmax scale of attention in the base-2 domain, log2(e) / sqrt(hd).  The
@@ -60,7 +90,22 @@ struct GemmArgs {
 // both sides must use this one value.
 inline float attention_scale_log2(int hd) { return 1.4426950408889634f / sqrtf((float)hd); }
 
-hipError_t launch_gemm(int epilogue, const GemmArgs& a, const GroupTable& tab, hipStream_t stream);
+hipError_t launch_gemm(int epilogue, const GemmArgs& a, const GroupTable& tab, hipStream_t stream,
+                       const NormAux* aux = nullptr);
+
+// 1 / sqrt(sum of a row's chunk sums / d + eps) for every row of every group
+// (rows [0, split) from ss_lo[g], the rest from ss_hi[g] of `aux`), packed
+// into rinv [G * R].
+hipError_t launch_row_rinv(int G, int R, int d, int split, const NormAux& aux, float eps, float* rinv,
+                           hipStream_t stream);
+// Side outputs for fp32 rows that no GEMM epilogue produced: `rows` rows of
+// `src` [rows][d] in regions of rows_per_layer rows; region q uses gain row
+// layer0 + q % L.  Writes the 16-bit copy dst16 [rows][d] (bf16, or fp16 per
+// f16) and the chunk sums, chunk-major per region: dss + q * rows_per_layer *
+// (d / 64) holds [d / 64][rows_per_layer].
+hipError_t launch_norm_aux_rows(int rows, int d, const float* src, int rows_per_layer, int L,
+                                int layer0, const float* gamma, uint16_t* dst16, float* dss,
+                                bool f16, hipStream_t stream);
 
 // Row-wise RMSNorm of every group's R rows (fp32 in, bf16 -- or fp16 when
 // f16 is set -- out, packed).
@@ -81,8 +126,13 @@ hipError_t launch_cast_rows(int G, int R, int d, int split_in, const GroupTable&
                             hipStream_t stream);
 
 // X(-1, s) rows -> fp32 slot: token-id lookup (bf16 table) or a row copy.
+// With dst16 non-null the lookup also writes the RMSNorm side outputs of the
+// rows (gain row `gamma`, [d]): dst16 [n][d] and the chunk sums dss
+// [d / 64][ss_ld] (chunk-major, ss_ld >= n).
 hipError_t launch_gather_tokens(int n, int d, const int32_t* ids, int V, const uint16_t* embed,
-                                float* dst, int32_t* bad_flag, hipStream_t stream);
+                                float* dst, int32_t* bad_flag, hipStream_t stream,
+                                const float* gamma = nullptr, uint16_t* dst16 = nullptr,
+                                float* dss = nullptr, int ss_ld = 0, bool f16 = false);
 hipError_t launch_copy_rows_bf16(int n, int d, const uint16_t* src, float* dst,
                                  hipStream_t stream);
 

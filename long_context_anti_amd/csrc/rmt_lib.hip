@@ -112,6 +112,18 @@ struct rmt_model {
   uint16_t* ubuf = nullptr;  // [C*R][F]
   float* xbuf[2] = {nullptr, nullptr};  // [B][L][n][d] each
   float* memw = nullptr;     // [B][L][m][d]
+  // LLAMA: RMSNorm inputs prepared by the producers of the rows (16-bit
+  // copies y * gamma and 64-column chunk sums of y^2): X slots (parallel to
+  // xbuf), memory rows (parallel to the two memory buffers, same parity), and
+  // the per-launch H rows; rinv holds the launch's 1/rms per row.
+  // X slots of the 16-bit copies: slot l holds X(l-1, .); slot L takes the
+  // last layer's copies, which no cell reads
+  uint16_t* xb16[2] = {nullptr, nullptr};  // [B][L+1][n][d]
+  float* xss[2] = {nullptr, nullptr};      // [B][L+1] slots of [d/64][n] (chunk-major)
+  uint16_t* mb16[2] = {nullptr, nullptr};  // [B][L][m][d]; [0] pairs with out->mem, [1] with memw
+  float* mss[2] = {nullptr, nullptr};      // [B][L] slots of [d/64][m]
+  float* hss = nullptr;      // [C] cells of [d/64][R]
+  float* rinv = nullptr;     // [C*R]
   int32_t* flag = nullptr;   // bad-token flag
 
   // timing
@@ -173,6 +185,7 @@ int32_t validate_config(const rmt_config* c) {
     return fail(RMT_EINVAL, "post_norm is 0 or 1, and 1 only for ENCODER cells");
   if (c->cell == RMT_CELL_LLAMA) {
     if (c->vocab < 1) return fail(RMT_EINVAL, "vocab must be >= 1");
+    if (c->m % 8 != 0) return fail(RMT_EUNSUPPORTED, "LLAMA cells need m a multiple of 8 (got %d)", c->m);
     if (!(c->rope_theta > 0.f)) return fail(RMT_EINVAL, "rope_theta must be > 0");
   }
   if ((int64_t)c->L * R * 2 * widest > INT32_MAX) return fail(RMT_EINVAL, "sizes overflow int32");
@@ -256,9 +269,13 @@ int32_t run_cells(rmt_model* M, const Cell* cells, int G, const void* tokens, co
     if (l == 0 && c.cell != RMT_CELL_LINEAR_GELU) {
       // X(-1, s): this segment's input rows, into slot 0 of the read buffer.
       if (c.cell == RMT_CELL_LLAMA) {
+        // with the RMSNorm-1 inputs of layer 0: 16-bit copy and chunk sums
+        const size_t nc = d / kChunk;
         LAUNCH(launch_gather_tokens(ns, d, (const int32_t*)tokens + tok0, c.vocab, M->embed,
-                                    slot(xr, b, 0), M->flag, M->stream));
-        MARK(RMT_STAGE_GATHER, 0.0, (double)ns * (4 + (size_t)d * 6));
+                                    slot(xr, b, 0), M->flag, M->stream, M->g1,
+                                    M->xb16[(k + 1) & 1] + (size_t)b * (L + 1) * n * d,
+                                    M->xss[(k + 1) & 1] + (size_t)b * (L + 1) * n * nc, n, c.dtype == RMT_F16));
+        MARK(RMT_STAGE_GATHER, 0.0, (double)ns * (4 + (size_t)d * 8 + nc * 4));
       } else {
         LAUNCH(launch_copy_rows_bf16(ns, d, (const uint16_t*)tokens + tok0 * d, slot(xr, b, 0),
                                      M->stream));
@@ -296,38 +313,67 @@ int32_t run_cells(rmt_model* M, const Cell* cells, int G, const void* tokens, co
 
   const bool f16 = c.dtype == RMT_F16;   // LLAMA cells only: every 16-bit operand in fp16
   ga.f16 = f16;
+  NormAux ax;
+  std::memset(&ax, 0, sizeof(ax));
+  const size_t nc = d / kChunk;
+  // memory-buffer parity of segment s (the buffer mem_buf picks), for the
+  // memory rows' 16-bit copies and chunk sums
+  auto mpar = [&](int s) { return ((S - 1 - s) % 2 == 0) ? 0 : 1; };
   if (c.cell == RMT_CELL_LLAMA) {
     const int hd = c.head_dim, Hq = c.n_heads, Hkv = c.n_kv_heads, NQ = nqkv(c);
-    // RMSNorm 1 of [M(l, s-1); X(l-1, s)]
-    set_io(in_lo, in_hi, nullptr, nullptr);
-    LAUNCH(launch_rmsnorm(G, R, d, m, tab, M->g1, c.eps, M->abuf, M->stream, f16));
-    MARK(RMT_STAGE_NORM1, 0.0, rows * d * 6);
-    // QKV projection + RoPE on Q and K
-    for (int g = 0; g < G; ++g) packed_out[g] = M->qkv + (size_t)g * R * NQ;
-    set_io(nullptr, nullptr, packed_out, nullptr);
-    ga.A = M->abuf; ga.B = M->wqkv; ga.M = R; ga.N = NQ; ga.K = d;
+    const int pr = (k + 1) & 1;    // X read parity
+    // RMSNorm 1 of [M(l, s-1); X(l-1, s)]: 1/rms per row from the chunk sums
+    // that the rows' producers wrote (down projections, gather, memory prep)
+    for (int g = 0; g < G; ++g) {
+      const int l = cells[g].l, s = cells[g].s, b = cells[g].b;
+      ax.ss_lo[g] = M->mss[mpar(s - 1)] + ((size_t)b * L + l) * m * nc;
+      ax.ss_hi[g] = M->xss[pr] + ((size_t)b * (L + 1) + l) * n * nc;
+    }
+    ax.ss_ld_lo = m;
+    ax.ss_ld_hi = n;
+    LAUNCH(launch_row_rinv(G, R, d, m, ax, c.eps, M->rinv, M->stream));
+    MARK(RMT_STAGE_NORM1, 0.0, rows * (nc * 4 + 4));
+    // QKV projection of the rows' 16-bit copies y * g1 (memory rows, then
+    // segment rows), scaled by 1/rms per row, + RoPE on Q and K
+    for (int g = 0; g < G; ++g) {
+      const int l = cells[g].l, s = cells[g].s, b = cells[g].b;
+      tab.in_lo[g] = M->mb16[mpar(s - 1)] + ((size_t)b * L + l) * m * d;
+      tab.in_hi[g] = M->xb16[pr] + ((size_t)b * (L + 1) + l) * n * d;
+      tab.out_lo[g] = M->qkv + (size_t)g * R * NQ;
+      tab.out_hi[g] = nullptr;
+    }
+    ga.A = nullptr; ga.B = M->wqkv; ga.M = R; ga.N = NQ; ga.K = d;
     ga.split_in = R; ga.split_out = R; ga.ld_res = 0; ga.ld_out = NQ;
     ga.rope = M->rope; ga.rope_cols = (Hq + Hkv) * hd; ga.hd = hd;
     ga.q_cols = Hq * hd; ga.q_scale = attention_scale_log2(hd);   // Q leaves with the softmax scale
+    ga.a_split = m; ga.row_scale = M->rinv;
     LAUNCH(launch_gemm(EPI_QKV_ROPE, ga, tab, M->stream));
-    ga.q_cols = 0;
-    MARK(RMT_STAGE_QKV, 2.0 * rows * d * NQ, rows * d * 2 + G_ * NQ * d * 2 + rows * NQ * 2);
+    ga.q_cols = 0; ga.a_split = 0; ga.row_scale = nullptr;
+    MARK(RMT_STAGE_QKV, 2.0 * rows * d * NQ, rows * d * 2 + G_ * NQ * d * 2 + rows * NQ * 2 + rows * 4);
     // causal GQA attention inside each cell
     LAUNCH(launch_attention(M->qkv, M->att, G, R, Hq, Hkv, hd, true, true, M->stream, f16));
     MARK(RMT_STAGE_ATTN, 2.0 * G_ * Hq * hd * (double)R * (R + 1), rows * NQ * 2 + rows * Hq * hd * 2);
-    // O projection + residual A -> H
+    // O projection + residual A -> H (fp32), and H's RMSNorm-2 inputs: the
+    // 16-bit copy H * g2 (the gate/up operand) and its chunk sums
     for (int g = 0; g < G; ++g) packed_out[g] = M->hbuf + (size_t)g * R * d;
+    std::memset(&ax, 0, sizeof(ax));
+    for (int g = 0; g < G; ++g) {
+      ax.rows_lo[g] = ax.rows_hi[g] = M->abuf + (size_t)g * R * d;   // every row is "lo" (split R)
+      ax.ss_lo[g] = ax.ss_hi[g] = M->hss + (size_t)g * R * nc;
+      ax.layer_lo[g] = ax.layer_hi[g] = cells[g].l;
+    }
+    ax.ss_ld_lo = ax.ss_ld_hi = R;
     set_io(in_lo, in_hi, packed_out, nullptr);
     ga.A = M->att; ga.B = M->wo; ga.M = R; ga.N = d; ga.K = Hq * hd;
     ga.split_in = m; ga.split_out = R; ga.ld_res = d; ga.ld_out = d;
-    LAUNCH(launch_gemm(EPI_RESID_F32, ga, tab, M->stream));
+    ga.aux_gamma = M->g2;
+    LAUNCH(launch_gemm(EPI_RESID_NORM_F32, ga, tab, M->stream, &ax));
+    ga.aux_gamma = nullptr;
     MARK(RMT_STAGE_OPROJ, 2.0 * rows * Hq * hd * d,
-         rows * Hq * hd * 2 + G_ * d * Hq * hd * 2 + rows * d * 8);
-    // RMSNorm 2 of H
-    for (int g = 0; g < G; ++g) packed_lo[g] = M->hbuf + (size_t)g * R * d;
-    set_io(packed_lo, packed_lo, nullptr, nullptr);
-    LAUNCH(launch_rmsnorm(G, R, d, R, tab, M->g2, c.eps, M->abuf, M->stream, f16));
-    MARK(RMT_STAGE_NORM2, 0.0, rows * d * 6);
+         rows * Hq * hd * 2 + G_ * d * Hq * hd * 2 + rows * d * 10 + rows * nc * 4);
+    // RMSNorm 2: 1/rms per row of H
+    LAUNCH(launch_row_rinv(G, R, d, R, ax, c.eps, M->rinv, M->stream));
+    MARK(RMT_STAGE_NORM2, 0.0, rows * (nc * 4 + 4));
   } else if (c.cell == RMT_CELL_ENCODER && c.post_norm) {
     const int hd = c.head_dim, H = c.n_heads, NQ = nqkv(c);
     // A = [M(l, s-1); X(l-1, s)] as bf16 (the attention sees A itself)
@@ -442,22 +488,49 @@ int32_t run_cells(rmt_model* M, const Cell* cells, int G, const void* tokens, co
   set_io(nullptr, nullptr, packed_out, nullptr);
   ga.A = M->abuf; ga.B = M->wgu; ga.M = R; ga.N = 2 * F; ga.K = d;
   ga.split_in = R; ga.split_out = R; ga.ld_res = 0; ga.ld_out = F;
+  // LLAMA: abuf holds H * g2, and the rows take their 1/rms here
+  ga.row_scale = c.cell == RMT_CELL_LLAMA ? M->rinv : nullptr;
   LAUNCH(launch_gemm(EPI_SWIGLU, ga, tab, M->stream));
-  MARK(RMT_STAGE_GATEUP, 2.0 * rows * d * 2 * F, rows * d * 2 + G_ * 2 * F * d * 2 + rows * F * 2);
+  ga.row_scale = nullptr;
+  MARK(RMT_STAGE_GATEUP, 2.0 * rows * d * 2 * F,
+       rows * d * 2 + G_ * 2 * F * d * 2 + rows * F * 2 + (c.cell == RMT_CELL_LLAMA ? rows * 4 : 0));
 
   // down projection + residual; rows [0, n) -> X(l, s), rows [n, R) -> M(l, s)
+  double aux_bytes = 0.0;
   if (c.cell == RMT_CELL_LLAMA) {
     for (int g = 0; g < G; ++g) packed_lo[g] = M->hbuf + (size_t)g * R * d;
     set_io(packed_lo, packed_lo, x_out, m_out);
     ga.split_in = R;
+    // and the RMSNorm-1 inputs of the rows' next cells: X(l, s) for (l+1, s)
+    // (gain g1[l+1]; none after the last layer), M(l, s) for (l, s+1) (gain
+    // g1[l]; none after the last segment)
+    std::memset(&ax, 0, sizeof(ax));
+    const int pw = k & 1;
+    for (int g = 0; g < G; ++g) {
+      const int l = cells[g].l, s = cells[g].s, b = cells[g].b;
+      // slot l+1 (slot L, a discard area, after the last layer)
+      ax.rows_lo[g] = M->xb16[pw] + ((size_t)b * (L + 1) + l + 1) * n * d;
+      ax.ss_lo[g] = M->xss[pw] + ((size_t)b * (L + 1) + l + 1) * n * nc;
+      // after the last segment these copies are not read (the next forward
+      // call prepares its own from the memory it is given)
+      ax.rows_hi[g] = M->mb16[mpar(s)] + ((size_t)b * L + l) * m * d;
+      ax.ss_hi[g] = M->mss[mpar(s)] + ((size_t)b * L + l) * m * nc;
+      ax.layer_lo[g] = std::min(l + 1, L - 1);
+      ax.layer_hi[g] = l;
+    }
+    ax.ss_ld_lo = n;
+    ax.ss_ld_hi = m;
+    aux_bytes = rows * ((double)d * 2 + nc * 4);
+    ga.aux_gamma = M->g1;
   } else {
     set_io(in_lo, in_hi, x_out, m_out);
     ga.split_in = m;
   }
   ga.A = M->ubuf; ga.B = M->wd; ga.M = R; ga.N = d; ga.K = F;
   ga.split_out = ns; ga.ld_res = d; ga.ld_out = d;
-  LAUNCH(launch_gemm(EPI_RESID_F32, ga, tab, M->stream));
-  MARK(RMT_STAGE_DOWN, 2.0 * rows * F * d, rows * F * 2 + G_ * d * F * 2 + rows * d * 8);
+  LAUNCH(launch_gemm(c.cell == RMT_CELL_LLAMA ? EPI_RESID_NORM_F32 : EPI_RESID_F32, ga, tab, M->stream, &ax));
+  ga.aux_gamma = nullptr;
+  MARK(RMT_STAGE_DOWN, 2.0 * rows * F * d, rows * F * 2 + G_ * d * F * 2 + rows * d * 8 + aux_bytes);
   return RMT_OK;
 }
 
@@ -539,6 +612,17 @@ std::vector<Piece> workspace_pieces(rmt_model* M, int B) {
   pieces.push_back({(void**)&M->xbuf[0], (size_t)B * L * n * d * 4});
   pieces.push_back({(void**)&M->xbuf[1], (size_t)B * L * n * d * 4});
   pieces.push_back({(void**)&M->memw, (size_t)B * L * m * d * 4});
+  if (c.cell == RMT_CELL_LLAMA) {
+    const size_t nc = d / kChunk;
+    for (int p = 0; p < 2; ++p) {
+      pieces.push_back({(void**)&M->xb16[p], (size_t)B * (L + 1) * n * d * 2});
+      pieces.push_back({(void**)&M->xss[p], (size_t)B * (L + 1) * n * nc * 4});
+      pieces.push_back({(void**)&M->mb16[p], (size_t)B * L * m * d * 2});
+      pieces.push_back({(void**)&M->mss[p], (size_t)B * L * m * nc * 4});
+    }
+    pieces.push_back({(void**)&M->hss, rows * nc * 4});
+    pieces.push_back({(void**)&M->rinv, rows * 4});
+  }
   return pieces;
 }
 
@@ -628,6 +712,14 @@ int32_t start_forward(rmt_model* M, const void* mem0, const rmt_output* out) {
   if ((const void*)dst != mem0) {
     HIP_TRY(hipMemcpyAsync(dst, mem0, mem_bytes, hipMemcpyDeviceToDevice, M->stream));
     MARK(RMT_STAGE_GATHER, 0.0, 2.0 * mem_bytes);
+  }
+  if (c.cell == RMT_CELL_LLAMA) {
+    // RMSNorm-1 inputs of M(l, -1): 16-bit copies y * g1[l] and chunk sums
+    const int par = (c.S % 2 == 0) ? 0 : 1;     // the parity of segment -1
+    const int rows = M->batch * c.L * c.m;
+    HIP_TRY(launch_norm_aux_rows(rows, c.d, dst, c.m, c.L, 0, M->g1, M->mb16[par], M->mss[par],
+                                 c.dtype == RMT_F16, M->stream));
+    MARK(RMT_STAGE_GATHER, 0.0, (double)rows * c.d * 6 + (double)rows * (c.d / kChunk) * 4);
   }
   return RMT_OK;
 }

@@ -99,9 +99,14 @@ def test_workspace_size_llama1b_and_batch():
     def want(B):
         cells = min(32, B * c.L)
         rows = cells * c.R
+        nc = c.d // 64          # 64-column chunk sums per row (RMSNorm inputs)
+        # X slots' 16-bit copies and chunk sums (L + 1 slots: the last is a discard area), the same for
+        # the memory rows, twice (ping-pong), then the launch's H chunk sums and 1/rms per row
+        norm_inputs = [B * (c.L + 1) * c.n * c.d * 2, B * (c.L + 1) * c.n * nc * 4,
+                       B * c.L * c.m * c.d * 2, B * c.L * c.m * nc * 4] * 2 + [rows * nc * 4, rows * 4]
         return _layout([rows * c.d * 2, rows * c.F * 2, rows * c.n_qkv * 2, rows * c.Hq * c.hd * 2,
                         rows * c.d * 4, B * c.L * c.n * c.d * 4, B * c.L * c.n * c.d * 4,
-                        B * c.L * c.m * c.d * 4])
+                        B * c.L * c.m * c.d * 4] + norm_inputs)
     h = _create(c)
     ws1 = _bytes(h, Lib.RMT_BUF_WORKSPACE)
     assert ws1 == want(1)
