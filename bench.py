@@ -48,10 +48,10 @@ ENCODER_STAGE_NAMES = {"norm1": "layernorm1", "norm2": "layernorm2", "gateup": "
 # post-norm: the first norm-stage launch is the bf16 copy of A, the second stage holds both LayerNorms
 POSTNORM_STAGE_NAMES = {"norm1": "cast_a_bf16", "norm2": "layernorms", "gateup": "ffn_w1", "down": "ffn_w2"}
 GEMM_KERNELS = {
-    "llama": {"qkv": "QKV stage + RoPE epilogue (gemm_bf16_kernel<1, ...>)",
-              "oproj": "O stage + residual epilogue (gemm_bf16_kernel<3, ...>)",
-              "gateup": "gate/up stage + SwiGLU epilogue (gemm_bf16_kernel<2, ...>)",
-              "down": "down stage + residual epilogue (gemm_bf16_kernel<3, ...>)"},
+    "llama": {"qkv": "QKV stage, rows scaled by 1/rms + RoPE epilogue (gemm_bf16_kernel<1, ...>)",
+              "oproj": "O stage + residual and RMSNorm side-output epilogue (gemm_bf16_kernel<7, ...>)",
+              "gateup": "gate/up stage, rows scaled by 1/rms + SwiGLU epilogue (gemm_bf16_kernel<2, ...>)",
+              "down": "down stage + residual and RMSNorm side-output epilogue (gemm_bf16_kernel<7, ...>)"},
     "encoder": {"qkv": "QKV stage + bias epilogue (gemm_bf16_kernel<4>)",
                 "oproj": "O stage + bias + residual epilogue (gemm_bf16_kernel<6>)",
                 "gateup": "W1 stage + bias + ReLU epilogue (gemm_bf16_kernel<5>)",
