@@ -191,8 +191,12 @@ int32_t rmt_model_create(const rmt_config* cfg, const rmt_weights* w, void* stre
  *   RMT_BUF_WORKSPACE  the activations: per-launch buffers for up to
  *                      min(32, B L) cells (normalised rows, Q/K/V, attention
  *                      output, H, U), the X ping-pong pair of every sequence
- *                      and a second memory buffer [B][L][m][d]; depends on
- *                      L, R, d, F and the batch B, not on S.
+ *                      and a second memory buffer [B][L][m][d]; for LLAMA
+ *                      cells also the inputs of the RMSNorms that the rows'
+ *                      producers prepare (16-bit copies y * gamma and sums of
+ *                      y^2 over 64-column chunks, for every X slot, memory
+ *                      row and H row) and the per-launch 1/rms rows.  Depends
+ *                      on L, R, d, F and the batch B, not on S.
  * rmt_workspace_bytes writes the size in bytes that `kind` needs for the
  * model's current batch.  Errors: RMT_EINVAL. */
 #define RMT_BUF_WEIGHTS 0

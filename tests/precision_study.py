@@ -5,13 +5,15 @@ evaluated in fp32 exactly as the oracle defines it, except that the values the
 GPU path stores in a 16-bit type -- each of them an MFMA operand -- can be
 rounded at their point of the dataflow:
 
-  norm1     the normalised cell input, operand of the Q/K/V product
+  norm1     the 16-bit operand of the Q/K/V product: y * g with 1/rms applied
+            to the product's rows (the GPU's dataflow), or the normalised
+            row itself (the oracle's order; --norm-order normalised)
   qkv       Q (after RoPE, carrying the softmax scale log2(e)/sqrt(hd)), K
             (after RoPE) and V, operands of the two attention products
   probs     the softmax probabilities, operand of P V (the row sums are taken
             over the rounded values, as on the GPU)
   attn_out  the attention output, operand of the O product
-  norm2     the normalised H, operand of the gate/up product
+  norm2     the same for H, operand of the gate/up product
   u         silu(gate) * up, operand of the down product
 
 to bf16 or to fp16 (round to nearest even).  With no point rounded the cell
@@ -58,22 +60,43 @@ def round_fp16(x: np.ndarray) -> np.ndarray:
 ROUND = {"bf16": ri.round_bf16, "fp16": round_fp16}
 
 
+NORM_ORDERS = ("scaled_after", "normalised")
+
+
 def emulated_llama_cell(A: np.ndarray, w: Dict[str, np.ndarray], cfg, points: Iterable[str],
-                        fmt: str = "bf16") -> np.ndarray:
-    """The pre-norm LLaMA cell in fp32 with the named points rounded to `fmt`."""
+                        fmt: str = "bf16", norm_order: str = "scaled_after") -> np.ndarray:
+    """The pre-norm LLaMA cell in fp32 with the named points rounded to `fmt`.
+
+    norm_order says where an RMSNorm's 1/rms enters its GEMM, which decides
+    what the norm1 / norm2 points round:
+      scaled_after  the GPU's dataflow: the 16-bit operand is y * g, and the
+                    product's rows are multiplied by 1/rms afterwards (in fp32)
+      normalised    the oracle's order: the operand is rms_norm(y) * g itself
+    Both equal rms_norm(y, g) @ W up to fp32 rounding when nothing is rounded.
+    """
     pts = set(points)
     unknown = pts - set(POINTS)
     assert not unknown, unknown
+    assert norm_order in NORM_ORDERS, norm_order
     rnd = ROUND[fmt]
 
     def at(name, x):
         return rnd(x) if name in pts else x
 
+    def normed_product(name, y, g, Ws):
+        """rms_norm(y, g) @ W for each W in Ws, with the rounding point `name`."""
+        if norm_order == "normalised":
+            z = at(name, orc.rms_norm(y, g, cfg.eps))
+            return [z @ W for W in Ws]
+        rinv = (np.float32(1.0) / np.sqrt(np.mean(y * y, axis=1, dtype=np.float32)
+                                          + np.float32(cfg.eps))).astype(np.float32)
+        z = at(name, (y * g).astype(np.float32))
+        return [(z @ W) * rinv[:, None] for W in Ws]
+
     R = A.shape[0]
     Hq, Hkv, hd = cfg.Hq, cfg.Hkv, cfg.hd
     c = np.float32(math.log2(math.e) / math.sqrt(hd))
-    z = at("norm1", orc.rms_norm(A, w["g1"], cfg.eps))
-    qkv = z @ w["wqkv"]
+    (qkv,) = normed_product("norm1", A, w["g1"], [w["wqkv"]])
     nq, nk = Hq * hd, Hkv * hd
     pos = np.arange(R)
     q = orc.rope_rotate_half(qkv[:, :nq].reshape(R, Hq, hd), pos, cfg.theta) * c
@@ -91,15 +114,16 @@ def emulated_llama_cell(A: np.ndarray, w: Dict[str, np.ndarray], cfg, points: It
         att[:, h, :] = (p @ v[:, j, :]) / p.sum(axis=1, keepdims=True)
     att = at("attn_out", att.reshape(R, nq))
     H = A + att @ w["wo"]
-    hn = at("norm2", orc.rms_norm(H, w["g2"], cfg.eps))
-    u = at("u", orc.silu(hn @ w["wg"]) * (hn @ w["wu"]))
+    gate, up = normed_product("norm2", H, w["g2"], [w["wg"], w["wu"]])
+    u = at("u", orc.silu(gate) * up)
     return H + u @ w["wd"]
 
 
-def sweep(cfg, layers, tokens, mem0, embed, S: int, points=(), fmt="bf16", cell=None):
+def sweep(cfg, layers, tokens, mem0, embed, S: int, points=(), fmt="bf16", cell=None,
+          norm_order="scaled_after"):
     """Segment by segment, layer by layer (the oracle's sequential order) over
     the first S segments with the emulated cell.  Returns (hidden, memory)."""
-    cell = cell or (lambda A, w: emulated_llama_cell(A, w, cfg, points, fmt))
+    cell = cell or (lambda A, w: emulated_llama_cell(A, w, cfg, points, fmt, norm_order))
     n = cfg.n
     M = [np.array(mem0[l], np.float32) for l in range(cfg.L)]
     hidden = []
@@ -124,16 +148,18 @@ def load(cfg, S: int, seed: int = 0):
     return layers, ri.tokens(cfg, seed, S=S), ri.initial_memory(cfg, seed), ri.embedding(cfg, seed)
 
 
-def rounding_table(cfg, S: int, variants, seed: int = 0, log=print) -> Dict[str, Tuple[float, float]]:
+def rounding_table(cfg, S: int, variants, seed: int = 0, log=print,
+                   norm_order: str = "scaled_after") -> Dict[str, Tuple[float, float]]:
     """Relative L2 error of hidden and memory after S segments, for each
-    (label, points, fmt) variant, against the unrounded sweep."""
+    (label, points, fmt) variant, against the unrounded sweep (the oracle's
+    cell up to fp32 rounding order)."""
     layers, tok, mem0, embed = load(cfg, S, seed)
     t0 = time.perf_counter()
     h_ref, m_ref = sweep(cfg, layers, tok, mem0, embed, S)
     log(f"reference sweep: {time.perf_counter() - t0:.1f} s")
     out = {}
     for label, points, fmt in variants:
-        h, m = sweep(cfg, layers, tok, mem0, embed, S, points, fmt)
+        h, m = sweep(cfg, layers, tok, mem0, embed, S, points, fmt, norm_order=norm_order)
         out[label] = (rel_l2(h, h_ref), rel_l2(m, m_ref))
         log(f"{label:40s} hidden {out[label][0]:.3e}  mem {out[label][1]:.3e}")
     return out
@@ -168,6 +194,8 @@ def main():
     ap.add_argument("--segments", type=int, default=1)
     ap.add_argument("--chaos", type=int, default=0, help="segments of the perturbation study instead")
     ap.add_argument("--quick", action="store_true", help="only all-bf16 and all-fp16")
+    ap.add_argument("--norm-order", default="scaled_after", choices=NORM_ORDERS,
+                    help="where 1/rms enters the GEMMs after the RMSNorms (what norm1/norm2 round)")
     args = ap.parse_args()
     cfg = {"llama1b": ri.LLAMA_1B, "llama8b": ri.LLAMA_8B, "tiny_llama": ri.TINY_LLAMA}[args.workload]
     print(f"{cfg.name}: L={cfg.L} d={cfg.d} R={cfg.R}", flush=True)
@@ -175,7 +203,8 @@ def main():
         chaos_growth(cfg, args.chaos, log=lambda m: print(m, flush=True))
         return
     variants = STANDARD_VARIANTS if not args.quick else [STANDARD_VARIANTS[0], STANDARD_VARIANTS[-1]]
-    rounding_table(cfg, args.segments, variants, log=lambda m: print(m, flush=True))
+    print(f"norm order: {args.norm_order}", flush=True)
+    rounding_table(cfg, args.segments, variants, log=lambda m: print(m, flush=True), norm_order=args.norm_order)
 
 
 if __name__ == "__main__":

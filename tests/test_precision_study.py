@@ -19,20 +19,22 @@ from oracle import rmt_oracle as orc
 import precision_study as ps
 
 
+@pytest.mark.parametrize("norm_order", ps.NORM_ORDERS)
 @pytest.mark.parametrize("cfg", [ri.TINY_LLAMA, ri.TINY_LLAMA_HD128], ids=lambda c: c.name)
-def test_unrounded_emulation_is_the_oracle_cell(cfg):
+def test_unrounded_emulation_is_the_oracle_cell(cfg, norm_order):
     """No point rounded: the oracle's cell, up to fp32 evaluation order (the
-    emulation forms exponentials in base 2 from prescaled Q, as the GPU does)."""
+    emulation forms exponentials in base 2 from prescaled Q, as the GPU does,
+    and, in the GPU's order, applies 1/rms to the GEMM's product rows)."""
     c1 = dataclasses.replace(cfg, L=1, S=1)
     w = [{k: np.asarray(v, np.float32) for k, v in d.items()} for d in ri.all_weights(c1)]
     tok, mem0, emb = ri.tokens(c1), ri.initial_memory(c1), ri.embedding(c1)
     A = np.concatenate([mem0[0], emb[tok]])
-    y_em = ps.emulated_llama_cell(A, w[0], c1, points=())
+    y_em = ps.emulated_llama_cell(A, w[0], c1, points=(), norm_order=norm_order)
     y_or = orc.cell_llama(A, w[0], c1.Hq, c1.Hkv, c1.hd, c1.eps, c1.theta)
     err = np.max(np.abs(y_em - y_or)) / np.max(np.abs(y_or))
     assert err < 2e-6, err
     # and the sweep over the whole tiny grid
-    h_em, m_em = ps.sweep(c1, w, tok, mem0, emb, 1)
+    h_em, m_em = ps.sweep(c1, w, tok, mem0, emb, 1, norm_order=norm_order)
     h_or, m_or = orc.forward_sequential(c1, w, tok, mem0, emb)
     assert ps.rel_l2(h_em, h_or) < 2e-6 and ps.rel_l2(m_em, m_or) < 2e-6
 
