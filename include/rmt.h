@@ -179,7 +179,10 @@ int32_t rmt_diag_schedule(int32_t L, int32_t S, int32_t* diag_ptr, int32_t* cell
  * device work (both come with rmt_model_bind).
  * Errors: RMT_EINVAL (bad sizes or NULL weights the cell needs),
  * RMT_EUNSUPPORTED (Hq/Hkv not 1, 2 or a multiple of 4, an ENCODER with
- * n_kv_heads != n_heads, hd not 64/128, widths not multiples of 64, ...). */
+ * n_kv_heads != n_heads, hd not 64/128, widths not multiples of 64, a LLAMA
+ * cell whose m is not a multiple of 8 -- its QKV product reads the memory
+ * rows and the segment rows from separate buffers in whole 8-row loads --,
+ * ...). */
 int32_t rmt_model_create(const rmt_config* cfg, const rmt_weights* w, void* stream,
                          rmt_model** out);
 

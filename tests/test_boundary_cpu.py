@@ -288,3 +288,18 @@ def test_wrapper_grouped_gemm_layer_range():
         rmt.grouped_gemm(A, B, [0, 3], Cm)
     with pytest.raises(ValueError, match="entries"):
         rmt.grouped_gemm(A, B, [0], Cm)
+
+
+def test_llama_memory_rows_must_be_whole_loads():
+    """The LLaMA cell's QKV product reads the memory rows and the segment
+    rows from separate buffers in 8-row loads: m must be a multiple of 8."""
+    L = _L()
+    bad = dataclasses.replace(ri.TINY_LLAMA, m=36)
+    c = _config(bad)
+    w = _fake_weights(bad)
+    h = C.c_void_p()
+    assert L.lib().rmt_model_create(C.byref(c), C.byref(w), None, C.byref(h)) == L.RMT_EUNSUPPORTED
+    assert b"multiple of 8" in L.lib().rmt_last_error()
+    ok = dataclasses.replace(ri.TINY_LLAMA, m=32)
+    h = _create(ok)
+    L.lib().rmt_model_destroy(h)
