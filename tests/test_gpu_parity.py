@@ -178,6 +178,37 @@ def test_llama1b_full_length_teacher_forced():
 
 
 @pytest.mark.timeout(900)
+def test_llama1b_drawn_gains_teacher_forced():
+    """The 1B-shaped LLaMA sweep with RMSNorm gains 1 + N(0, 0.1^2) per layer
+    and column (the workload's own gains are 1).  Segment 64's cells all sit
+    on full diagonals (16 cells per launch, the 288-row GEMM tiles), where the
+    residual epilogues write each output row's next RMSNorm operand y * gamma
+    with the gain of the cell that reads it: gamma1 of layer l+1 for X(l, s),
+    of layer l for M(l, s).  A swapped or misplaced gain changes the result
+    there, which unit gains cannot show.  Checked teacher-forced (the oracle
+    computes segment s from the GPU's own M(., s-1)) at segments 0 (ramp
+    diagonals) and 64, and diagonal == sequential bitwise."""
+    cfg = dataclasses.replace(ri.LLAMA_1B, name="llama1b_gains_rmt_L16_S128", gain_std=0.1)
+    gu.say(f"[parity] {cfg.name} full length S={cfg.S}, drawn RMSNorm gains: teacher-forced segments")
+    run = gu.GpuRun(cfg)
+    g1 = np.stack([w["g1"] for w in run.layers])
+    assert np.std(g1) > 0.05 and not np.allclose(g1[0], g1[1])
+    hd, md = run.run("diagonal")
+    hs, ms = run.run("sequential")
+    assert np.array_equal(hd, hs) and np.array_equal(md, ms)
+    n = cfg.n
+    for s in (0, 64):
+        m_in = _gpu_state_after(run, s)
+        m_out = _gpu_state_after(run, s + 1)
+        h_o, m_o = orc.forward_sequential(cfg, run.layers, run.x[s * n:(s + 1) * n], m_in, run.embed)
+        e_h = gu.rel_l2(hd[s * n:(s + 1) * n], h_o)
+        e_m = gu.rel_l2(m_out, m_o)
+        gu.say(f"  segment {s}: rel L2 hidden {e_h:.3e} mem {e_m:.3e}")
+        assert e_h <= BF16_TOL and e_m <= BF16_TOL
+    run.close()
+
+
+@pytest.mark.timeout(900)
 def test_encoder1b_full_length_teacher_forced():
     """The encoder-layer workload over the full 131,072 tokens: diagonal ==
     sequential bitwise, and segments across the run checked one step at a
