@@ -603,9 +603,29 @@ __global__ __launch_bounds__((BM / WTM) * (BN / WTN) * 64, 1) void gemm_bf16_ker
     const int lr = lane >> 3;
     const int lc = 4 * (lane & 7);
     auto paired = [&](int i, int t, int t2) __attribute__((always_inline)) {
-      lds_sync();
       const int col = wcol0 + t * 32 + lc;     // column of the first block's values
       const int col2 = wcol0 + t2 * 32 + lc;   // column of the second block's values
+      // A rotation pair lies in one head, which is wholly rotated (Q, K) or
+      // not (V), and wholly Q or not: both tests are wave-uniform.
+      const bool rot = wcol0 + t * 32 < a.rope_cols;
+      const bool isq = wcol0 + t * 32 < a.q_cols;
+      // RoPE, rotate-half: column c < hd/2 of a head pairs with c + hd/2.  The
+      // (cos, sin) pairs of the lane's four rows are requested before any of
+      // the piece's stores: the compiler cannot tell the table from the
+      // output, and would otherwise hold each row's loads behind the previous
+      // row's stores, one memory round trip per row.  Rows past M read the
+      // last valid row and store nothing.
+      float2 cs[4][4];
+      if (rot) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int row = min(wrow0 + i * 32 + 8 * j + lr, a.M - 1);
+          const float2* src = a.rope + (size_t)row * (a.hd >> 1) + col % a.hd;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) cs[j][e] = src[e];
+        }
+      }
+      lds_sync();
       uint16_t* C = (uint16_t*)tab.out_lo[g];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -615,19 +635,17 @@ __global__ __launch_bounds__((BM / WTM) * (BN / WTN) * 64, 1) void gemm_bf16_ker
         f32x4 x2 = *(const f32x4*)(ep + r * EP_LD + 32 + lc);
         if (row >= a.M || col >= a.N) continue;
         {
-          // RoPE, rotate-half: column c < hd/2 of a head pairs with c + hd/2.
-          if (col < a.rope_cols) {
-            const float2* cs = a.rope + (size_t)row * (a.hd >> 1) + col % a.hd;
+          if (rot) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              const float2 c = cs[e];
+              const float2 c = cs[j][e];
               const float y1 = x1[e] * c.x - x2[e] * c.y;
               const float y2 = x2[e] * c.x + x1[e] * c.y;
               x1[e] = y1;
               x2[e] = y2;
             }
           }
-          if (col < a.q_cols) {   // Q: the attention scale (a rotation pair is wholly Q or not)
+          if (isq) {   // Q: the attention scale
             x1 *= a.q_scale;
             x2 *= a.q_scale;
           }
