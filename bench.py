@@ -100,24 +100,6 @@ def measured_traffic():
         return None
 
 
-def smi_snapshot():
-    """Product name and current clocks of the first GPU from rocm-smi (a child
-    process, after the timed region), or None when the tool is unavailable."""
-    import json
-    import subprocess
-    try:
-        r = subprocess.run(["rocm-smi", "--showproductname", "--showclocks", "--json"],
-                           capture_output=True, text=True, timeout=20)
-        data = json.loads(r.stdout)
-    except (OSError, ValueError, subprocess.SubprocessError):
-        return None
-    card = next((v for k, v in sorted(data.items()) if k.startswith("card")), None)
-    if not isinstance(card, dict):
-        return None
-    keep = ("series", "model", "sku", "sclk", "mclk", "fclk", "socclk")
-    return {k: v for k, v in card.items() if any(w in k.lower() for w in keep)} or None
-
-
 def timed_steps(fn, steps, stream):
     import torch
     torch.cuda.synchronize()
@@ -362,7 +344,7 @@ def main():
     props = torch.cuda.get_device_properties(0)
     device = {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
               "compute_units": props.multi_processor_count,
-              "hbm_gib": round(props.total_memory / 2**30, 1), "smi": smi_snapshot()}
+              "hbm_gib": round(props.total_memory / 2**30, 1)}
     if B > 1:
         config["sequences"] = B
     if llama:
