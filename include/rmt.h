@@ -187,7 +187,10 @@ int32_t rmt_model_create(const rmt_config* cfg, const rmt_weights* w, void* stre
                          rmt_model** out);
 
 /* Caller-owned device buffers of a model.
- *   RMT_BUF_WEIGHTS    the packed weights ([L][N][K] bf16, K contiguous),
+ *   RMT_BUF_WEIGHTS    the packed weights ([L][N][K] bf16, K contiguous; for
+ *                      128-wide heads the Q and K rows of each head are
+ *                      grouped by RoPE rotation pair, which leaves the
+ *                      attention unchanged),
  *                      gains, shifts and biases, the RoPE table and the
  *                      bad-token flag: fixed by the config, independent of S
  *                      and of the batch.

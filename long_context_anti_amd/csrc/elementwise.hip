@@ -282,13 +282,13 @@ __global__ __launch_bounds__(256) void linear_gelu_f32_kernel(int R, int d, int 
 }
 
 // dst[l][r][k] (bf16, or fp16 with DST_F16) from src[l][k][col(r)] through a
-// 64 x 64 LDS tile.
+// 64 x 64 LDS tile; col(r) per mode (see launch_pack).
 template <bool SRC_BF16, bool DST_F16>
 __global__ __launch_bounds__(256) void pack_kernel(int K, int N_src, const void* __restrict__ src0,
-                                                   const void* __restrict__ src1, int interleave,
+                                                   const void* __restrict__ src1, int mode, int pair_cols,
                                                    uint16_t* __restrict__ dst) {
   __shared__ uint16_t tile[64][65];
-  const int N_dst = interleave ? 2 * N_src : N_src;
+  const int N_dst = mode == PACK_GATE_UP ? 2 * N_src : N_src;
   const int r0 = (int)blockIdx.x * 64;
   const int k0 = (int)blockIdx.y * 64;
   const int l = (int)blockIdx.z;
@@ -298,10 +298,16 @@ __global__ __launch_bounds__(256) void pack_kernel(int K, int N_src, const void*
   const int r = r0 + tx;
   int col = r;
   const void* src = src0;
-  if (interleave) {
+  if (mode == PACK_GATE_UP) {
     const int blk = r >> 6, j = r & 63;
     col = blk * 32 + (j & 31);
     src = j < 32 ? src0 : src1;
+  } else if (mode == PACK_ROPE_PAIRS && r < pair_cols) {
+    // 128-wide head h, position p: the 64-column group q = p / 64 holds the
+    // head's rotation pairs 32 q .. 32 q + 31, first elements (dimensions
+    // 32 q + w) then second elements (64 + 32 q + w)
+    const int h = r >> 7, p = r & 127, q = p >> 6, w = p & 63;
+    col = h * 128 + (w < 32 ? 32 * q + w : 64 + 32 * q + (w - 32));
   }
   for (int i = ty; i < 64; i += 4) {
     const int k = k0 + i;
@@ -424,12 +430,15 @@ hipError_t launch_linear_gelu_f32(int G, int R, int d, int split_in, int split_o
 }
 
 hipError_t launch_pack(int L, int K, int N_src, const void* src0, const void* src1,
-                       int src_is_bf16, int interleave, uint16_t* dst, hipStream_t stream,
-                       int dst_f16) {
-  const int N_dst = interleave ? 2 * N_src : N_src;
+                       int src_is_bf16, int mode, uint16_t* dst, hipStream_t stream,
+                       int dst_f16, int pair_cols) {
+  if (mode != PACK_PLAIN && mode != PACK_GATE_UP && mode != PACK_ROPE_PAIRS) return hipErrorInvalidValue;
+  if (mode == PACK_ROPE_PAIRS && (pair_cols < 0 || pair_cols % 128 != 0 || pair_cols > N_src))
+    return hipErrorInvalidValue;
+  const int N_dst = mode == PACK_GATE_UP ? 2 * N_src : N_src;
   dim3 grid((N_dst + 63) / 64, (K + 63) / 64, L);
   auto go = [&](auto kern) {
-    hipLaunchKernelGGL(kern, grid, dim3(256), 0, stream, K, N_src, src0, src1, interleave, dst);
+    hipLaunchKernelGGL(kern, grid, dim3(256), 0, stream, K, N_src, src0, src1, mode, pair_cols, dst);
   };
   if (src_is_bf16) {
     if (dst_f16) go(pack_kernel<true, true>);

@@ -609,7 +609,9 @@ __global__ __launch_bounds__((BM / WTM) * (BN / WTN) * 64, 1) void gemm_bf16_ker
       // not (V), and wholly Q or not: both tests are wave-uniform.
       const bool rot = wcol0 + t * 32 < a.rope_cols;
       const bool isq = wcol0 + t * 32 < a.q_cols;
-      // RoPE, rotate-half: column c < hd/2 of a head pairs with c + hd/2.  The
+      // RoPE, rotate-half, over 64-column groups: column c < 32 of a group
+      // pairs with c + 32, at frequency index 32 ((col % hd) / 64) + col % 32
+      // (a 64-wide head is one group; a 128-wide head is packed as two).  The
       // (cos, sin) pairs of the lane's four rows are requested before any of
       // the piece's stores: the compiler cannot tell the table from the
       // output, and would otherwise hold each row's loads behind the previous
@@ -620,7 +622,7 @@ __global__ __launch_bounds__((BM / WTM) * (BN / WTN) * 64, 1) void gemm_bf16_ker
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int row = min(wrow0 + i * 32 + 8 * j + lr, a.M - 1);
-          const float2* src = a.rope + (size_t)row * (a.hd >> 1) + col % a.hd;
+          const float2* src = a.rope + (size_t)row * (a.hd >> 1) + 32 * ((col % a.hd) >> 6) + (col & 31);
 #pragma unroll
           for (int e = 0; e < 4; ++e) cs[j][e] = src[e];
         }
@@ -702,27 +704,17 @@ __global__ __launch_bounds__((BM / WTM) * (BN / WTN) * 64, 1) void gemm_bf16_ker
             if (row < a.M && ocol < out_cols) *(u32x4*)(C + (size_t)row * a.ld_out + ocol) = v;
           }
         }
-    } else {  // EPI_QKV_ROPE: the wave's columns start on a head boundary
-      // (WTN is a multiple of hd), so block t pairs with t + P, P = hd / 64.
-      auto rope_pieces = [&](auto pc) __attribute__((always_inline)) {
-        constexpr int P = decltype(pc)::value;
-        static_assert(NI % (2 * P) == 0, "heads must not straddle a wave's columns");
+    } else {  // EPI_QKV_ROPE: the wave's columns start on a 64-column group
+      // boundary (WTN is a multiple of 64), so block t pairs with t + 1.
+      static_assert(NI % 2 == 0, "rotation groups must not straddle a wave's columns");
 #pragma unroll
-        for (int i = 0; i < MI; ++i)
+      for (int i = 0; i < MI; ++i)
 #pragma unroll
-          for (int t = 0; t < NI; ++t) {
-            if ((t / P) % 2 != 0) continue;
-            stage(acc[i][t], 0);
-            stage(acc[i][t + P], 1);
-            paired(i, t, t + P);
-          }
-      };
-      if constexpr (WTN >= 128) {
-        if (a.hd == 128) rope_pieces(std::integral_constant<int, 2>{});
-        else rope_pieces(std::integral_constant<int, 1>{});
-      } else {
-        rope_pieces(std::integral_constant<int, 1>{});
-      }
+        for (int t = 0; t < NI; t += 2) {
+          stage(acc[i][t], 0);
+          stage(acc[i][t + 1], 1);
+          paired(i, t, t + 1);
+        }
     }
   }
 }
@@ -755,10 +747,9 @@ void launch_one(const GemmArgs& a, const GroupTable& tab, const NormAux& aux, hi
 //              exactly four tiles.                              speed 1.00
 //   256 x 256: eight waves of 64 x 128 (2 x 4 blocks).           speed 0.95
 //   192 x 256: eight waves of 96 x 64 (3 x 2 blocks).            speed 0.85
-//   128 x 256: eight waves of 64 x 64; 32 x 128 for RoPE over
-//              128-wide heads.                                  speed 0.72
-// RoPE needs both halves of a head in one wave's columns, so 128-wide heads
-// exclude the 64-column waves of the 288- and 192-row shapes.  Every shape uses the
+//   128 x 256: eight waves of 64 x 64.                          speed 0.72
+// RoPE rotates within 64-column groups (128-wide heads are packed as two
+// such groups), so every shape serves the QKV product.  Every shape uses the
 // same K slicing and lane/k assignment, so a cell's result does not depend on
 // the choice.
 int num_cus() {
@@ -780,10 +771,9 @@ double tile_cost(const GemmArgs& a, int G, int bm, double speed) {
 
 template <int EPI, bool F16>
 void launch_epi(const GemmArgs& a, const GroupTable& tab, const NormAux& aux, hipStream_t stream) {
-  const bool wide_heads = EPI == EPI_QKV_ROPE && a.hd == 128;
-  const double c288 = wide_heads ? 1e300 : tile_cost(a, tab.G, 288, 1.00);
+  const double c288 = tile_cost(a, tab.G, 288, 1.00);
   const double c256 = tile_cost(a, tab.G, 256, 0.95);
-  const double c192 = wide_heads ? 1e300 : tile_cost(a, tab.G, 192, 0.85);
+  const double c192 = tile_cost(a, tab.G, 192, 0.85);
   const double c128 = tile_cost(a, tab.G, 128, 0.72);
   if (c288 <= c256 && c288 <= c192 && c288 <= c128) {
     launch_one<EPI, F16, 288, 96, 64>(a, tab, aux, stream);
@@ -791,8 +781,6 @@ void launch_epi(const GemmArgs& a, const GroupTable& tab, const NormAux& aux, hi
     launch_one<EPI, F16, 256, 64, 128>(a, tab, aux, stream);
   } else if (c192 <= c128) {
     launch_one<EPI, F16, 192, 96, 64>(a, tab, aux, stream);
-  } else if (wide_heads) {
-    launch_one<EPI, F16, 128, 32, 128>(a, tab, aux, stream);
   } else {
     launch_one<EPI, F16, 128, 64, 64>(a, tab, aux, stream);
   }
@@ -807,6 +795,8 @@ hipError_t launch_gemm(int epilogue, const GemmArgs& a, const GroupTable& tab, h
                            epilogue == EPI_BIAS_RELU_BF16;
   if (plain_store && a.N % 8 != 0) return hipErrorInvalidValue;   // whole 16-byte output chunks
   if (a.q_cols < 0 || a.q_cols % 32 != 0) return hipErrorInvalidValue;   // whole 32-column blocks
+  if (epilogue == EPI_QKV_ROPE && (a.rope_cols < 0 || a.rope_cols % 64 != 0 || (a.hd != 64 && a.hd != 128)))
+    return hipErrorInvalidValue;   // whole 64-column rotation groups
   if (a.a_split < 0 || a.a_split % 8 != 0 || (a.a_split > 0 && epilogue != EPI_QKV_ROPE))
     return hipErrorInvalidValue;   // whole 8-row loads on each side of the split
   const bool resid = epilogue == EPI_RESID_F32 || epilogue == EPI_RESID_BIAS_F32 || epilogue == EPI_RESID_NORM_F32;

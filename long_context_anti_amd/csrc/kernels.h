@@ -70,7 +70,9 @@ struct GemmArgs {
   int ld_res;          // residual row stride (elements)
   int ld_out;          // output row stride (elements)
   const float2* rope;  // EPI_QKV_ROPE: (cos, sin) table [M][hd/2]
-  int rope_cols;       // EPI_QKV_ROPE: columns [0, rope_cols) are rotated
+  int rope_cols;       // EPI_QKV_ROPE: columns [0, rope_cols) are rotated, in 64-column
+                       //   groups whose column c < 32 pairs with c + 32, at frequency index
+                       //   32 ((col % hd) / 64) + col % 32 (PACK_ROPE_PAIRS order for hd 128)
   int hd;              // EPI_QKV_ROPE: head dimension (64 or 128)
   const float* bias;   // EPI_*BIAS*: fp32 [Lw][N], row layer[g] added to every output row
   int q_cols;          // EPI_QKV_ROPE, EPI_BIAS_BF16: columns [0, q_cols) (a multiple of 32)
@@ -152,11 +154,20 @@ hipError_t launch_linear_gelu_f32(int G, int R, int d, int split_in, int split_o
 
 // Weight packing: dst[l][r][k] = src_sel(r)[l][k][col(r)] as bf16, or as fp16
 // when dst_f16 is set (from fp32 or bf16, rounded to nearest even).
-// interleave == 0: dst row r <- src0 column r (N_dst = N_src).
-// interleave == 1: dst row r in block r/64: first 32 rows <- src0 columns,
+// PACK_PLAIN:      dst row r <- src0 column r (N_dst = N_src).
+// PACK_GATE_UP:    dst row r in block r/64: first 32 rows <- src0 columns,
 //                  last 32 rows <- src1 columns (N_dst = 2 N_src).
+// PACK_ROPE_PAIRS: as PACK_PLAIN, except that the first pair_cols rows (a
+//                  multiple of 128: the Q and K heads of 128) are reordered
+//                  within each head into two 64-row groups, group q holding
+//                  the dimensions 32 q .. 32 q + 31 and then 64 + 32 q ..
+//                  64 + 32 q + 31: every rotation pair of RoPE (d, d + 64)
+//                  then sits 32 rows apart inside one group, as it does in a
+//                  64-wide head.  Q and K take the same order, so their dot
+//                  products, and the attention, are unchanged.
+enum PackMode : int { PACK_PLAIN = 0, PACK_GATE_UP = 1, PACK_ROPE_PAIRS = 2 };
 hipError_t launch_pack(int L, int K, int N_src, const void* src0, const void* src1,
-                       int src_is_bf16, int interleave, uint16_t* dst, hipStream_t stream,
-                       int dst_f16 = 0);
+                       int src_is_bf16, int mode, uint16_t* dst, hipStream_t stream,
+                       int dst_f16 = 0, int pair_cols = 0);
 
 }  // namespace rmt

@@ -652,10 +652,10 @@ int32_t pack_weights(rmt_model* M) {
     HIP_TRY(hipMemcpyAsync(M->b32, w->b, (size_t)L * d * 4, hipMemcpyDeviceToDevice, st));
   } else if (c.cell == RMT_CELL_ENCODER) {
     const int bf = w->weight_dtype == RMT_BF16;
-    HIP_TRY(launch_pack(L, d, (int)F, w->w1, nullptr, bf, 0, M->wgu, st));
-    HIP_TRY(launch_pack(L, (int)F, d, w->w2, nullptr, bf, 0, M->wd, st));
-    HIP_TRY(launch_pack(L, d, (int)NQ, w->wqkv, nullptr, bf, 0, M->wqkv, st));
-    HIP_TRY(launch_pack(L, (int)HQD, d, w->wo, nullptr, bf, 0, M->wo, st));
+    HIP_TRY(launch_pack(L, d, (int)F, w->w1, nullptr, bf, PACK_PLAIN, M->wgu, st));
+    HIP_TRY(launch_pack(L, (int)F, d, w->w2, nullptr, bf, PACK_PLAIN, M->wd, st));
+    HIP_TRY(launch_pack(L, d, (int)NQ, w->wqkv, nullptr, bf, PACK_PLAIN, M->wqkv, st));
+    HIP_TRY(launch_pack(L, (int)HQD, d, w->wo, nullptr, bf, PACK_PLAIN, M->wo, st));
     const size_t Ld4 = (size_t)L * d * 4;
     HIP_TRY(hipMemcpyAsync(M->g1, w->g1, Ld4, hipMemcpyDeviceToDevice, st));
     HIP_TRY(hipMemcpyAsync(M->beta1, w->beta1, Ld4, hipMemcpyDeviceToDevice, st));
@@ -668,12 +668,16 @@ int32_t pack_weights(rmt_model* M) {
   } else {
     const int bf = w->weight_dtype == RMT_BF16;
     const int f16 = c.dtype == RMT_F16;   // operands packed as fp16
-    HIP_TRY(launch_pack(L, d, (int)F, w->wg, w->wu, bf, 1, M->wgu, st, f16));
-    HIP_TRY(launch_pack(L, (int)F, d, w->wd, nullptr, bf, 0, M->wd, st, f16));
+    HIP_TRY(launch_pack(L, d, (int)F, w->wg, w->wu, bf, PACK_GATE_UP, M->wgu, st, f16));
+    HIP_TRY(launch_pack(L, (int)F, d, w->wd, nullptr, bf, PACK_PLAIN, M->wd, st, f16));
     HIP_TRY(hipMemcpyAsync(M->g2, w->g2, (size_t)L * d * 4, hipMemcpyDeviceToDevice, st));
     if (c.cell == RMT_CELL_LLAMA) {
-      HIP_TRY(launch_pack(L, d, (int)NQ, w->wqkv, nullptr, bf, 0, M->wqkv, st, f16));
-      HIP_TRY(launch_pack(L, (int)HQD, d, w->wo, nullptr, bf, 0, M->wo, st, f16));
+      // 128-wide heads: Q and K columns in rotation-pair groups of 64, so that
+      // the QKV epilogue rotates within any 64-column wave tile
+      const int rot = (c.n_heads + c.n_kv_heads) * c.head_dim;
+      HIP_TRY(launch_pack(L, d, (int)NQ, w->wqkv, nullptr, bf, c.head_dim == 128 ? PACK_ROPE_PAIRS : PACK_PLAIN,
+                          M->wqkv, st, f16, c.head_dim == 128 ? rot : 0));
+      HIP_TRY(launch_pack(L, (int)HQD, d, w->wo, nullptr, bf, PACK_PLAIN, M->wo, st, f16));
       HIP_TRY(hipMemcpyAsync(M->g1, w->g1, (size_t)L * d * 4, hipMemcpyDeviceToDevice, st));
       // RoPE table: angle p * theta^(-2i/hd) in double precision.
       const int half = c.head_dim / 2;
@@ -1081,7 +1085,7 @@ int32_t rmt_pack_weight(int32_t L, int32_t K, int32_t N, const void* src, int32_
     return fail(RMT_EINVAL, "need L >= 1 and positive K, N that are multiples of 8");
   if (!src || !dst) return fail(RMT_EINVAL, "src and dst must be non-NULL");
   if (src_dtype != RMT_F32 && src_dtype != RMT_BF16) return fail(RMT_EINVAL, "bad src_dtype");
-  HIP_TRY(launch_pack(L, K, N, src, nullptr, src_dtype == RMT_BF16, 0, (uint16_t*)dst,
+  HIP_TRY(launch_pack(L, K, N, src, nullptr, src_dtype == RMT_BF16, PACK_PLAIN, (uint16_t*)dst,
                       (hipStream_t)stream));
   return RMT_OK;
 }
