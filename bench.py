@@ -10,7 +10,8 @@ whole sequence with inputs already in HBM.  Alongside: the same GPU's
 sequential per-cell path, per-stage GPU times (HIP events recorded on the
 library's stream between launches), the grouped-GEMM fraction of the MI355X
 bf16 dense MFMA peak, the isolated 1152 x 2048 x 8192 grouped GEMM at
-G = 1, 4, 8, 16, and the CPU oracle timed on a prefix of the sequence.
+G = 1, 4, 8, 16, the CPU oracle timed on a prefix of the sequence, and (as
+`secondary`) the 8B-shaped RMT with fp16 operands, one timed step.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu] [--no-seq]
                     [--workload llama1b|llama8b|norm_swiglu_1b|encoder1b] [--dtype bf16|f16]
@@ -156,6 +157,57 @@ def gemm_sweep(steps=20):
     return out
 
 
+def secondary_llama8b(steps=1, warmup=1):
+    """The LLaMA-8B-shaped workload (32 layers, d = 4096, 2048 + 128 rows, 64
+    segments, 131,072 tokens) with fp16 operands, the precision that meets the
+    2e-2 gate at that depth: tokens/s of the diagonal sweep and the grouped-GEMM
+    stage rates from per-launch events.  No CPU leg, no sequential path."""
+    import torch
+    import long_context_anti_amd as rmt
+    import rmt_inputs as ri
+    from rmt_inputs import device as rdev
+
+    cfg = ri.LLAMA_8B
+    t0 = time.perf_counter()
+    layers = gen_layers(cfg)
+    embed = ri.embedding(cfg)
+    dw = rdev.device_weights(cfg, layers, embed)
+    del layers
+    kw = rdev.model_kwargs(cfg)
+    kw["dtype"] = rmt.RMT_F16
+    model = rmt.RMTModel(**kw, weights=dw)
+    tok_d = rdev.segment_inputs(cfg, ri.tokens(cfg, 0))
+    mem0_d = rdev.f32_tensor(ri.initial_memory(cfg, 0))
+    hidden = torch.empty((cfg.T, cfg.d), dtype=torch.float32, device="cuda")
+    mem = torch.empty((cfg.L, cfg.m, cfg.d), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    diag = lambda: model.forward_diagonal(tok_d, mem0_d, hidden, mem)  # noqa: E731
+    for _ in range(warmup):
+        diag()
+    torch.cuda.synchronize()
+    log(f"[bench] {cfg.name} (fp16 operands): ready in {time.perf_counter() - t0:.1f} s")
+    wall, _ = timed_steps(diag, steps, stream)
+    model.enable_timing(True)
+    timed_steps(diag, steps, stream)
+    stages = model.stage_times()
+    model.enable_timing(False)
+    model.close()
+    del dw, model
+    torch.cuda.empty_cache()
+    ms = {"ms": 0.0, "flops": 0.0}
+    for k in ("qkv", "oproj", "gateup", "down"):
+        ms["ms"] += stages[k]["ms"]
+        ms["flops"] += stages[k]["flops"]
+    tf = ms["flops"] / (ms["ms"] / 1e3) / 1e12
+    gu = stages["gateup"]
+    gu_tf = gu["flops"] / (gu["ms"] / 1e3) / 1e12
+    log(f"[bench] {cfg.name}: {wall / steps * 1e3:.1f} ms/step")
+    return {"workload": cfg.name, "dtype": "f16", "value": round(cfg.T * steps / wall, 1), "unit": "tokens/s",
+            "steps": steps, "warmup": warmup, "ms_per_step": round(wall / steps * 1e3, 2),
+            "grouped_gemm_stages": {"tflops": round(tf, 1), "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)},
+            "gateup": {"tflops": round(gu_tf, 1), "frac_bf16_peak": round(gu_tf / PEAK_BF16_TFLOPS, 4)}}
+
+
 def cpu_baseline(cfg, layers, tokens, mem0, embed, gpu_hidden, gpu_mem_prefix_fn, S_prefix):
     """The CPU oracle as it stands, timed on a prefix of S_prefix segments."""
     from threadpoolctl import threadpool_info
@@ -197,6 +249,8 @@ def main():
     ap.add_argument("--dtype", default=None, choices=["bf16", "f16"],
                     help="16-bit operand type of the LLaMA-shaped cell (default: the workload's bf16); "
                          "f16 is the precision that meets the 2e-2 gate at the 8B shape")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="skip the secondary LLaMA-8B-shaped measurement (fp16 operands) of the default run")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy, the reference for HBM byte counters")
     args = ap.parse_args()
@@ -398,6 +452,11 @@ def main():
         log(f"[bench] CPU oracle on {Sp} segments ...")
         result["cpu_baseline"] = cpu_baseline(cfg, layers, tokens, mem0, embed, hidden_np,
                                               gpu_mem_prefix, Sp)
+    model.close()
+    del emb_dev
+    if (not args.no_secondary and args.workload == "llama1b" and B == 1 and not f16
+            and not args.calibrate_copy):
+        result["secondary"] = secondary_llama8b()
     if args.calibrate_copy:
         src = torch.ones(256 * 2**20, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
@@ -405,8 +464,6 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    model.close()
-    del emb_dev
     print(json.dumps(result), flush=True)
 
 
