@@ -1,7 +1,10 @@
-// Row-wise and layout kernels of the diagonal sweep (gfx950): RMSNorm over
-// every cell of a diagonal, the segment-input gather, the fp32 linear+GELU
-// cell, and weight packing.  All of them are HBM-bound; they read and write
-// full 16-byte (or 8-byte) vectors along rows.
+// Row-wise and layout kernels of the diagonal sweep (gfx950): RMSNorm and
+// LayerNorm over every cell of a diagonal, the LLaMA cell's RMSNorm pieces
+// that no GEMM epilogue produces (the side outputs of gathered and initial
+// rows, and 1/rms per row from the chunk sums), the segment-input gather,
+// the fp32 linear+GELU cell, and weight packing.  They are HBM- or
+// latency-bound; they read and write full 16-byte (or 8-byte) vectors along
+// rows.
 #include "kernels.h"
 
 namespace rmt {

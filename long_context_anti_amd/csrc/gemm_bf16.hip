@@ -8,8 +8,10 @@
 // Batching for Recurrent Memory Transformers": one launch covers all cells of
 // a diagonal, whatever their number.
 //
-// Design (measured on MI355X; the operand stream from L2, not the MFMA rate,
-// is what limits this kernel, so tiles are as large as LDS allows):
+// Design (measured on MI355X: the operand traffic through LDS and the
+// per-slice barrier, under the chip's power limit, bound this kernel -- with
+// every operand L2-resident it runs no faster -- so tiles are as large as LDS
+// and the register file allow):
 //   * Output tiles of 288, 256, 192 or 128 rows x 256 columns, chosen per launch
 //     by a cost model of whole rounds of one tile per CU (see launch_epi);
 //     waves compute 32 x 32 blocks with v_mfma_f32_32x32x16_bf16.  A cell
@@ -24,6 +26,12 @@
 //   * Workgroup ids are renumbered so each XCD (ids = x mod 8) receives a
 //     contiguous run of tiles; within a cell the M tile varies fastest, so the
 //     tiles sharing a weight panel run together in one XCD's L2.
+//   * Epilogues fuse what follows each product in the cell: RoPE and the
+//     softmax scale (QKV), SwiGLU (gate/up), biases and ReLU, the fp32
+//     residual add with the split write-back of X and M rows, and for the
+//     LLaMA-shaped cell the next RMSNorm's inputs (the 16-bit copy y * gamma
+//     and 64-column chunk sums of y^2) and the 1/rms row scales of its
+//     consumers.
 //   * Every output element is produced by one lane with the same K order for
 //     every tile shape and every G, so a cell's result does not depend on
 //     which diagonal (or the sequential sweep) it runs in.

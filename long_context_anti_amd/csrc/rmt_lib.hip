@@ -19,6 +19,10 @@
 //     other, so the write-back never lands on rows another tile of the same
 //     launch still reads as its residual, and M(., S-1) ends in out->mem
 //     without a final copy.
+// The LLaMA cell's RMSNorm inputs (16-bit copies y * gamma and chunk sums of
+// y^2, written by whoever produces the rows) travel with their rows: X
+// copies in slot l+1 of the X buffer being written, M copies in the memory
+// buffer of M's parity, so the same two facts cover them.
 // With B sequences (rmt_model_set_batch) every sequence has its own X
 // ping-pong pair and memory buffers, and a diagonal's launches cover the
 // cells of all B sequences (layer-major, sequence fastest, so cells of one
