@@ -100,7 +100,11 @@ def _both(cfg, S=None):
     return out
 
 
-@pytest.mark.parametrize("cfg", [ri.TINY_LLAMA, ri.TINY_LLAMA_HD128, TINY_GQA2], ids=lambda c: c.name)
+TINY_MHA_HD128 = dataclasses.replace(ri.TINY_LLAMA_HD128, name="tiny_llama_mha_hd128", wid=33, Hkv=4)
+
+
+@pytest.mark.parametrize("cfg", [ri.TINY_LLAMA, ri.TINY_LLAMA_HD128, TINY_GQA2, TINY_MHA_HD128],
+                         ids=lambda c: c.name)
 def test_tiny_llama_f16(cfg):
     gu.say(f"[f16] {cfg.name}")
     e = _both(cfg)

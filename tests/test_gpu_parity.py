@@ -39,9 +39,17 @@ def test_linear_gelu_fp32():
 
 
 TINY_GQA2 = dataclasses.replace(ri.TINY_LLAMA, name="tiny_llama_gqa2", wid=32, Hq=4, Hkv=2)
+# Head layouts around the packed rotation-pair order of 128-wide heads and the
+# attention's workgroup mapping: one query head per KV head (MHA) and two at
+# hd = 128 (every K head reordered like the Q heads), eight at hd = 64 (two
+# workgroups per KV head).
+TINY_MHA_HD128 = dataclasses.replace(ri.TINY_LLAMA_HD128, name="tiny_llama_mha_hd128", wid=33, Hkv=4)
+TINY_GQA2_HD128 = dataclasses.replace(ri.TINY_LLAMA_HD128, name="tiny_llama_gqa2_hd128", wid=34, Hkv=2)
+TINY_GQA8 = dataclasses.replace(ri.TINY_LLAMA, name="tiny_llama_gqa8", wid=35, d=512, Hq=8, Hkv=1)
 
 
 @pytest.mark.parametrize("cfg", [ri.TINY_SWIGLU, ri.TINY_LLAMA, ri.TINY_LLAMA_HD128, TINY_GQA2,
+                                 TINY_MHA_HD128, TINY_GQA2_HD128, TINY_GQA8,
                                  ri.TINY_ENCODER, ri.TINY_ENCODER_HD128, ri.TINY_ENCODER_POSTNORM,
                                  ri.TINY_ENCODER_POSTNORM_HD128, ri.TINY_ENCODER_WIDE,
                                  ri.TINY_ENCODER_WIDE_POSTNORM],
