@@ -185,6 +185,24 @@ def test_llama1b_full_length_teacher_forced():
     run.close()
 
 
+@pytest.mark.timeout(300)
+def test_llama1b_repeat_bitwise():
+    """Run-to-run determinism at full size: three diagonal sweeps of the whole
+    131,072-token LLaMA-1B-shaped sequence (every kernel, every tile shape of
+    the ramps and full diagonals, the LDS-staged epilogues) give bitwise the
+    same hidden rows and memory.  A race between waves or workgroups would
+    show here first."""
+    cfg = ri.LLAMA_1B
+    gu.say(f"[parity] {cfg.name}: three full-length diagonal sweeps, bitwise")
+    run = gu.GpuRun(cfg)
+    h0, m0 = run.run("diagonal")
+    for _ in range(2):
+        h1, m1 = run.run("diagonal")
+        assert np.array_equal(h0, h1) and np.array_equal(m0, m1)
+    assert np.isfinite(h0).all() and np.isfinite(m0).all()
+    run.close()
+
+
 @pytest.mark.timeout(900)
 def test_llama1b_drawn_gains_teacher_forced():
     """The 1B-shaped LLaMA sweep with RMSNorm gains 1 + N(0, 0.1^2) per layer
