@@ -120,15 +120,13 @@ def test_bf16_teacher_forced_segment_1(runs8b, inputs8b):
     assert e_h <= TOL and e_m <= TOL
 
 
-@pytest.mark.timeout(1200)
-def test_bf16_full_length_teacher_forced(runs8b, inputs8b):
+def _full_length_teacher_forced(run, inputs8b, label):
     """The full 131,072-token sequence (64 segments, ramps of 31 diagonals at
     each end): diagonal == sequential bitwise, and the last segment checked
     one step at a time from the GPU's own state, within 2e-2."""
     import torch
     layers, tok, _, embed = inputs8b
-    run = runs8b[BF16]
-    gu.say(f"[8b] bf16 full length S={CFG.S}")
+    gu.say(f"[8b] {label} full length S={CFG.S}")
     hd, md = run.run("diagonal")
     hs, ms = run.run("sequential")
     assert np.array_equal(hd, hs) and np.array_equal(md, ms)
@@ -145,3 +143,15 @@ def test_bf16_full_length_teacher_forced(runs8b, inputs8b):
     e_h, e_m = gu.rel_l2(hd[s * n:], h_o), gu.rel_l2(md, m_o)
     gu.say(f"  segment {s} (teacher-forced): rel L2 hidden {e_h:.3e} mem {e_m:.3e}")
     assert e_h <= TOL and e_m <= TOL
+
+
+@pytest.mark.timeout(1200)
+def test_bf16_full_length_teacher_forced(runs8b, inputs8b):
+    _full_length_teacher_forced(runs8b[BF16], inputs8b, "bf16")
+
+
+@pytest.mark.timeout(1200)
+def test_f16_full_length_teacher_forced(runs8b, inputs8b):
+    """fp16 operands, the configuration that meets the gate at this depth,
+    over the whole sweep as well."""
+    _full_length_teacher_forced(runs8b[F16], inputs8b, "fp16")
