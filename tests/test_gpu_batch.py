@@ -106,3 +106,46 @@ def test_full_width_batch_fills_the_largest_launch(B):
         assert np.array_equal(mb[b], singles[b][1][0]), f"memory of sequence {b}"
         assert np.isfinite(hb[b]).all()
     model.close()
+
+
+@pytest.mark.timeout(900)
+def test_batch_outputs_past_int32_offsets():
+    """The LLaMA-1B-shaped workload at full length (128 segments, 131,072
+    tokens) with B = 9: the hidden output holds 9 x 131,072 x 2,048 = 2.42e9
+    elements, and sequence 8 starts at element 2^31, past INT32_MAX.  Its
+    hidden states and memory, and those of sequence 0, equal their own B = 1
+    runs bit for bit, and no element of the batched outputs is left unwritten
+    (compared on the device: the batched hidden states alone are 9.7 GB)."""
+    import torch
+    import long_context_anti_amd as rmt
+    cfg, B = ri.LLAMA_1B, 9
+    T = cfg.S * cfg.n
+    assert (B - 1) * T * cfg.d > 2**31 - 1     # INT32_MAX
+    gu.say(f"[batch] {cfg.name} full length B={B}")
+    layers = ri.all_weights(cfg, 0, workers=8)
+    embed = ri.embedding(cfg, 0)
+    xs = [ri.tokens(cfg, 300 + b) for b in range(B)]
+    mems = [ri.initial_memory(cfg, 300 + b) for b in range(B)]
+    dw = rdev.device_weights(cfg, layers, embed)
+    model = rmt.RMTModel(**rdev.model_kwargs(cfg), weights=dw)
+    del dw, layers
+    tok_d = torch.stack([rdev.segment_inputs(cfg, x) for x in xs]).contiguous()
+    mem0_d = rdev.f32_tensor(np.stack(mems))
+    singles = {}
+    for b in (0, B - 1):
+        h = torch.full((1, T, cfg.d), float("nan"), dtype=torch.float32, device="cuda")
+        m = torch.full((1, cfg.L, cfg.m, cfg.d), float("nan"), dtype=torch.float32, device="cuda")
+        model.forward_diagonal(tok_d[b:b + 1].contiguous(), mem0_d[b:b + 1].contiguous(), h, m)
+        torch.cuda.synchronize()
+        singles[b] = (h, m)
+    model.set_batch(B)
+    hb = torch.full((B, T, cfg.d), float("nan"), dtype=torch.float32, device="cuda")
+    mb = torch.full((B, cfg.L, cfg.m, cfg.d), float("nan"), dtype=torch.float32, device="cuda")
+    model.forward_diagonal(tok_d, mem0_d, hb, mb)
+    torch.cuda.synchronize()
+    gu.say("  batched sweep done")
+    for b, (h, m) in singles.items():
+        assert torch.equal(hb[b], h[0]), f"hidden of sequence {b}"
+        assert torch.equal(mb[b], m[0]), f"memory of sequence {b}"
+    assert bool(torch.isfinite(hb).all()) and bool(torch.isfinite(mb).all())
+    model.close()
