@@ -16,7 +16,8 @@ rounded at their point of the dataflow:
   norm2     the same for H, operand of the gate/up product
   u         silu(gate) * up, operand of the down product
 
-to bf16 or to fp16 (round to nearest even).  With no point rounded the cell
+to bf16 or to fp16 (round to nearest even), or to the value of a two-term
+bf16 split (bf16x2: hi + lo, both bf16).  With no point rounded the cell
 equals the oracle's ``cell_llama`` up to fp32 rounding order (pinned by
 ``tests/test_precision_study.py``).  The weights are bf16 values in both
 cases; fp16 holds every one of them exactly except magnitudes below 2^-17
@@ -26,6 +27,7 @@ Run as a script for the full-size tables quoted in the design notes, e.g.
 
     python tests/precision_study.py --workload llama8b --segments 2
     python tests/precision_study.py --workload llama1b --chaos 12
+    python tests/precision_study.py --workload llama8b --segments 2 --split
 
 (minutes of CPU time and tens of GB of memory at the 8B shape).
 """
@@ -57,7 +59,17 @@ def round_fp16(x: np.ndarray) -> np.ndarray:
         return np.asarray(x, np.float32).astype(np.float16).astype(np.float32)
 
 
-ROUND = {"bf16": ri.round_bf16, "fp16": round_fp16}
+def round_bf16x2(x: np.ndarray) -> np.ndarray:
+    """The value of a two-term bf16 split, hi + lo with hi = bf16(x) and
+    lo = bf16(x - hi): what an operand carries when each product is formed
+    from both terms (hi W + lo W, or for Q K^T the three products qh kh +
+    qh kl + ql kh, which drop only the ql kl term), accumulated in fp32."""
+    x = np.asarray(x, np.float32)
+    hi = ri.round_bf16(x)
+    return (hi + ri.round_bf16((x - hi).astype(np.float32))).astype(np.float32)
+
+
+ROUND = {"bf16": ri.round_bf16, "fp16": round_fp16, "bf16x2": round_bf16x2}
 
 
 NORM_ORDERS = ("scaled_after", "normalised")
@@ -65,7 +77,9 @@ NORM_ORDERS = ("scaled_after", "normalised")
 
 def emulated_llama_cell(A: np.ndarray, w: Dict[str, np.ndarray], cfg, points: Iterable[str],
                         fmt: str = "bf16", norm_order: str = "scaled_after") -> np.ndarray:
-    """The pre-norm LLaMA cell in fp32 with the named points rounded to `fmt`.
+    """The pre-norm LLaMA cell in fp32 with the named points rounded to `fmt`
+    (one format for every point, or a dict of per-point formats, bf16 for the
+    points it does not name).
 
     norm_order says where an RMSNorm's 1/rms enters its GEMM, which decides
     what the norm1 / norm2 points round:
@@ -78,10 +92,11 @@ def emulated_llama_cell(A: np.ndarray, w: Dict[str, np.ndarray], cfg, points: It
     unknown = pts - set(POINTS)
     assert not unknown, unknown
     assert norm_order in NORM_ORDERS, norm_order
-    rnd = ROUND[fmt]
+    fmts = fmt if isinstance(fmt, dict) else {}
+    assert set(fmts) <= pts, (fmts, pts)
 
     def at(name, x):
-        return rnd(x) if name in pts else x
+        return ROUND[fmts.get(name, fmt if isinstance(fmt, str) else "bf16")](x) if name in pts else x
 
     def normed_product(name, y, g, Ws):
         """rms_norm(y, g) @ W for each W in Ws, with the rounding point `name`."""
@@ -187,6 +202,18 @@ STANDARD_VARIANTS = (
     + [("all six in fp16", POINTS, "fp16")]
 )
 
+# bf16 everywhere except two-term splits at the largest contributors: the
+# Q/K/V product's A operand (norm1), then Q, K and V (qkv), then the gate/up
+# product's A operand (norm2)
+SPLIT_VARIANTS = (
+    [("all six in bf16", POINTS, "bf16"),
+     ("qkv as hi+lo, rest bf16", POINTS, {"qkv": "bf16x2"}),
+     ("norm1 and qkv as hi+lo, rest bf16", POINTS, {"norm1": "bf16x2", "qkv": "bf16x2"}),
+     ("norm1, qkv, norm2 as hi+lo, rest bf16", POINTS, {"norm1": "bf16x2", "qkv": "bf16x2",
+                                                         "norm2": "bf16x2"}),
+     ("all six in fp16", POINTS, "fp16")]
+)
+
 
 def main():
     ap = argparse.ArgumentParser()
@@ -194,6 +221,8 @@ def main():
     ap.add_argument("--segments", type=int, default=1)
     ap.add_argument("--chaos", type=int, default=0, help="segments of the perturbation study instead")
     ap.add_argument("--quick", action="store_true", help="only all-bf16 and all-fp16")
+    ap.add_argument("--split", action="store_true",
+                    help="two-term bf16 splits at the largest contributors instead")
     ap.add_argument("--norm-order", default="scaled_after", choices=NORM_ORDERS,
                     help="where 1/rms enters the GEMMs after the RMSNorms (what norm1/norm2 round)")
     args = ap.parse_args()
@@ -203,6 +232,8 @@ def main():
         chaos_growth(cfg, args.chaos, log=lambda m: print(m, flush=True))
         return
     variants = STANDARD_VARIANTS if not args.quick else [STANDARD_VARIANTS[0], STANDARD_VARIANTS[-1]]
+    if args.split:
+        variants = SPLIT_VARIANTS
     print(f"norm order: {args.norm_order}", flush=True)
     rounding_table(cfg, args.segments, variants, log=lambda m: print(m, flush=True), norm_order=args.norm_order)
 
