@@ -8,9 +8,12 @@ At this depth bf16 operands miss the 2e-2 gate on the first segment already
 (tests/precision_study.py) reproduces such figures, and shows that the error
 is bf16's rounding step itself: with every 16-bit operand in fp16 instead --
 same kernels, same MFMA rate, RMT_F16 -- the GPU measures 2.2e-3 / 2.7e-3 on
-the first segment and 3.3e-3 / 4.0e-3 over two.  So: bf16 against the gate as
-strict xfails with the measured figures, fp16 against the gate as tests that
-must pass, and for both diagonal == sequential bit for bit."""
+the first segment and 3.3e-3 / 4.0e-3 over two.  Keeping bf16 operands but
+carrying some of them in two bf16 terms (hi + lo; the same module, --split)
+clears the two-segment gate with margin only when the gate/up product, the
+largest stage, runs twice.  So: bf16 against the gate as strict xfails with
+the measured figures, fp16 against the gate as tests that must pass, and for
+both diagonal == sequential bit for bit."""
 import numpy as np
 import pytest
 
