@@ -8,10 +8,13 @@
 // Batching for Recurrent Memory Transformers": one launch covers all cells of
 // a diagonal, whatever their number.
 //
-// Design (measured on MI355X: the operand traffic through LDS and the
-// per-slice barrier, under the chip's power limit, bound this kernel -- with
-// every operand L2-resident it runs no faster -- so tiles are as large as LDS
-// and the register file allow):
+// Design (measured on MI355X: no one unit saturates.  The operand stream into
+// LDS, the LDS reads -- conflict free, 4 LDS cycles per 16-byte wave read,
+// with waves waiting to issue them 2-3% of their cycles -- and the MFMAs each
+// run well below their rates, and with every operand L2-resident the kernel
+// runs no faster.  What binds is each slice's barrier across the workgroup's
+// waves under the chip's power limit, so tiles are as large as LDS and the
+// register file allow):
 //   * Output tiles of 288, 256, 192 or 128 rows x 256 columns, chosen per launch
 //     by a cost model of whole rounds of one tile per CU (see launch_epi);
 //     waves compute 32 x 32 blocks with v_mfma_f32_32x32x16_bf16.  A cell
