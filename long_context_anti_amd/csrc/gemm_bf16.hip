@@ -95,8 +95,9 @@ struct Half16<true> {
 
 // Chunk permutation of LDS row r: logical 16-byte chunk c sits at physical
 // position c ^ swz(r).  It depends only on r mod 32, and 16-byte reads of 32
-// consecutive rows at one logical chunk hit distinct banks (checked for both
-// 32 and 64 four-byte banks).
+// consecutive rows at one logical chunk are free of bank conflicts on gfx950:
+// measured, both by a probe of this read pattern (4 LDS cycles per wave-wide
+// read, the conflict-free rate) and by the kernel's own bank-conflict counter.
 __device__ __forceinline__ int swz(int r) {
   if constexpr (CPR == 8) return ((r >> 1) ^ ((r & 1) << 2)) & 7;
   else return ((r >> 1) + (r >> 3)) & 3;
