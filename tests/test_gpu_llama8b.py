@@ -158,3 +158,38 @@ def test_f16_full_length_teacher_forced(runs8b, inputs8b):
     """fp16 operands, the configuration that meets the gate at this depth,
     over the whole sweep as well."""
     _full_length_teacher_forced(runs8b[F16], inputs8b, "fp16")
+
+
+@pytest.mark.timeout(900)
+def test_f16_batch_of_two_full_length(runs8b):
+    """Two 131,072-token sequences through the same diagonals at this shape:
+    every full diagonal holds 2 x 32 = 64 cells of 2,176 rows, so it takes two
+    launches of 32, the largest the group tables carry.  Each sequence equals
+    its own single-sequence run bit for bit (compared on the device: the
+    batched hidden states are 4.3 GB)."""
+    import torch
+    from rmt_inputs import device as rdev
+    run = runs8b[F16]
+    gu.say("[8b] fp16, batch of two at full length")
+    toks = [run.tokens, rdev.segment_inputs(CFG, ri.tokens(CFG, 1))]
+    mems = [run.mem0_dev, rdev.f32_tensor(ri.initial_memory(CFG, 1))]
+    T = CFG.S * CFG.n
+    singles = []
+    for b in range(2):
+        h = torch.full((T, CFG.d), float("nan"), dtype=torch.float32, device="cuda")
+        m = torch.full((CFG.L, CFG.m, CFG.d), float("nan"), dtype=torch.float32, device="cuda")
+        run.model.forward_diagonal(toks[b], mems[b], h, m)
+        singles.append((h, m))
+    torch.cuda.synchronize()
+    try:
+        run.model.set_batch(2)
+        hb = torch.full((2, T, CFG.d), float("nan"), dtype=torch.float32, device="cuda")
+        mb = torch.full((2, CFG.L, CFG.m, CFG.d), float("nan"), dtype=torch.float32, device="cuda")
+        run.model.forward_diagonal(torch.stack(toks).contiguous(), torch.stack(mems).contiguous(), hb, mb)
+        torch.cuda.synchronize()
+        for b, (h, m) in enumerate(singles):
+            assert torch.equal(hb[b], h), f"hidden of sequence {b}"
+            assert torch.equal(mb[b], m), f"memory of sequence {b}"
+        assert bool(torch.isfinite(hb).all())
+    finally:
+        run.model.set_batch(1)
